@@ -1,0 +1,304 @@
+"""Plain fp64 CPU oracle for LServe-style unified block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+bench's cpu_baseline leg may import this module. The library path never calls
+it, and it shares no code with the GPU kernels or their bindings.
+
+Inputs are raw bf16 bit patterns (numpy uint16) and int arrays exactly as the
+GPU receives them; bf16 is decoded exactly to fp64 and everything after that is
+fp64 NumPy. Sources (the LServe pages):
+
+* "LServe: Efficient Long-sequence LLM Serving with Unified Sparse Attention"
+  (arXiv 2502.14866), abstract: half the heads become streaming heads in both
+  prefill and decode; a constant number of KV pages suffices; a hierarchical,
+  query-centric page selector prunes pages; less important tokens are skipped
+  block-wise.
+* "LServe + SampleAttention" blog, sections "LServe -- Prefill Phase" (Figure 1)
+  and "LServe -- Decode Phase" (Figure 2): a KV tile is computed or skipped whole
+  at kernel-tile granularity; a streaming head keeps sink tokens plus a local
+  window (the Lambda shape); decode scores every page from a per-page summary,
+  keeps the top-k and attends token by token inside the kept pages.
+
+The page bound sum_c max(q_c*kmin_c, q_c*kmax_c) is the query-aware bound of
+Quest (cited by the LServe paper); the pages call it only "a summary vector per
+page". Readings taken where the pages are silent are listed in each docstring.
+
+Every function here is pinned by a test in tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact decode of bf16 bit patterns: the 16 bits are the top half of an fp32."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def tokens_of_sequence(cache: np.ndarray, page_row: np.ndarray, L: int, P: int,
+                       token_idx: Optional[np.ndarray] = None) -> np.ndarray:
+    """Token-major view of one sequence of a paged cache.
+
+    cache is [NP, Hkv, P, D]; token t of the sequence lives at
+    cache[page_row[t // P], :, t % P, :] (PagedAttention layout). Returns [n, Hkv, D].
+    """
+    t = np.arange(L) if token_idx is None else np.asarray(token_idx, dtype=np.int64)
+    return cache[np.asarray(page_row, dtype=np.int64)[t // P], :, t % P, :]
+
+
+def _softmax_attend(s: np.ndarray, v: np.ndarray) -> Tuple[np.ndarray, float]:
+    """out = sum_c softmax(s)_c v_c with max subtraction; lse = ln sum_c exp(s_c)."""
+    if s.size == 0:
+        return np.zeros(v.shape[-1]), -math.inf
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    return (p @ v) / l, m + math.log(l)
+
+
+# ----------------------------------------------------------------------------- prefill
+
+def prefill_kept_tiles(i: int, streaming: bool, mask_row, sink_tiles: int,
+                       local_tiles: int) -> List[int]:
+    """KV tiles kept for query tile i (blog, Prefill section and Figure 1).
+
+    Dense head: the tiles j <= i whose mask entry is set (entries above the diagonal
+    are ignored; causality always holds). Streaming head (Lambda shape): the first
+    sink_tiles tiles plus the local_tiles most recent tiles, the diagonal tile counted
+    among the local ones; the tiles in between are never visited.
+    """
+    if streaming:
+        return [j for j in range(i + 1) if j < sink_tiles or j > i - local_tiles]
+    return [j for j in range(i + 1) if mask_row[j]]
+
+
+def prefill_ref(q_bits, k_cache_bits, v_cache_bits, page_table, L: int, Hq: int, Hkv: int,
+                D: int, P: int, T: int, head_kind, block_mask, sink_tiles: int,
+                local_tiles: int, sm_scale: float, rows: Optional[Sequence[int]] = None,
+                heads: Optional[Sequence[int]] = None):
+    """Block-sparse / Lambda causal attention of one sequence, fp64.
+
+    Query row r of head h (KV head g = h // (Hq/Hkv)) attends to the keys
+    K(r) = { c <= r : c // T is a kept tile of (h, r // T) }:
+      out[r, h] = sum_{c in K(r)} softmax_c(sm_scale * q_r . k_c) v_c,
+      lse[h, r] = ln sum_{c in K(r)} exp(sm_scale * q_r . k_c).
+    Only the diagonal tile is cut at token level (c <= r); every other kept tile
+    enters whole. A row with no key gets out = 0 and lse = -inf.
+
+    rows/heads restrict the evaluation (default: all). Returns (out, lse) with
+    out [n_rows, n_heads, D] and lse [n_heads, n_rows] in the order given.
+    """
+    G = Hq // Hkv
+    rows = list(range(L)) if rows is None else [int(r) for r in rows]
+    heads = list(range(Hq)) if heads is None else [int(h) for h in heads]
+    Kc = bf16_to_f64(k_cache_bits)
+    Vc = bf16_to_f64(v_cache_bits)
+    K = tokens_of_sequence(Kc, page_table, L, P)            # [L, Hkv, D]
+    V = tokens_of_sequence(Vc, page_table, L, P)
+    Q = bf16_to_f64(q_bits)                                  # [L, Hq, D]
+    mask = np.asarray(block_mask)
+    out = np.zeros((len(rows), len(heads), D))
+    lse = np.full((len(heads), len(rows)), -math.inf)
+    by_tile: Dict[int, List[Tuple[int, int]]] = {}
+    for ri, r in enumerate(rows):
+        by_tile.setdefault(r // T, []).append((ri, r))
+    for hi, h in enumerate(heads):
+        g = h // G
+        streaming = bool(head_kind[g])
+        for i, members in by_tile.items():
+            kept = prefill_kept_tiles(i, streaming, mask[h, i], sink_tiles, local_tiles)
+            keys = np.concatenate([np.arange(j * T, min((j + 1) * T, L)) for j in kept]) \
+                if kept else np.zeros(0, dtype=np.int64)
+            rr = np.array([r for _, r in members])
+            s = sm_scale * (Q[rr, h, :] @ K[keys, g, :].T)   # [rows, keys]
+            allowed = keys[None, :] <= rr[:, None]
+            for (ri, r), srow, arow in zip(members, s, allowed):
+                o, z = _softmax_attend(srow[arow], V[keys[arow], g, :])
+                out[ri, hi] = o
+                lse[hi, ri] = z
+    return out, lse
+
+
+def prefill_kept_tile_count(nT: int, Hq: int, Hkv: int, head_kind, block_mask, sink_tiles: int,
+                            local_tiles: int) -> int:
+    """Number of kept (head, query tile, KV tile) triples: the unit of prefill work."""
+    G = Hq // Hkv
+    mask = np.asarray(block_mask)
+    total = 0
+    for h in range(Hq):
+        if head_kind[h // G]:
+            for i in range(nT):
+                total += min(sink_tiles, i + 1) + min(local_tiles, max(0, i + 1 - sink_tiles))
+        else:
+            total += int(np.tril(mask[h] != 0).sum())
+    return total
+
+
+# ----------------------------------------------------------------------------- page bounds
+
+def bounds_ref(k_cache_bits, page_table, seq_lens, P: int, Lp: int, head_kind,
+               pages: Optional[Sequence[Tuple[int, int]]] = None):
+    """Per-page key summary (blog, Decode section: "a summary vector per page").
+
+    For every valid page j of sequence b (physical page p = page_table[b, j]), every
+    dense KV head g and every logical sub-page u of Lp tokens that holds at least one
+    valid token, the channel-wise min and max of the keys over the valid tokens of
+    that sub-page. Valid tokens of page j are t < seq_lens[b] - j*P.
+
+    Returns (values, defined): values [NP, Hkv, P/Lp, 2, D] fp64 (index 0 = min,
+    1 = max) and a bool [NP, Hkv, P/Lp] marking the entries that are defined.
+    pages restricts the work to the given (b, j) pairs.
+    """
+    Kc = bf16_to_f64(k_cache_bits)
+    NP, Hkv, _, D = Kc.shape
+    U = P // Lp
+    values = np.zeros((NP, Hkv, U, 2, D))
+    defined = np.zeros((NP, Hkv, U), dtype=bool)
+    pt = np.asarray(page_table)
+    lens = [int(x) for x in seq_lens]
+    if pages is None:
+        pages = [(b, j) for b in range(len(lens)) for j in range((lens[b] + P - 1) // P)]
+    for b, j in pages:
+        p = int(pt[b, j])
+        valid = min(P, lens[b] - j * P)
+        for g in range(Hkv):
+            if head_kind[g]:
+                continue
+            for u in range(U):
+                lo, hi = u * Lp, min((u + 1) * Lp, valid)
+                if hi <= lo:
+                    continue
+                kk = Kc[p, g, lo:hi, :]
+                values[p, g, u, 0] = kk.min(axis=0)
+                values[p, g, u, 1] = kk.max(axis=0)
+                defined[p, g, u] = True
+    return values, defined
+
+
+# ----------------------------------------------------------------------------- selection
+
+def subpage_bound(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> float:
+    """Upper bound of max_{h, t} q_h . k_t over the tokens of one sub-page.
+
+    For each query head h of the group: sum over channels c of
+    max(q_hc * kmin_c, q_hc * kmax_c) (the Quest bound); the group takes the max over
+    its heads, so the result still bounds every head's best dot product.
+    """
+    per_head = np.maximum(q_group * kmin[None, :], q_group * kmax[None, :]).sum(axis=1)
+    return float(per_head.max())
+
+
+def page_scores_ref(q_bits, bounds_values, bounds_defined, page_table, seq_lens, Hq: int,
+                    Hkv: int, P: int, Lp: int, head_kind,
+                    pairs: Optional[Sequence[Tuple[int, int]]] = None) -> Dict[Tuple[int, int], np.ndarray]:
+    """Score of every valid page of every (sequence b, dense KV head g).
+
+    A page's score is the max of the bounds of its sub-pages that hold valid tokens
+    (the hierarchical step: Lp-token summaries reduced to the P-token page that is
+    selected). Returns {(b, g): scores[n_b]} with n_b = ceil(seq_lens[b] / P).
+    """
+    G = Hq // Hkv
+    Q = bf16_to_f64(q_bits)                      # [B, Hq, D]
+    pt = np.asarray(page_table)
+    lens = [int(x) for x in seq_lens]
+    if pairs is None:
+        pairs = [(b, g) for b in range(len(lens)) for g in range(Hkv) if not head_kind[g]]
+    out = {}
+    for b, g in pairs:
+        L = lens[b]
+        n = (L + P - 1) // P
+        qg = Q[b, g * G:(g + 1) * G, :]
+        sc = np.empty(n)
+        for j in range(n):
+            p = int(pt[b, j])
+            valid = min(P, L - j * P)
+            nsub = (valid + Lp - 1) // Lp
+            best = -math.inf
+            for u in range(nsub):
+                assert bounds_defined[p, g, u]
+                best = max(best, subpage_bound(qg, bounds_values[p, g, u, 0], bounds_values[p, g, u, 1]))
+            sc[j] = best
+        out[(b, g)] = sc
+    return out
+
+
+def topk_pages_ref(scores: np.ndarray, k: int) -> List[int]:
+    """The k best pages: order by (score descending, page index ascending), keep the
+    first k (all pages when there are at most k), return them in ascending order."""
+    n = len(scores)
+    if n <= k:
+        return list(range(n))
+    order = sorted(range(n), key=lambda j: (-scores[j], j))
+    return sorted(order[:k])
+
+
+def select_ref(q_bits, k_cache_bits, page_table, seq_lens, Hq: int, Hkv: int, P: int, Lp: int,
+               token_budget: int, head_kind, pairs=None):
+    """Query-aware page selection for one decode step, end to end (bounds -> scores ->
+    top-k with k = token_budget / P). Returns ({(b, g): selected pages}, scores dict)."""
+    lens = [int(x) for x in seq_lens]
+    if pairs is None:
+        pairs = [(b, g) for b in range(len(lens)) for g in range(Hkv) if not head_kind[g]]
+    bs = sorted({b for b, _ in pairs})
+    pages = [(b, j) for b in bs for j in range((lens[b] + P - 1) // P)]
+    vals, defined = bounds_ref(k_cache_bits, page_table, seq_lens, P, Lp, head_kind, pages=pages)
+    scores = page_scores_ref(q_bits, vals, defined, page_table, seq_lens, Hq, Hkv, P, Lp,
+                             head_kind, pairs=pairs)
+    k = token_budget // P
+    return {bg: topk_pages_ref(s, k) for bg, s in scores.items()}, scores
+
+
+# ----------------------------------------------------------------------------- decode
+
+def decode_keys_ref(L: int, P: int, streaming: bool, selected: Sequence[int], sink_tokens: int,
+                    local_tokens: int) -> np.ndarray:
+    """Token positions one decode query attends to (the query sits at position L-1 and
+    the context holds tokens 0..L-1).
+
+    Dense head: every valid token of the selected pages (token-level attention inside
+    the kept pages). Streaming head: tokens t < sink_tokens or t >= L - local_tokens.
+    """
+    if streaming:
+        return np.array([t for t in range(L) if t < sink_tokens or t >= L - local_tokens],
+                        dtype=np.int64)
+    toks = [np.arange(j * P, min((j + 1) * P, L)) for j in sorted(int(x) for x in selected)]
+    return np.concatenate(toks).astype(np.int64) if toks else np.zeros(0, dtype=np.int64)
+
+
+def decode_ref(q_bits, k_cache_bits, v_cache_bits, page_table, seq_lens, Hq: int, Hkv: int,
+               P: int, head_kind, selected: Dict[Tuple[int, int], Sequence[int]],
+               sink_tokens: int, local_tokens: int, sm_scale: float,
+               batches: Optional[Sequence[int]] = None):
+    """Sparse decode attention, fp64: out[b, h] = softmax-weighted sum of v over the key
+    set of (b, KV head h // G) from decode_keys_ref; lse = ln sum exp(scores); an empty
+    key set gives out = 0 and lse = -inf. selected maps (b, g) of dense heads to page
+    indices. Returns (out [nb, Hq, D], lse [nb, Hq]) for the batches given."""
+    G = Hq // Hkv
+    Kc = bf16_to_f64(k_cache_bits)
+    Vc = bf16_to_f64(v_cache_bits)
+    Q = bf16_to_f64(q_bits)
+    pt = np.asarray(page_table)
+    lens = [int(x) for x in seq_lens]
+    bl = list(range(len(lens))) if batches is None else [int(b) for b in batches]
+    D = Kc.shape[-1]
+    out = np.zeros((len(bl), Hq, D))
+    lse = np.full((len(bl), Hq), -math.inf)
+    for bi, b in enumerate(bl):
+        L = lens[b]
+        for g in range(Hkv):
+            streaming = bool(head_kind[g])
+            keys = decode_keys_ref(L, P, streaming, [] if streaming else selected[(b, g)],
+                                   sink_tokens, local_tokens)
+            Kt = tokens_of_sequence(Kc, pt[b], L, P, keys)[:, g, :]
+            Vt = tokens_of_sequence(Vc, pt[b], L, P, keys)[:, g, :]
+            for h in range(g * G, (g + 1) * G):
+                o, z = _softmax_attend(sm_scale * (Kt @ Q[b, h]), Vt)
+                out[bi, h] = o
+                lse[bi, h] = z
+    return out, lse

@@ -1,0 +1,374 @@
+"""Pins of the fp64 oracle against facts fixed by the mathematics and the pages.
+
+Each test checks the oracle against something other than itself: a library routine
+(torch's scaled_dot_product_attention in float64 on the CPU), a closed form, an
+explicitly materialised token mask, brute force over tokens, a hand-derived worked
+example (tests/golden/select_tiny.json) or an invariant of the Quest bound.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from workloads import cases
+from tests.helpers import bits
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _sdpa_f64(q_tok, k_tok, v_tok, G, scale, mask=None, causal=False):
+    """Library attention on token-major tensors: q [L,Hq,D], k/v [Lk,Hkv,D] -> [L,Hq,D]."""
+    q = q_tok.double().permute(1, 0, 2)[None]
+    k = k_tok.double().repeat_interleave(G, dim=1).permute(1, 0, 2)[None]
+    v = v_tok.double().repeat_interleave(G, dim=1).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, is_causal=causal, scale=scale)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _prefill(c, **kw):
+    return oracle.prefill_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.numpy(),
+                              c.L, c.Hq, c.Hkv, c.D, c.P, c.T, c.head_kind, c.block_mask.numpy(),
+                              c.sink_tiles, c.local_tiles, c.sm_scale, **kw)
+
+
+# ----------------------------------------------------------------------------- prefill pins
+
+@pytest.mark.parametrize("L,T,P,D", [(200, 64, 64, 64), (130, 32, 64, 32), (96, 32, 16, 16)])
+def test_prefill_all_kept_equals_causal_sdpa(L, T, P, D):
+    c = cases.make_prefill("t", L, 4, 2, D, T, P, [0, 0], 1, 1, "all", 11, "cpu",
+                           keep_tokens=True, extra_pages=3)
+    out, lse = _prefill(c)
+    ref = _sdpa_f64(c.q, c.k_tok, c.v_tok, c.G, c.sm_scale, causal=True)
+    assert np.abs(out - ref).max() < 1e-12
+    # lse against an explicit log-sum-exp over the causal prefix
+    q = c.q.double().numpy()
+    k = c.k_tok.double().numpy()
+    for r in [0, 1, T - 1, T, L - 1]:
+        s = c.sm_scale * (k[:r + 1, 1, :] @ q[r, 3, :])
+        assert abs(lse[3, r] - np.log(np.exp(s).sum())) < 1e-10
+
+
+def _lambda_token_mask(L, T, sink_tiles, local_tiles):
+    """Streaming support written per token pair: key c is visible to query r iff c <= r
+    and c lies in the first sink_tiles*T tokens or in the local_tiles tiles ending with
+    the query's own tile."""
+    r = torch.arange(L)[:, None]
+    c = torch.arange(L)[None, :]
+    local_start = (r // T - local_tiles + 1) * T
+    return (c <= r) & ((c < sink_tiles * T) | (c >= local_start))
+
+
+@pytest.mark.parametrize("sink,local", [(1, 3), (2, 1), (0, 2), (1, 1)])
+def test_prefill_lambda_equals_materialised_mask(sink, local):
+    L, T = 300, 32
+    c = cases.make_prefill("t", L, 2, 1, 32, T, 16, [1], sink, local, "all", 12, "cpu",
+                           keep_tokens=True)
+    out, _ = _prefill(c)
+    m = _lambda_token_mask(L, T, sink, local)
+    ref = _sdpa_f64(c.q, c.k_tok, c.v_tok, c.G, c.sm_scale, mask=m[None, None])
+    assert np.abs(out - ref).max() < 1e-12
+
+
+def test_prefill_lambda_wide_window_is_dense():
+    L, T = 257, 32
+    nT = (L + T - 1) // T
+    c = cases.make_prefill("t", L, 2, 1, 32, T, 64, [1], 2, nT - 2, "all", 13, "cpu",
+                           keep_tokens=True)
+    out, _ = _prefill(c)
+    ref = _sdpa_f64(c.q, c.k_tok, c.v_tok, c.G, c.sm_scale, causal=True)
+    assert np.abs(out - ref).max() < 1e-12
+
+
+def test_prefill_row0_is_v0_and_const_v():
+    c = cases.make_prefill("t", 150, 4, 2, 32, 32, 64, [0, 1], 1, 2, "random", 14, "cpu",
+                           mask_arg=5, keep_tokens=True)
+    out, lse = _prefill(c)
+    v = c.v_tok.double().numpy()
+    for h in range(4):
+        assert np.array_equal(out[0, h], v[0, h // 2])
+        assert lse[h, 0] == pytest.approx(c.sm_scale * float(
+            (c.q[0, h].double() * c.k_tok[0, h // 2].double()).sum()), abs=1e-12)
+    c.v_cache[:] = torch.tensor(0.71875, dtype=torch.bfloat16)
+    out2, _ = _prefill(c)
+    assert np.abs(out2 - 0.71875).max() < 1e-12
+
+
+def test_prefill_diagonal_only_is_per_tile_causal():
+    L, T = 170, 32
+    c = cases.make_prefill("t", L, 2, 2, 32, T, 32, [0, 0], 1, 1, "diag", 15, "cpu",
+                           keep_tokens=True)
+    out, _ = _prefill(c)
+    for i in range((L + T - 1) // T):
+        sl = slice(i * T, min((i + 1) * T, L))
+        ref = _sdpa_f64(c.q[sl], c.k_tok[sl], c.v_tok[sl], 1, c.sm_scale, causal=True)
+        assert np.abs(out[sl] - ref).max() < 1e-12
+
+
+def test_prefill_zero_query_averages_kept_keys():
+    """q = 0 gives equal weights, so out[r] is the mean of v over K(r); the key set is
+    written here per token from the block mask (ignoring tiles above the diagonal) and
+    the Lambda rule."""
+    L, T = 333, 32
+    nT = (L + T - 1) // T
+    c = cases.make_prefill("t", L, 4, 2, 16, T, 64, [0, 1], 1, 3, "random", 16, "cpu",
+                           mask_arg=12, keep_tokens=True, upper_junk=True)
+    c.q.zero_()
+    out, lse = _prefill(c)
+    v = c.v_tok.double().numpy()
+    mask = c.block_mask.numpy()
+    lam = _lambda_token_mask(L, T, 1, 3).numpy()
+    for h in range(4):
+        g = h // 2
+        for r in range(L):
+            if c.head_kind[g]:
+                keys = np.nonzero(lam[r])[0]
+            else:
+                keys = np.array([t for t in range(r + 1) if mask[h, r // T, t // T]])
+            assert np.abs(out[r, h] - v[keys, g].mean(axis=0)).max() < 1e-12
+            assert lse[h, r] == pytest.approx(math.log(len(keys)), abs=1e-12)
+    assert nT == 11
+
+
+def test_prefill_empty_row():
+    L, T = 64, 16
+    c = cases.make_prefill("t", L, 1, 1, 16, T, 16, [0], 1, 1, "diag", 17, "cpu")
+    c.block_mask[0, 2, 2] = 0            # tile 2 keeps nothing
+    out, lse = _prefill(c)
+    assert np.all(out[32:48, 0] == 0) and np.all(np.isneginf(lse[0, 32:48]))
+
+
+def test_prefill_kept_tile_count_matches_enumeration():
+    c = cases.make_prefill("t", 300, 4, 2, 16, 32, 64, [0, 1], 1, 3, "random", 18, "cpu",
+                           mask_arg=9, upper_junk=True)
+    n = oracle.prefill_kept_tile_count(c.nT, c.Hq, c.Hkv, c.head_kind, c.block_mask.numpy(),
+                                       c.sink_tiles, c.local_tiles)
+    lam = _lambda_token_mask(c.nT, 1, 1, 3).numpy()      # tile-level Lambda with T = 1
+    m = c.block_mask.numpy()
+    brute = sum(int(lam.sum()) if c.head_kind[h // 2] else
+                sum(int(m[h, i, j]) for i in range(c.nT) for j in range(i + 1)) for h in range(4))
+    assert n == brute
+
+
+# ----------------------------------------------------------------------------- golden example
+
+def _golden_case():
+    gj = json.load(open(os.path.join(HERE, "golden", "select_tiny.json")))
+    P, L, D = gj["P"], gj["L"], gj["D"]
+    pt = np.array(gj["page_table"], dtype=np.int32)
+    NP = len(pt)
+    keys = np.array(gj["keys"] + [gj["pad_key"]], dtype=np.float32)
+    vals = np.array(gj["values"] + [gj["pad_value"]], dtype=np.float32)
+    # KV head 0 dense, KV head 1 streaming; both hold the same tokens
+    kc = torch.zeros((NP, 2, P, D), dtype=torch.bfloat16)
+    vc = torch.zeros((NP, 2, P, D), dtype=torch.bfloat16)
+    for t in range(NP * P):
+        kc[pt[t // P], :, t % P] = torch.tensor(keys[t]).to(torch.bfloat16)
+        vc[pt[t // P], :, t % P] = torch.tensor(vals[t]).to(torch.bfloat16)
+    q = torch.zeros((1, 4, D), dtype=torch.bfloat16)
+    q[0, :2] = torch.tensor(gj["q_dense_group"]).to(torch.bfloat16)
+    return gj, P, L, pt, kc, vc, q
+
+
+def test_golden_bounds_scores_selection():
+    gj, P, L, pt, kc, vc, q = _golden_case()
+    hk = [0, 1]
+    vals, defined = oracle.bounds_ref(bits(kc), pt[None], [L], P, gj["Lp"], hk)
+    for j in range(4):
+        p = pt[j]
+        assert defined[p, 0, 0] and not defined[p, 1, 0]
+        assert vals[p, 0, 0, 0].tolist() == gj["bounds_min"][j]
+        assert vals[p, 0, 0, 1].tolist() == gj["bounds_max"][j]
+        qg = bits(q)[0, :2]
+        per_head = [oracle.subpage_bound(oracle.bf16_to_f64(qg[h:h + 1]), vals[p, 0, 0, 0],
+                                         vals[p, 0, 0, 1]) for h in range(2)]
+        assert per_head == gj["per_head_bounds"][j]
+    scores = oracle.page_scores_ref(bits(q), vals, defined, pt[None], [L], 4, 2, P, gj["Lp"], hk)
+    assert scores[(0, 0)].tolist() == gj["page_scores"]
+    for k, exp in gj["selected"].items():
+        sel, _ = oracle.select_ref(bits(q), bits(kc), pt[None], [L], 4, 2, P, gj["Lp"],
+                                   int(k) * P, hk)
+        assert sel[(0, 0)] == exp
+
+
+def test_golden_decode_key_sets():
+    gj, P, L, pt, kc, vc, q = _golden_case()
+    zero = torch.zeros_like(q)
+    sel = {(0, 0): gj["selected"]["3"]}
+    out, lse = oracle.decode_ref(bits(zero), bits(kc), bits(vc), pt[None], [L], 4, 2, P, [0, 1],
+                                 sel, 1, 2, 1.0)
+    assert oracle.decode_keys_ref(L, P, False, sel[(0, 0)], 1, 2).tolist() == gj["decode_q0_dense_k3_keys"]
+    assert oracle.decode_keys_ref(L, P, True, [], 1, 2).tolist() == gj["decode_streaming_sink1_local2_keys"]
+    assert np.allclose(out[0, 0], gj["decode_q0_dense_k3_out"], rtol=0, atol=1e-15)
+    assert np.allclose(out[0, 3], gj["decode_q0_streaming_out"], rtol=0, atol=1e-15)
+    assert lse[0, 0] == pytest.approx(math.log(6)) and lse[0, 2] == pytest.approx(math.log(3))
+
+
+# ----------------------------------------------------------------------------- bounds pins
+
+@pytest.mark.parametrize("P,Lp", [(16, 4), (16, 16), (8, 1)])
+def test_bounds_brute_force(P, Lp):
+    lens = [37, 16, 1, 50]
+    c = cases.make_decode("t", lens, 4, 2, 8, P, Lp, [0, 1], 4 * P, 4, 8, 21, "cpu",
+                          keep_tokens=True, extra_pages=2)
+    vals, defined = oracle.bounds_ref(bits(c.k_cache), c.page_table.numpy(), lens, P, Lp, c.head_kind)
+    pt = c.page_table.numpy()
+    seen = 0
+    for b, L in enumerate(lens):
+        kt = c.k_tok[b].double().numpy()
+        for t0 in range(0, L, Lp):
+            j, u = t0 // P, (t0 % P) // Lp
+            p = pt[b, j]
+            lo = [math.inf] * c.D
+            hi = [-math.inf] * c.D
+            for t in range(t0, min(t0 + Lp, L)):
+                for ch in range(c.D):
+                    lo[ch] = min(lo[ch], kt[t, 0, ch])
+                    hi[ch] = max(hi[ch], kt[t, 0, ch])
+            assert defined[p, 0, u] and not defined[p, 1, u]
+            assert vals[p, 0, u, 0].tolist() == lo and vals[p, 0, u, 1].tolist() == hi
+            seen += 1
+    assert defined.sum() == seen
+    if Lp == 1:
+        # single-token sub-page: min = max = the key itself
+        assert np.array_equal(vals[defined][:, 0], vals[defined][:, 1])
+
+
+# ----------------------------------------------------------------------------- selection pins
+
+def test_bound_is_upper_bound_and_tight_for_single_tokens():
+    lens = [70, 33]
+    P = 16
+    for Lp in (16, 4, 1):
+        c = cases.make_decode("t", lens, 8, 2, 16, P, Lp, [0, 0], 2 * P, 4, 8, 22, "cpu",
+                              keep_tokens=True, planted=True)
+        vals, defined = oracle.bounds_ref(bits(c.k_cache), c.page_table.numpy(), lens, P, Lp, c.head_kind)
+        sc = oracle.page_scores_ref(bits(c.q), vals, defined, c.page_table.numpy(), lens, 8, 2, P, Lp,
+                                    c.head_kind)
+        q = c.q.double().numpy()
+        for b, L in enumerate(lens):
+            k = c.k_tok[b].double().numpy()
+            for g in range(2):
+                dots = q[b, 4 * g:4 * g + 4] @ k[:, g, :].T           # [G, L]
+                for j in range((L + P - 1) // P):
+                    true = dots[:, j * P:min((j + 1) * P, L)].max()
+                    assert sc[(b, g)][j] >= true - 1e-12
+                    if Lp == 1:
+                        assert sc[(b, g)][j] == pytest.approx(true, abs=1e-12)
+
+
+def test_subpage_scores_tighter_than_page_summary():
+    lens = [90]
+    P = 32
+    c = cases.make_decode("t", lens, 4, 1, 16, P, 8, [0], 2 * P, 4, 8, 23, "cpu", planted=True)
+    kb = bits(c.k_cache)
+    fine = oracle.page_scores_ref(bits(c.q), *oracle.bounds_ref(kb, c.page_table.numpy(), lens, P, 8, [0]),
+                                  c.page_table.numpy(), lens, 4, 1, P, 8, [0])
+    coarse = oracle.page_scores_ref(bits(c.q), *oracle.bounds_ref(kb, c.page_table.numpy(), lens, P, P, [0]),
+                                    c.page_table.numpy(), lens, 4, 1, P, P, [0])
+    assert np.all(fine[(0, 0)] <= coarse[(0, 0)] + 1e-12)
+    assert np.any(fine[(0, 0)] < coarse[(0, 0)])
+
+
+def test_bound_split_sign_identity():
+    """sum_c max(q kmin, q kmax) = q+ . kmax + q- . kmin whenever kmin <= kmax (the form a
+    kernel may evaluate as one dot product of length 2D)."""
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        q = rng.standard_normal((4, 128))
+        a, b = rng.standard_normal((2, 128))
+        kmin, kmax = np.minimum(a, b), np.maximum(a, b)
+        lit = oracle.subpage_bound(q, kmin, kmax)
+        alt = (np.maximum(q, 0) @ kmax + np.minimum(q, 0) @ kmin).max()
+        assert abs(lit - alt) <= 1e-12 * max(1.0, abs(lit))
+
+
+def test_topk_matches_lexsort_and_small_n():
+    rng = np.random.default_rng(7)
+    for n, k in [(100, 10), (64, 64), (10, 64), (500, 64), (33, 1)]:
+        s = np.round(rng.standard_normal(n) * 4) / 4         # many ties
+        got = oracle.topk_pages_ref(s, k)
+        order = np.lexsort((np.arange(n), -s))               # primary: -s, secondary: index
+        assert got == sorted(order[:k].tolist())
+        if n <= k:
+            assert got == list(range(n))
+
+
+def test_budget_covering_context_selects_everything():
+    lens = [100, 64, 5]
+    P = 16
+    c = cases.make_decode("t", lens, 4, 2, 8, P, 4, [0, 1], 8 * P, 4, 8, 24, "cpu")
+    sel, _ = oracle.select_ref(bits(c.q), bits(c.k_cache), c.page_table.numpy(), lens, 4, 2, P, 4,
+                               8 * P, c.head_kind)
+    for b, L in enumerate(lens):
+        assert sel[(b, 0)] == list(range((L + P - 1) // P))
+
+
+# ----------------------------------------------------------------------------- decode pins
+
+def test_decode_full_budget_equals_dense_and_prefill_last_row():
+    lens = [77, 128, 3]
+    P = 16
+    c = cases.make_decode("t", lens, 4, 2, 32, P, P, [0, 0], 1024, 4, 8, 25, "cpu",
+                          keep_tokens=True)
+    sel = {(b, g): list(range((L + P - 1) // P)) for b, L in enumerate(lens) for g in range(2)}
+    out, lse = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.numpy(),
+                                 lens, 4, 2, P, c.head_kind, sel, 4, 8, c.sm_scale)
+    for b, L in enumerate(lens):
+        ref = _sdpa_f64(c.q[b:b + 1], c.k_tok[b], c.v_tok[b], 2, c.sm_scale)
+        assert np.abs(out[b] - ref[0]).max() < 1e-12
+        # same as row L-1 of an all-kept prefill whose last query is this decode query
+        qpf = torch.zeros((L, 4, 32), dtype=torch.bfloat16)
+        qpf[L - 1] = c.q[b]
+        npg = (L + P - 1) // P
+        pout, plse = oracle.prefill_ref(bits(qpf), bits(c.k_cache), bits(c.v_cache),
+                                        c.page_table.numpy()[b, :npg], L, 4, 2, 32, P, 16, [0, 0],
+                                        np.ones((4, (L + 15) // 16, (L + 15) // 16), np.uint8),
+                                        1, 1, c.sm_scale, rows=[L - 1])
+        assert np.abs(pout[0] - out[b]).max() < 1e-12
+        assert np.abs(plse[:, 0] - lse[b]).max() < 1e-12
+
+
+def test_decode_streaming_wide_window_is_dense():
+    lens = [50, 200]
+    c = cases.make_decode("t", lens, 4, 2, 16, 16, 16, [1, 1], 64, 30, 20, 26, "cpu",
+                          keep_tokens=True)
+    out, _ = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.numpy(),
+                               [50], 4, 2, 16, c.head_kind, {}, 30, 20, c.sm_scale)
+    ref = _sdpa_f64(c.q[0:1], c.k_tok[0], c.v_tok[0], 2, c.sm_scale)
+    assert np.abs(out[0] - ref[0]).max() < 1e-12
+
+
+def test_decode_zero_query_averages_key_set():
+    lens = [1000, 77, 64, 1]
+    P = 64
+    c = cases.make_decode("t", lens, 8, 2, 16, P, 16, [0, 1], 4 * P, 100, 130, 27, "cpu",
+                          keep_tokens=True)
+    c.q.zero_()
+    rng = np.random.default_rng(3)
+    sel = {}
+    for b, L in enumerate(lens):
+        n = (L + P - 1) // P
+        sel[(b, 0)] = sorted(rng.choice(n, size=min(n, 4), replace=False).tolist())
+    out, lse = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.numpy(),
+                                 lens, 8, 2, P, c.head_kind, sel, 100, 130, c.sm_scale)
+    for b, L in enumerate(lens):
+        v = c.v_tok[b].double().numpy()
+        dense_keys = [t for t in range(L) if t // P in sel[(b, 0)]]
+        stream_keys = [t for t in range(L) if t < 100 or t > L - 1 - 130]
+        for h in range(4):
+            assert np.abs(out[b, h] - v[dense_keys, 0].mean(0)).max() < 1e-12
+        for h in range(4, 8):
+            assert np.abs(out[b, h] - v[stream_keys, 1].mean(0)).max() < 1e-12
+            assert lse[b, h] == pytest.approx(math.log(len(stream_keys)))
+
+
+def test_decode_empty_sequence():
+    c = cases.make_decode("t", [0, 5], 2, 1, 8, 4, 4, [0], 8, 1, 1, 28, "cpu")
+    out, lse = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.numpy(),
+                                 [0, 5], 2, 1, 4, [0], {(0, 0): [], (1, 0): [0, 1]}, 1, 1, 1.0)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
