@@ -1,0 +1,196 @@
+/*
+ * ubs.h -- unified block-sparse attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libubs.so. Four operations make up the hot path of LServe-style
+ * unified sparse attention ("LServe: Efficient Long-sequence LLM Serving with
+ * Unified Sparse Attention", arXiv 2502.14866; and the blog "LServe +
+ * SampleAttention", sections "LServe -- Prefill Phase" with Figure 1 and
+ * "LServe -- Decode Phase" with Figure 2):
+ *
+ *   sparse_prefill     block-sparse causal attention over a paged GQA KV cache;
+ *                      each KV tile is computed whole or skipped whole, and
+ *                      streaming heads keep only sink tiles plus a local window.
+ *   build_page_bounds  per-page, per-channel key min/max (the page summary).
+ *   select_pages       query-aware page scores and top-k selection.
+ *   sparse_decode      GQA decode attention over the kept pages (dense heads)
+ *                      or the sink and local tokens (streaming heads).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every pointer is a DEVICE pointer unless its comment says "host".
+ * - bf16 tensors are passed as raw 16-bit patterns (ubs_bf16_t).
+ * - All tensors are dense, row-major (last index fastest) and 16-byte aligned.
+ * - Paged KV cache: k_cache / v_cache are [NP][Hkv][P][D]; token t of a
+ *   sequence lives in physical page page_table[t / P] at row t % P. Page ids
+ *   must be in [0, NP); entries past a sequence's last page are never read.
+ * - head_kind is HOST memory, uint8 [Hkv]: 0 = dense (retrieval) KV head,
+ *   1 = streaming KV head. Query head h belongs to KV head h / (Hq / Hkv).
+ *   Hkv <= 64.
+ * - The library never allocates device memory, never synchronises and keeps
+ *   no pointer after it returns. Work is enqueued on `stream`; results are
+ *   valid once the stream has reached that point, and inputs must stay alive
+ *   until then. Calls that share a workspace must be ordered on one stream.
+ * - Return value: UBS_OK (0) or a negative UBS_ERR_* code. Arguments are
+ *   validated on the host before any HIP call; on error nothing is enqueued
+ *   and ubs_last_error() returns a message for the calling thread.
+ */
+#ifndef UBS_H
+#define UBS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t ubs_bf16_t; /* raw bfloat16 bits */
+
+#define UBS_OK 0
+#define UBS_ERR_INVALID_ARGUMENT (-1) /* null pointer, negative size, Hq % Hkv != 0, ... */
+#define UBS_ERR_UNSUPPORTED (-2)      /* a size outside the shapes the kernels implement */
+#define UBS_ERR_WORKSPACE_TOO_SMALL (-3)
+#define UBS_ERR_HIP (-4)              /* a HIP launch failed; message from the runtime */
+
+/* Thread-local description of the last failing call (empty string if none). */
+const char* ubs_last_error(void);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int ubs_version(void);
+
+/*
+ * sparse_prefill -- block-sparse / streaming causal attention of ONE sequence.
+ *
+ * Defined by the blog's "LServe -- Prefill Phase" section and its Figure 1:
+ * every (query head h, query tile i) computes or skips each KV tile j whole.
+ * Query row r (tile i = r / T) of head h (KV head g = h / (Hq/Hkv)) attends to
+ *     K(r) = { c <= r : c / T is a kept tile of (h, i) }
+ * with kept tiles
+ *     dense KV head g:     { j <= i : block_mask[h][i][j] != 0 }
+ *     streaming KV head g: { j <= i : j < sink_tiles  or  j > i - local_tiles }
+ * (the local window counts the diagonal tile; the tiles in between are never
+ * loaded). Only the diagonal tile is cut per token (c <= r). Mask entries
+ * above the diagonal are ignored, and mask rows of streaming heads are not read.
+ *     out[r][h][:] = sum_{c in K(r)} softmax_c(sm_scale * q_r . k_c) * v_c
+ *     lse[h][r]    = ln sum_{c in K(r)} exp(sm_scale * q_r . k_c)
+ * A row with an empty K(r) gets out = 0 and lse = -inf.
+ *
+ *   q           bf16 [L][Hq][D]
+ *   k_cache,    bf16 [NP][Hkv][P][D]
+ *   v_cache
+ *   page_table  int32 [ceil(L / P)]
+ *   block_mask  uint8 [Hq][nT][nT], nT = ceil(L / T); may be NULL when every
+ *               KV head streams
+ *   out         fp32 [L][Hq][D]           (fully written)
+ *   lse         fp32 [Hq][L] or NULL      (fully written when given)
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; the softmax weights
+ * are rounded to bf16 before the P.V product.
+ * Supported: D in {64, 128}; T in {64, 128}; P a multiple of 16; L >= 0
+ * (L = 0 is a no-op); Hq % Hkv == 0.
+ */
+int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                   const int32_t* page_table, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t P, int32_t T, const uint8_t* head_kind /* host */,
+                   const uint8_t* block_mask, int32_t sink_tiles, int32_t local_tiles,
+                   float sm_scale, float* out, float* lse, hipStream_t stream);
+
+/*
+ * build_page_bounds -- the per-page key summary used to score pages.
+ *
+ * Defined by the blog's "LServe -- Decode Phase" section ("a summary vector
+ * per page") together with the query-aware bound of Quest that the LServe
+ * paper cites. For every sequence b, every valid page j < ceil(seq_lens[b]/P)
+ * (physical page p = page_table[b][j]), every DENSE KV head g and every
+ * logical sub-page u of Lp tokens holding at least one valid token
+ * (t < seq_lens[b]):
+ *     bounds[p][g][u][0][c] = min over those tokens of k[c]
+ *     bounds[p][g][u][1][c] = max over those tokens of k[c]
+ * Entries of streaming heads, of unreferenced pages and of sub-pages with no
+ * valid token are left untouched. Values are exact (bf16 min/max).
+ *
+ *   k_cache     bf16 [NP][Hkv][P][D]
+ *   page_table  int32 [B][max_pages]
+ *   seq_lens    int32 [B], 0 <= seq_lens[b] <= max_pages * P
+ *   bounds      bf16 [NP][Hkv][P/Lp][2][D]
+ * A physical page referenced by several sequences must hold the same valid
+ * tokens in each. Supported: D in {64, 128}; P a multiple of 16, <= 256;
+ * Lp divides P.
+ */
+int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, const int32_t* seq_lens,
+                      int32_t B, int32_t max_pages, int32_t Hkv, int32_t D, int32_t P, int32_t Lp,
+                      const uint8_t* head_kind /* host */, ubs_bf16_t* bounds, hipStream_t stream);
+
+/*
+ * select_pages -- query-aware top-k page selection for one decode step.
+ *
+ * Defined by the blog's "LServe -- Decode Phase" section and Figure 2 (score
+ * every page from its summary, keep the top-k) and the LServe abstract
+ * (hierarchical, query-centric page selection with a constant page budget).
+ * For each sequence b and DENSE KV head g with query heads h of its group:
+ *   sub-page bound  s_u = max_h sum_c max(q[b][h][c] * kmin_u[c], q[b][h][c] * kmax_u[c])
+ *   page score      s_j = max over the sub-pages u of page j that hold valid tokens
+ *   selection       the k = token_budget / P pages first in the order
+ *                   (score descending, page index ascending); every page when
+ *                   the sequence has at most k pages.
+ * Scores are evaluated in fp32 as q+ . kmax + q- . kmin (q+ = max(q, 0),
+ * q- = min(q, 0)), which equals the sum above term by term.
+ *
+ *   q             bf16 [B][Hq][D]
+ *   bounds        bf16 [NP][Hkv][P/Lp][2][D], as written by build_page_bounds
+ *   page_table    int32 [B][max_pages]
+ *   seq_lens      int32 [B]
+ *   selected      int32 [B][Hkv][k]: page indices j (into page_table[b]) in
+ *                 ascending order, unused slots -1; streaming heads get all -1
+ *   num_selected  int32 [B][Hkv]: min(k, ceil(seq_lens[b]/P)); 0 for streaming
+ *   workspace     >= select_pages_workspace_size(...) bytes, any contents
+ * Supported: D in {64, 128}; Hq/Hkv <= 16; P a multiple of 16, <= 256;
+ * P/Lp in {1, 2, 4, 8, 16}; token_budget a positive multiple of P;
+ * max_pages <= 65536.
+ */
+size_t select_pages_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv);
+int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* page_table,
+                 const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv,
+                 int32_t D, int32_t P, int32_t Lp, int32_t token_budget,
+                 const uint8_t* head_kind /* host */, int32_t* selected, int32_t* num_selected,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sparse_decode -- sparse paged GQA decode attention (one query per sequence).
+ *
+ * Defined by the blog's "LServe -- Decode Phase" section and Figure 2
+ * (token-level attention only inside the selected pages) and the LServe
+ * abstract (streaming heads in decode too). The query of sequence b sits at
+ * position L-1 with L = seq_lens[b]; its key set for KV head g is
+ *   dense g:     every valid token (t < L) of the pages selected[b][g][0 .. n)
+ *                with n = num_selected[b][g]
+ *   streaming g: tokens t < sink_tokens or t >= L - local_tokens
+ *     out[b][h][:] = sum_t softmax_t(sm_scale * q[b][h] . k_t) * v_t
+ *     lse[b][h]    = ln sum_t exp(sm_scale * q[b][h] . k_t)
+ * An empty key set gives out = 0, lse = -inf. The key set is split across
+ * work-groups (split-KV); partial (max, sum, output) triples are merged with a
+ * log-sum-exp combine. Arithmetic is fp32 on bf16 inputs.
+ *
+ *   q             bf16 [B][Hq][D]
+ *   selected      int32 [B][Hkv][max_selected], entries in [0, ceil(L/P)),
+ *                 distinct; read for dense heads only (may be NULL if none)
+ *   num_selected  int32 [B][Hkv], each <= max_selected
+ *   out           fp32 [B][Hq][D]        (fully written)
+ *   lse           fp32 [B][Hq] or NULL
+ *   workspace     >= sparse_decode_workspace_size(...) bytes. Its first
+ *                 4 * B * Hkv bytes are arrival counters that must be zero
+ *                 before the first call; every call leaves them zero.
+ * Supported: D in {64, 128}; Hq/Hkv <= 16; P a multiple of 16, <= 256.
+ */
+size_t sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                    int32_t max_selected, int32_t sink_tokens, int32_t local_tokens);
+int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                  const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                  int32_t Hq, int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind /* host */,
+                  const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
+                  int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* UBS_H */

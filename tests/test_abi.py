@@ -1,0 +1,155 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/ubs.h declares, and host-side validation returns the documented error codes
+before any HIP call (so only fake, never-dereferenced pointers are passed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import unified_block_sparse_amd as ubs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 0x10000            # a fake, 16-byte aligned "device pointer" (never dereferenced)
+KIND = (ctypes.c_uint8 * 8)(0, 0, 0, 0, 1, 1, 1, 1)
+NULL = None
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "ubs.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*[\s\*]+([A-Za-z_]\w*)\s*\(", src, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ubs.load()
+    names = _declared_functions()
+    assert {"sparse_prefill", "build_page_bounds", "select_pages", "sparse_decode"} <= names
+    for n in names:
+        assert hasattr(lib, n), f"libubs.so does not export {n}"
+    assert set(ubs.EXPORTED) == names
+    assert lib.ubs_version() >= 100
+
+
+def _prefill(**kw):
+    a = dict(q=A, k=A, v=A, pt=A, L=256, Hq=8, Hkv=8, D=128, P=64, T=128, kind=KIND, mask=A,
+             sink=1, local=4, scale=0.1, out=A, lse=NULL, stream=NULL)
+    a.update(kw)
+    return ubs.load().sparse_prefill(a["q"], a["k"], a["v"], a["pt"], a["L"], a["Hq"], a["Hkv"], a["D"],
+                                     a["P"], a["T"], a["kind"], a["mask"], a["sink"], a["local"], a["scale"],
+                                     a["out"], a["lse"], a["stream"])
+
+
+def _err():
+    return ubs.load().ubs_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(D=96), -2, "D=96"),
+    (dict(T=32), -2, "T=32"),
+    (dict(Hq=12), -1, "multiple"),
+    (dict(P=40), -2, "P=40"),
+    (dict(kind=None), -1, "head_kind"),
+    (dict(kind=(ctypes.c_uint8 * 8)(0, 2, 0, 0, 1, 1, 1, 1)), -1, "head_kind[1]"),
+    (dict(q=None), -1, "non-NULL"),
+    (dict(mask=None), -1, "block_mask"),
+    (dict(L=-1), -1, "L=-1"),
+    (dict(sink=-1), -1, "sink_tiles"),
+    (dict(q=A + 8), -1, "aligned"),
+    (dict(scale=float("nan")), -1, "NaN"),
+])
+def test_prefill_validation(kw, code, frag):
+    assert _prefill(**kw) == code
+    assert frag in _err()
+
+
+def test_prefill_empty_and_all_streaming_mask_ok():
+    assert _prefill(L=0) == 0                       # nothing to launch
+    assert _err() == ""
+    all_stream = (ctypes.c_uint8 * 8)(*([1] * 8))
+    assert _prefill(L=0, kind=all_stream, mask=None) == 0
+
+
+def _bounds(**kw):
+    a = dict(k=A, pt=A, sl=A, B=4, maxp=512, Hkv=8, D=128, P=64, Lp=16, kind=KIND, out=A, stream=NULL)
+    a.update(kw)
+    return ubs.load().build_page_bounds(a["k"], a["pt"], a["sl"], a["B"], a["maxp"], a["Hkv"], a["D"], a["P"],
+                                        a["Lp"], a["kind"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Lp=24), -2), (dict(P=48), -2), (dict(D=32), -2), (dict(B=-1), -1), (dict(k=None), -1),
+    (dict(Hkv=65), -2), (dict(out=A + 2), -1),
+])
+def test_bounds_validation(kw, code):
+    assert _bounds(**kw) == code
+
+
+def test_bounds_nothing_to_do():
+    assert _bounds(B=0) == 0
+    assert _bounds(kind=(ctypes.c_uint8 * 8)(*([1] * 8))) == 0   # no dense head
+
+
+def _select(**kw):
+    lib = ubs.load()
+    a = dict(q=A, bnd=A, pt=A, sl=A, B=4, maxp=512, Hq=32, Hkv=8, D=128, P=64, Lp=64, budget=4096,
+             kind=KIND, sel=A, nsel=A, ws=A, wsb=None, stream=NULL)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.select_pages_workspace_size(a["B"], a["maxp"], a["Hkv"])
+    return lib.select_pages(a["q"], a["bnd"], a["pt"], a["sl"], a["B"], a["maxp"], a["Hq"], a["Hkv"], a["D"],
+                            a["P"], a["Lp"], a["budget"], a["kind"], a["sel"], a["nsel"], a["ws"], a["wsb"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(budget=4000), -2), (dict(budget=0), -1), (dict(Lp=2), -2), (dict(Hq=24), -2),
+    (dict(maxp=20000), -2), (dict(wsb=16), -3), (dict(ws=None), -3), (dict(bnd=None), -1),
+    (dict(sel=None), -1), (dict(Hq=30), -1),
+])
+def test_select_validation(kw, code):
+    assert _select(**kw) == code
+
+
+def test_select_workspace_size():
+    lib = ubs.load()
+    assert lib.select_pages_workspace_size(4, 512, 8) >= 4 * 512 * 8 * 4
+    assert lib.select_pages_workspace_size(4, 512, 8) % 256 == 0
+
+
+def _decode(**kw):
+    lib = ubs.load()
+    a = dict(q=A, k=A, v=A, pt=A, sl=A, B=4, maxp=512, Hq=32, Hkv=8, D=128, P=64, kind=KIND, sel=A, nsel=A,
+             ms=64, sink=128, local=512, scale=0.088, out=A, lse=NULL, ws=A, wsb=None, stream=NULL)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.sparse_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["ms"],
+                                                    a["sink"], a["local"])
+    return lib.sparse_decode(a["q"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["maxp"], a["Hq"], a["Hkv"],
+                             a["D"], a["P"], a["kind"], a["sel"], a["nsel"], a["ms"], a["sink"], a["local"],
+                             a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=40), -2), (dict(P=512), -2), (dict(Hq=24), -2), (dict(Hq=136, Hkv=8), -2), (dict(D=80), -2),
+    (dict(sink=-1), -1), (dict(wsb=100), -3), (dict(nsel=None), -1), (dict(out=None), -1),
+    (dict(k=A + 4), -1),
+])
+def test_decode_validation(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_workspace_grows_with_budget():
+    lib = ubs.load()
+    small = lib.sparse_decode_workspace_size(4, 32, 8, 128, 64, 16, 128, 512)
+    big = lib.sparse_decode_workspace_size(4, 32, 8, 128, 64, 1024, 128, 512)
+    assert big > small >= 4 * 8 * 4
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros((4, 32, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((8, 8, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ubs.sparse_decode(q, kc, kc, torch.zeros((4, 2), dtype=torch.int32), torch.zeros(4, dtype=torch.int32),
+                          [0] * 4 + [1] * 4, None, None, 128, 512, 0.1)

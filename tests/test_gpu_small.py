@@ -1,0 +1,262 @@
+"""GPU parity on small cases: every kernel against the fp64 oracle on the same seeded
+bits, covering several tiles, ragged tails, partial pages, empty sequences, every
+supported D / T / G / P / Lp family, exact ties in page scores, determinism and
+page-table permutation invariance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import unified_block_sparse_amd as ubs
+from tests.gpu_cases import assert_attention_close, assert_lse_close, check_selection
+from tests.helpers import bits
+from workloads import cases
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+SENTINEL = 0x7F7F   # a finite bf16 pattern (about 3.4e38) left where bounds are undefined
+
+
+def _sync():
+    torch.cuda.synchronize(DEV)
+
+
+# ----------------------------------------------------------------------------- bounds
+
+BOUNDS_CASES = [
+    ([37, 16, 1, 50, 0], 16, 4, 128, [0, 1]),
+    ([200, 64, 65], 64, 16, 64, [0, 0, 1, 1]),
+    ([300], 128, 32, 128, [0]),
+    ([1000, 77], 32, 32, 64, [0, 1]),
+    ([129], 64, 4, 128, [1, 0]),
+    ([70, 3], 64, 1, 128, [0]),
+]
+
+
+@pytest.mark.parametrize("lens,P,Lp,D,hk", BOUNDS_CASES)
+def test_bounds_exact(lens, P, Lp, D, hk):
+    Hkv = len(hk)
+    c = cases.make_decode("b", lens, Hkv * 2, Hkv, D, P, Lp, hk, 2 * P, 4, 8, 31, DEV, extra_pages=3,
+                          planted=True)
+    out = torch.full((c.num_physical_pages, Hkv, P // Lp, 2, D), 0, dtype=torch.int16, device=DEV)
+    out.fill_(SENTINEL)
+    out = out.view(torch.bfloat16)
+    ubs.build_page_bounds(c.k_cache, c.page_table, c.seq_lens_t, hk, Lp, bounds=out)
+    _sync()
+    vals, defined = oracle.bounds_ref(bits(c.k_cache), c.page_table.cpu().numpy(), lens, P, Lp, hk)
+    got_bits = bits(out)
+    got = oracle.bf16_to_f64(got_bits)
+    assert defined.sum() > 0
+    assert np.array_equal(got[defined], vals[defined])
+    assert np.all(got_bits[~defined] == SENTINEL)
+
+
+# ----------------------------------------------------------------------------- selection
+
+def _oracle_select(c):
+    sel, scores = oracle.select_ref(bits(c.q), bits(c.k_cache), c.page_table.cpu().numpy(), c.seq_lens,
+                                    c.Hq, c.Hkv, c.P, c.Lp, c.token_budget, c.head_kind)
+    return sel, scores
+
+
+def _gpu_select(c):
+    bnd = ubs.build_page_bounds(c.k_cache, c.page_table, c.seq_lens_t, c.head_kind, c.Lp)
+    sel, num = ubs.select_pages(c.q, bnd, c.page_table, c.seq_lens_t, c.head_kind, c.P, c.token_budget)
+    _sync()
+    return sel.cpu().numpy(), num.cpu().numpy()
+
+
+SELECT_CASES = [
+    # lens, Hq, Hkv, D, P, Lp, head_kind, budget
+    ([37, 16, 1, 50, 0, 300], 8, 2, 128, 16, 4, [0, 1], 4 * 16),
+    ([2000, 1500, 64], 16, 4, 64, 64, 16, [0, 1, 0, 1], 8 * 64),
+    ([500, 4000], 32, 2, 128, 32, 32, [0, 0], 4 * 32),
+    ([1000, 129, 5000], 4, 4, 64, 128, 8, [0, 0, 1, 0], 3 * 128),
+    ([50000], 8, 1, 128, 64, 64, [0], 600 * 64),
+    ([3000, 20], 2, 2, 128, 16, 1, [0, 0], 16 * 16),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,P,Lp,hk,budget", SELECT_CASES)
+def test_select_matches_oracle(lens, Hq, Hkv, D, P, Lp, hk, budget):
+    c = cases.make_decode("s", lens, Hq, Hkv, D, P, Lp, hk, budget, 4, 8, 32, DEV, planted=True)
+    sel_g, num_g = _gpu_select(c)
+    sel_o, scores = _oracle_select(c)
+    check_selection(sel_g, num_g, sel_o, scores, hk, budget // P)
+
+
+def test_select_exact_ties_break_to_lower_index():
+    """Integer-valued q and keys make many page scores tie exactly (the sums are exact in
+    fp32 and fp64), so the tie-break must match the oracle bit for bit."""
+    c = cases.make_decode("t", [3000, 777, 4096], 8, 2, 128, 64, 16, [0, 0], 10 * 64, 4, 8, 33, DEV)
+    for t in (c.k_cache, c.q):
+        t.copy_(t.float().mul(0.7).round().clamp(-1, 1).to(torch.bfloat16))
+    sel_g, num_g = _gpu_select(c)
+    sel_o, scores = _oracle_select(c)
+    n_ties = sum(len(s) - len(set(s.tolist())) for s in scores.values())
+    assert n_ties > 0
+    swaps = check_selection(sel_g, num_g, sel_o, scores, c.head_kind, c.k_pages)
+    assert swaps == 0
+
+
+# ----------------------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    # lens, Hq, Hkv, D, P, Lp, head_kind, budget, sink, local
+    ([37, 16, 1, 50, 0, 300], 8, 2, 128, 16, 4, [0, 1], 4 * 16, 5, 20),
+    ([2000, 1500, 64], 32, 4, 64, 64, 16, [0, 1, 0, 1], 8 * 64, 64, 100),
+    ([500, 4000], 32, 2, 128, 32, 32, [1, 0], 4 * 32, 0, 64),
+    ([1000, 129, 5000], 4, 4, 64, 128, 8, [0, 0, 1, 0], 3 * 128, 128, 1024),
+    ([50000], 8, 1, 128, 64, 64, [0], 600 * 64, 0, 0),
+    ([20000, 777], 16, 2, 128, 64, 16, [1, 1], 64, 1000, 3000),
+    ([3000, 20], 2, 2, 128, 16, 1 * 16, [0, 1], 16 * 16, 7, 33),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,P,Lp,hk,budget,sink,local", DECODE_CASES)
+def test_decode_matches_oracle_on_oracle_selection(lens, Hq, Hkv, D, P, Lp, hk, budget, sink, local):
+    c = cases.make_decode("d", lens, Hq, Hkv, D, P, Lp, hk, budget, sink, local, 34, DEV, planted=True)
+    sel_o, _ = _oracle_select(c)
+    k = budget // P
+    sel_t = torch.full((c.B, Hkv, k), -1, dtype=torch.int32)
+    num_t = torch.zeros((c.B, Hkv), dtype=torch.int32)
+    for (b, g), s in sel_o.items():
+        sel_t[b, g, :len(s)] = torch.tensor(s, dtype=torch.int32)
+        num_t[b, g] = len(s)
+    out, lse = ubs.sparse_decode(c.q, c.k_cache, c.v_cache, c.page_table, c.seq_lens_t, hk, sel_t.to(DEV),
+                                 num_t.to(DEV), sink, local, c.sm_scale, return_lse=True)
+    _sync()
+    ref, ref_lse = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.cpu().numpy(),
+                                     lens, Hq, Hkv, P, hk, sel_o, sink, local, c.sm_scale)
+    assert_attention_close(out.cpu().numpy(), ref, "decode out")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, "decode lse")
+    # a second call reuses the workspace (arrival counters must have been reset)
+    out2 = ubs.sparse_decode(c.q, c.k_cache, c.v_cache, c.page_table, c.seq_lens_t, hk, sel_t.to(DEV),
+                             num_t.to(DEV), sink, local, c.sm_scale)
+    _sync()
+    assert torch.equal(out, out2)
+
+
+def test_decode_end_to_end_select_then_attend():
+    lens = [6000, 2500, 9000]
+    c = cases.make_decode("e", lens, 16, 4, 128, 64, 16, [0, 1, 0, 1], 16 * 64, 64, 256, 35, DEV,
+                          planted=True)
+    bnd = ubs.build_page_bounds(c.k_cache, c.page_table, c.seq_lens_t, c.head_kind, c.Lp)
+    sel, num = ubs.select_pages(c.q, bnd, c.page_table, c.seq_lens_t, c.head_kind, c.P, c.token_budget)
+    out = ubs.sparse_decode(c.q, c.k_cache, c.v_cache, c.page_table, c.seq_lens_t, c.head_kind, sel, num,
+                            c.sink_tokens, c.local_tokens, c.sm_scale)
+    _sync()
+    sel_o, scores = _oracle_select(c)
+    check_selection(sel.cpu().numpy(), num.cpu().numpy(), sel_o, scores, c.head_kind, c.k_pages)
+    ref, _ = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.cpu().numpy(), lens,
+                               c.Hq, c.Hkv, c.P, c.head_kind, sel_o, c.sink_tokens, c.local_tokens, c.sm_scale)
+    sg = sel.cpu().numpy()
+    got = out.cpu().numpy()
+    for b in range(c.B):
+        for g in range(c.Hkv):
+            if c.head_kind[g] or sg[b, g, :len(sel_o[(b, g)])].tolist() == sel_o[(b, g)]:
+                hs = slice(g * c.G, (g + 1) * c.G)
+                assert_attention_close(got[b, hs], ref[b, hs], f"end-to-end b={b} g={g}")
+
+
+def test_decode_full_budget_equals_dense_attention():
+    lens = [3000, 64, 1]
+    P = 64
+    c = cases.make_decode("f", lens, 8, 2, 128, P, P, [0, 0], 64 * P, 0, 0, 36, DEV, keep_tokens=True)
+    bnd = ubs.build_page_bounds(c.k_cache, c.page_table, c.seq_lens_t, c.head_kind, P)
+    sel, num = ubs.select_pages(c.q, bnd, c.page_table, c.seq_lens_t, c.head_kind, P, 64 * P)
+    out = ubs.sparse_decode(c.q, c.k_cache, c.v_cache, c.page_table, c.seq_lens_t, c.head_kind, sel, num, 0, 0,
+                            c.sm_scale)
+    _sync()
+    for b, L in enumerate(lens):
+        q = c.q[b].float()[None, :, None, :]                        # [1, Hq, 1, D]
+        k = c.k_tok[b].float().repeat_interleave(4, dim=1).permute(1, 0, 2)[None].contiguous()
+        v = c.v_tok[b].float().repeat_interleave(4, dim=1).permute(1, 0, 2)[None].contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(q.cpu(), k.cpu(), v.cpu(), scale=c.sm_scale)
+        assert_attention_close(out[b].cpu().numpy(), ref[0, :, 0].numpy(), f"dense b={b}")
+
+
+# ----------------------------------------------------------------------------- prefill
+
+PREFILL_CASES = [
+    # L, Hq, Hkv, D, T, P, head_kind, mask, mask_arg, sink, local
+    (200, 4, 2, 64, 64, 16, [0, 1], "random", 3, 1, 2),
+    (333, 8, 2, 128, 128, 64, [1, 0], "random", 1, 1, 1),
+    (1000, 2, 1, 128, 64, 32, [0], "all", None, 1, 1),
+    (130, 4, 4, 64, 128, 64, [0, 0, 1, 1], "diag", None, 0, 1),
+    (700, 16, 2, 128, 128, 64, [0, 1], "random", 6, 1, 2),
+    (1100, 4, 1, 64, 64, 128, [1], "all", None, 2, 3),
+    (257, 2, 2, 128, 64, 16, [1, 1], "all", None, 0, 0),     # every row empty
+]
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,D,T,P,hk,mask,marg,sink,local", PREFILL_CASES)
+def test_prefill_matches_oracle(L, Hq, Hkv, D, T, P, hk, mask, marg, sink, local):
+    c = cases.make_prefill("p", L, Hq, Hkv, D, T, P, hk, sink, local, mask, 41, DEV, mask_arg=marg,
+                           upper_junk=True, extra_pages=2)
+    out, lse = ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, hk, c.block_mask, sink, local, T,
+                                  c.sm_scale, return_lse=True)
+    _sync()
+    ref, ref_lse = oracle.prefill_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.cpu().numpy(),
+                                      L, Hq, Hkv, D, P, T, hk, c.block_mask.cpu().numpy(), sink, local,
+                                      c.sm_scale)
+    assert_attention_close(out.cpu().numpy(), ref, "prefill out")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, "prefill lse")
+
+
+def test_prefill_empty_tile_row():
+    L, T = 64 * 5 + 7, 64
+    c = cases.make_prefill("e", L, 2, 1, 128, T, 64, [0], 1, 1, "random", 42, DEV, mask_arg=4)
+    c.block_mask[0, 3, :] = 0                   # query tile 3 of head 0 keeps nothing
+    out, lse = ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, [0], c.block_mask, 1, 1, T,
+                                  c.sm_scale, return_lse=True)
+    _sync()
+    assert torch.all(out[3 * T:4 * T, 0] == 0)
+    assert torch.all(torch.isneginf(lse[0, 3 * T:4 * T]))
+    ref, _ = oracle.prefill_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.cpu().numpy(), L,
+                                2, 1, 128, 64, T, [0], c.block_mask.cpu().numpy(), 1, 1, c.sm_scale)
+    assert_attention_close(out.cpu().numpy(), ref, "prefill out")
+
+
+# ----------------------------------------------------------------------------- invariances
+
+def _repermute(cache, page_table, seed):
+    """Move every physical page to a new seeded position; remap the page table."""
+    NP = cache.shape[0]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    perm = torch.randperm(NP, generator=g).to(cache.device)
+    new = torch.empty_like(cache)
+    new[perm] = cache
+    return new, perm[page_table.long()].to(torch.int32)
+
+
+def test_prefill_deterministic_and_page_permutation_invariant():
+    c = cases.make_prefill("i", 900, 8, 2, 128, 128, 64, [0, 1], 1, 2, "random", 43, DEV, mask_arg=10)
+    args = ([0, 1], c.block_mask, 1, 2, 128, c.sm_scale)
+    o1 = ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, *args)
+    o2 = ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, *args)
+    kc, pt = _repermute(c.k_cache, c.page_table, 7)
+    vc, _ = _repermute(c.v_cache, c.page_table, 7)
+    o3 = ubs.sparse_prefill(c.q, kc, vc, pt, *args)
+    _sync()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_decode_deterministic_and_page_permutation_invariant():
+    c = cases.make_decode("i", [5000, 3000], 16, 4, 128, 64, 16, [0, 0, 1, 1], 16 * 64, 64, 512, 44, DEV,
+                          planted=True)
+    bnd = ubs.build_page_bounds(c.k_cache, c.page_table, c.seq_lens_t, c.head_kind, c.Lp)
+    sel, num = ubs.select_pages(c.q, bnd, c.page_table, c.seq_lens_t, c.head_kind, c.P, c.token_budget)
+    run = lambda kc, vc, pt, s, n: ubs.sparse_decode(c.q, kc, vc, pt, c.seq_lens_t, c.head_kind, s, n,  # noqa
+                                                     64, 512, c.sm_scale)
+    o1 = run(c.k_cache, c.v_cache, c.page_table, sel, num)
+    o2 = run(c.k_cache, c.v_cache, c.page_table, sel, num)
+    kc, pt = _repermute(c.k_cache, c.page_table, 9)
+    vc, _ = _repermute(c.v_cache, c.page_table, 9)
+    bnd2 = ubs.build_page_bounds(kc, pt, c.seq_lens_t, c.head_kind, c.Lp)
+    sel2, num2 = ubs.select_pages(c.q, bnd2, pt, c.seq_lens_t, c.head_kind, c.P, c.token_budget)
+    o3 = run(kc, vc, pt, sel2, num2)
+    _sync()
+    assert torch.equal(sel, sel2) and torch.equal(num, num2)
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)

@@ -1,0 +1,16 @@
+"""Unified block-sparse attention (LServe-style) for AMD Instinct MI355X (gfx950).
+
+The four operations of the hot path run as hand-written HIP kernels in
+libubs.so, reached through its C ABI (include/ubs.h):
+
+    sparse_prefill     block-sparse + streaming (Lambda) causal prefill attention
+    build_page_bounds  per-page, per-channel key min/max
+    select_pages       query-aware top-k page selection under a token budget
+    sparse_decode      sparse paged GQA decode with split-KV and LSE combine
+
+Build the library with ``python -m unified_block_sparse_amd.build``.
+"""
+from ._lib import (UBSError, load, sparse_prefill, build_page_bounds, select_pages,  # noqa: F401
+                   sparse_decode, LIB_PATH, EXPORTED)
+
+__all__ = ["UBSError", "load", "sparse_prefill", "build_page_bounds", "select_pages", "sparse_decode"]

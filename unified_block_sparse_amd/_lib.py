@@ -1,0 +1,267 @@
+"""ctypes binding of libubs.so (the C ABI in include/ubs.h).
+
+Argument marshalling only: tensors are checked for dtype, device, shape and
+contiguity, then their device pointers and the current HIP stream go to the C
+entry points, which run every step on the GPU. There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libubs.so")
+
+UBS_OK = 0
+ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
+EXPORTED = ("sparse_prefill", "build_page_bounds", "select_pages", "select_pages_workspace_size",
+            "sparse_decode", "sparse_decode_workspace_size", "ubs_last_error", "ubs_version")
+
+
+class UBSError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with {ERR_NAMES.get(code, code)} ({code}): {msg}")
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int32
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+def load() -> ctypes.CDLL:
+    """Load libubs.so (built by unified_block_sparse_amd.build); raises if it is missing."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run `python -m unified_block_sparse_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.ubs_last_error.restype = ctypes.c_char_p
+        lib.ubs_last_error.argtypes = []
+        lib.ubs_version.restype = ctypes.c_int
+        lib.ubs_version.argtypes = []
+        lib.sparse_prefill.restype = ctypes.c_int
+        lib.sparse_prefill.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _i, _f, _p, _p, _p]
+        lib.build_page_bounds.restype = ctypes.c_int
+        lib.build_page_bounds.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p]
+        lib.select_pages_workspace_size.restype = _sz
+        lib.select_pages_workspace_size.argtypes = [_i, _i, _i]
+        lib.select_pages.restype = ctypes.c_int
+        lib.select_pages.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
+        lib.sparse_decode_workspace_size.restype = _sz
+        lib.sparse_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+        lib.sparse_decode.restype = ctypes.c_int
+        lib.sparse_decode.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _i,
+                                      _f, _p, _p, _p, _sz, _p]
+        _lib = lib
+        return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != UBS_OK:
+        raise UBSError(fn, rc, load().ubs_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _kinds(head_kind: Sequence[int]) -> ctypes.Array:
+    return (ctypes.c_uint8 * len(head_kind))(*[int(x) for x in head_kind])
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ----------------------------------------------------------------------------- workspaces
+
+_ws_cache = {}
+
+
+def _workspace(kind: str, device, stream: int, nbytes: int) -> torch.Tensor:
+    """Per (kind, device, stream) zero-initialised workspace, grown on demand.
+
+    sparse_decode's arrival counters must start at zero and every call leaves them
+    zero, so a cached buffer stays valid across calls ordered on one stream.
+    """
+    key = (kind, device, stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   page_table: torch.Tensor, head_kind: Sequence[int], block_mask: Optional[torch.Tensor],
+                   sink_tiles: int, local_tiles: int, T: int, sm_scale: float,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   return_lse: bool = False):
+    """Block-sparse / streaming prefill attention of one sequence (see include/ubs.h).
+
+    q bf16 [L, Hq, D]; k_cache, v_cache bf16 [NP, Hkv, P, D]; page_table int32 [>= ceil(L/P)];
+    block_mask uint8 [Hq, nT, nT] (None when every KV head streams). Returns out fp32
+    [L, Hq, D] (and lse fp32 [Hq, L] with return_lse).
+    """
+    lib = load()
+    L, Hq, D = q.shape
+    NP, Hkv, P, D2 = k_cache.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(v_cache, "v_cache", torch.bfloat16, shape=k_cache.shape, device=dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    if D2 != D:
+        raise ValueError("q and k_cache head dims differ")
+    if len(head_kind) != Hkv:
+        raise ValueError("head_kind must have one entry per KV head")
+    nT = (L + T - 1) // T
+    if page_table.numel() < (L + P - 1) // P:
+        raise ValueError("page_table is shorter than ceil(L / P)")
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, shape=(Hq, nT, nT), device=dev)
+    if out is None:
+        out = torch.empty((L, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, shape=(L, Hq, D), device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, L), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(Hq, L), device=dev)
+    rc = lib.sparse_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), L, Hq, Hkv, D, P, T,
+                            _kinds(head_kind), _ptr(block_mask), sink_tiles, local_tiles, float(sm_scale),
+                            _ptr(out), _ptr(lse), _stream(dev))
+    _check("sparse_prefill", rc)
+    return (out, lse) if return_lse else out
+
+
+def build_page_bounds(k_cache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                      head_kind: Sequence[int], Lp: int, bounds: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-page key min/max of dense KV heads: bounds bf16 [NP, Hkv, P/Lp, 2, D]."""
+    lib = load()
+    NP, Hkv, P, D = k_cache.shape
+    B, max_pages = page_table.shape
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    if P % Lp:
+        raise ValueError("Lp must divide P")
+    if bounds is None:
+        bounds = torch.zeros((NP, Hkv, P // Lp, 2, D), dtype=torch.bfloat16, device=dev)
+    _need(bounds, "bounds", torch.bfloat16, shape=(NP, Hkv, P // Lp, 2, D), device=dev)
+    rc = lib.build_page_bounds(_ptr(k_cache), _ptr(page_table), _ptr(seq_lens), B, max_pages, Hkv, D, P, Lp,
+                               _kinds(head_kind), _ptr(bounds), _stream(dev))
+    _check("build_page_bounds", rc)
+    return bounds
+
+
+def select_pages(q: torch.Tensor, bounds: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                 head_kind: Sequence[int], P: int, token_budget: int,
+                 selected: Optional[torch.Tensor] = None, num_selected: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Top-k page selection: returns (selected int32 [B, Hkv, k], num_selected int32 [B, Hkv])."""
+    lib = load()
+    B, Hq, D = q.shape
+    NP, Hkv, U, two, D2 = bounds.shape
+    _, max_pages = page_table.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(bounds, "bounds", torch.bfloat16, device=dev)
+    _need(page_table, "page_table", torch.int32, shape=(B, max_pages), device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    if two != 2 or D2 != D or P % U:
+        raise ValueError("bounds must be [NP, Hkv, P/Lp, 2, D]")
+    Lp = P // U
+    if token_budget <= 0 or token_budget % P:
+        raise ValueError("token_budget must be a positive multiple of P")
+    k = token_budget // P
+    if selected is None:
+        selected = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    if num_selected is None:
+        num_selected = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    _need(selected, "selected", torch.int32, shape=(B, Hkv, k), device=dev)
+    _need(num_selected, "num_selected", torch.int32, shape=(B, Hkv), device=dev)
+    st = _stream(dev)
+    need = lib.select_pages_workspace_size(B, max_pages, Hkv)
+    if workspace is None:
+        workspace = _workspace("select", dev, st, need)
+    rc = lib.select_pages(_ptr(q), _ptr(bounds), _ptr(page_table), _ptr(seq_lens), B, max_pages, Hq, Hkv, D, P,
+                          Lp, token_budget, _kinds(head_kind), _ptr(selected), _ptr(num_selected),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(), st)
+    _check("select_pages", rc)
+    return selected, num_selected
+
+
+def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                  seq_lens: torch.Tensor, head_kind: Sequence[int], selected: Optional[torch.Tensor],
+                  num_selected: Optional[torch.Tensor], sink_tokens: int, local_tokens: int, sm_scale: float,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Sparse paged GQA decode: out fp32 [B, Hq, D] (and lse fp32 [B, Hq] with return_lse)."""
+    lib = load()
+    B, Hq, D = q.shape
+    NP, Hkv, P, D2 = k_cache.shape
+    _, max_pages = page_table.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(v_cache, "v_cache", torch.bfloat16, shape=k_cache.shape, device=dev)
+    _need(page_table, "page_table", torch.int32, shape=(B, max_pages), device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    if D2 != D:
+        raise ValueError("q and k_cache head dims differ")
+    if selected is not None:
+        _need(selected, "selected", torch.int32, device=dev)
+        if selected.dim() != 3 or selected.shape[:2] != (B, Hkv):
+            raise ValueError("selected must be [B, Hkv, max_selected]")
+        max_selected = selected.shape[2]
+    else:
+        max_selected = 0
+    if num_selected is not None:
+        _need(num_selected, "num_selected", torch.int32, shape=(B, Hkv), device=dev)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, shape=(B, Hq, D), device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq), device=dev)
+    st = _stream(dev)
+    need = lib.sparse_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens)
+    if workspace is None:
+        workspace = _workspace("decode", dev, st, need)
+    rc = lib.sparse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), B, max_pages,
+                           Hq, Hkv, D, P, _kinds(head_kind), _ptr(selected), _ptr(num_selected), max_selected,
+                           sink_tokens, local_tokens, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), st)
+    _check("sparse_decode", rc)
+    return (out, lse) if return_lse else out

@@ -1,0 +1,299 @@
+// C ABI of libubs: argument validation (host only, before any HIP call), workspace
+// sizing and dispatch to the gfx950 kernels. See include/ubs.h for the contract.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ubs.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return UBS_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(UBS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Splits head_kind (host) into dense / streaming KV-head lists.
+int head_lists(const uint8_t* head_kind, int Hkv, ubs::HeadList* dense, ubs::HeadList* streaming,
+               uint64_t* streaming_mask) {
+  REQUIRE(head_kind != nullptr, UBS_ERR_INVALID_ARGUMENT, "head_kind is NULL");
+  REQUIRE(Hkv >= 1 && Hkv <= ubs::kMaxKvHeads, UBS_ERR_UNSUPPORTED, "Hkv=%d outside [1, %d]", Hkv,
+          ubs::kMaxKvHeads);
+  dense->n = 0;
+  streaming->n = 0;
+  *streaming_mask = 0;
+  for (int g = 0; g < Hkv; ++g) {
+    REQUIRE(head_kind[g] <= 1, UBS_ERR_INVALID_ARGUMENT, "head_kind[%d]=%d is neither 0 nor 1", g,
+            (int)head_kind[g]);
+    if (head_kind[g]) {
+      streaming->h[streaming->n++] = (int16_t)g;
+      *streaming_mask |= 1ull << g;
+    } else {
+      dense->h[dense->n++] = (int16_t)g;
+    }
+  }
+  return UBS_OK;
+}
+
+int common_heads(int Hq, int Hkv, int D) {
+  REQUIRE(Hq >= 1 && Hkv >= 1, UBS_ERR_INVALID_ARGUMENT, "Hq=%d, Hkv=%d must be positive", Hq, Hkv);
+  REQUIRE(Hq % Hkv == 0, UBS_ERR_INVALID_ARGUMENT, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  REQUIRE(D == 64 || D == 128, UBS_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  return UBS_OK;
+}
+
+int paged_P(int P) {
+  REQUIRE(P > 0, UBS_ERR_INVALID_ARGUMENT, "P=%d must be positive", P);
+  REQUIRE(P == 16 || P == 32 || P == 64 || P == 128, UBS_ERR_UNSUPPORTED,
+          "P=%d (supported: 16, 32, 64, 128)", P);
+  return UBS_OK;
+}
+
+constexpr int kMaxSelectPages = 16384;
+
+}  // namespace
+
+extern "C" {
+
+const char* ubs_last_error(void) { return g_last_error.c_str(); }
+
+int ubs_version(void) { return 100; }
+
+int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                   const int32_t* page_table, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                   int32_t T, const uint8_t* head_kind, const uint8_t* block_mask, int32_t sink_tiles,
+                   int32_t local_tiles, float sm_scale, float* out, float* lse, hipStream_t stream) {
+  int rc = common_heads(Hq, Hkv, D);
+  if (rc) return rc;
+  REQUIRE(L >= 0, UBS_ERR_INVALID_ARGUMENT, "L=%d is negative", L);
+  REQUIRE(T == 64 || T == 128, UBS_ERR_UNSUPPORTED, "T=%d (supported: 64, 128)", T);
+  REQUIRE(P > 0 && P % 16 == 0, UBS_ERR_UNSUPPORTED, "P=%d must be a positive multiple of 16", P);
+  REQUIRE(Hq <= ubs::kMaxQHeads, UBS_ERR_UNSUPPORTED, "Hq=%d above %d", Hq, ubs::kMaxQHeads);
+  REQUIRE(sink_tiles >= 0 && local_tiles >= 0, UBS_ERR_INVALID_ARGUMENT,
+          "sink_tiles=%d, local_tiles=%d must be >= 0", sink_tiles, local_tiles);
+  REQUIRE(sm_scale == sm_scale, UBS_ERR_INVALID_ARGUMENT, "sm_scale is NaN");
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+  if (rc) return rc;
+  if (L == 0) return ok();
+  REQUIRE(q && k_cache && v_cache && page_table && out, UBS_ERR_INVALID_ARGUMENT,
+          "q, k_cache, v_cache, page_table and out must be non-NULL");
+  REQUIRE(dense.n == 0 || block_mask, UBS_ERR_INVALID_ARGUMENT, "block_mask is NULL but a KV head is dense");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), UBS_ERR_INVALID_ARGUMENT,
+          "q, k_cache, v_cache and out must be 16-byte aligned");
+  const int64_t nT = (L + T - 1) / T;
+  REQUIRE(nT * Hq < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large",
+          (long long)(nT * Hq));
+  ubs::PrefillArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.block_mask = block_mask;
+  a.L = L;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.P = P;
+  a.T = T;
+  a.sink_tiles = sink_tiles;
+  a.local_tiles = local_tiles;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse = lse;
+  const int G = Hq / Hkv;
+  int n = 0;
+  for (int d = 0; d < dense.n; ++d)
+    for (int x = 0; x < G; ++x) a.order.h[n++] = (int16_t)(dense.h[d] * G + x);
+  a.order.n_dense = n;
+  for (int d = 0; d < streaming.n; ++d)
+    for (int x = 0; x < G; ++x) a.order.h[n++] = (int16_t)(streaming.h[d] * G + x);
+  a.order.n_total = n;
+  return hip_status(ubs::launch_prefill(a, stream), "sparse_prefill launch");
+}
+
+int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, const int32_t* seq_lens,
+                      int32_t B, int32_t max_pages, int32_t Hkv, int32_t D, int32_t P, int32_t Lp,
+                      const uint8_t* head_kind, ubs_bf16_t* bounds, hipStream_t stream) {
+  REQUIRE(B >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT, "B=%d, max_pages=%d must be >= 0", B, max_pages);
+  REQUIRE(D == 64 || D == 128, UBS_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  int rc = paged_P(P);
+  if (rc) return rc;
+  REQUIRE(Lp > 0 && P % Lp == 0, UBS_ERR_UNSUPPORTED, "Lp=%d must divide P=%d", Lp, P);
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+  if (rc) return rc;
+  if (B == 0 || max_pages == 0 || dense.n == 0) return ok();
+  REQUIRE(k_cache && page_table && seq_lens && bounds, UBS_ERR_INVALID_ARGUMENT,
+          "k_cache, page_table, seq_lens and bounds must be non-NULL");
+  REQUIRE(aligned16(k_cache) && aligned16(bounds), UBS_ERR_INVALID_ARGUMENT,
+          "k_cache and bounds must be 16-byte aligned");
+  ubs::BoundsArgs a{k_cache, page_table, seq_lens, B, max_pages, Hkv, D, P, Lp, dense, bounds};
+  return hip_status(ubs::launch_bounds(a, stream), "build_page_bounds launch");
+}
+
+size_t select_pages_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv) {
+  if (B <= 0 || max_pages <= 0 || Hkv <= 0) return 256;
+  return ((size_t)B * Hkv * max_pages * sizeof(float) + 255) / 256 * 256;
+}
+
+int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* page_table,
+                 const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D,
+                 int32_t P, int32_t Lp, int32_t token_budget, const uint8_t* head_kind, int32_t* selected,
+                 int32_t* num_selected, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = common_heads(Hq, Hkv, D);
+  if (rc) return rc;
+  REQUIRE(B >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT, "B=%d, max_pages=%d must be >= 0", B, max_pages);
+  rc = paged_P(P);
+  if (rc) return rc;
+  REQUIRE(Lp > 0 && P % Lp == 0, UBS_ERR_UNSUPPORTED, "Lp=%d must divide P=%d", Lp, P);
+  REQUIRE(pow2(P / Lp) && P / Lp <= 16, UBS_ERR_UNSUPPORTED, "P/Lp=%d (supported: 1, 2, 4, 8, 16)", P / Lp);
+  REQUIRE(Hq / Hkv <= 16 && pow2(Hq / Hkv), UBS_ERR_UNSUPPORTED, "Hq/Hkv=%d (supported: 1, 2, 4, 8, 16)",
+          Hq / Hkv);
+  REQUIRE(token_budget > 0, UBS_ERR_INVALID_ARGUMENT, "token_budget=%d must be positive", token_budget);
+  REQUIRE(token_budget % P == 0, UBS_ERR_UNSUPPORTED, "token_budget=%d is not a multiple of P=%d", token_budget, P);
+  REQUIRE(max_pages <= kMaxSelectPages, UBS_ERR_UNSUPPORTED, "max_pages=%d above %d", max_pages, kMaxSelectPages);
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  REQUIRE(q && page_table && seq_lens && selected && num_selected, UBS_ERR_INVALID_ARGUMENT,
+          "q, page_table, seq_lens, selected and num_selected must be non-NULL");
+  REQUIRE(dense.n == 0 || bounds, UBS_ERR_INVALID_ARGUMENT, "bounds is NULL but a KV head is dense");
+  REQUIRE(aligned16(q) && (bounds == nullptr || aligned16(bounds)), UBS_ERR_INVALID_ARGUMENT,
+          "q and bounds must be 16-byte aligned");
+  const size_t need = select_pages_workspace_size(B, max_pages, Hkv);
+  REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
+          "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  ubs::SelectArgs a{};
+  a.q = q;
+  a.bounds = bounds;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.max_pages = max_pages;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.P = P;
+  a.Lp = Lp;
+  a.k = token_budget / P;
+  a.dense = dense;
+  a.streaming_mask = smask;
+  a.selected = selected;
+  a.num_selected = num_selected;
+  a.scores = static_cast<float*>(workspace);
+  return hip_status(ubs::launch_select(a, stream), "select_pages launch");
+}
+
+static size_t decode_counter_bytes(int B, int Hkv) { return ((size_t)B * Hkv * 4 + 255) / 256 * 256; }
+
+size_t sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                    int32_t max_selected, int32_t sink_tokens, int32_t local_tokens) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_selected < 0 || sink_tokens < 0 ||
+      local_tokens < 0)
+    return 256;
+  // the split plan depends only on these sizes; all heads dense is the largest case
+  const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, Hkv, P, max_selected, sink_tokens, local_tokens);
+  const ubs::DecodePlan ps = ubs::plan_decode(B, Hkv, 0, P, max_selected, sink_tokens, local_tokens);
+  const int ms = pl.max_splits > ps.max_splits ? pl.max_splits : ps.max_splits;
+  return decode_counter_bytes(B, Hkv) + (size_t)B * Hq * ms * (D + 2) * sizeof(float);
+}
+
+int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                  const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq,
+                  int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind, const int32_t* selected,
+                  const int32_t* num_selected, int32_t max_selected, int32_t sink_tokens, int32_t local_tokens,
+                  float sm_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  int rc = common_heads(Hq, Hkv, D);
+  if (rc) return rc;
+  REQUIRE(B >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT, "B=%d, max_pages=%d must be >= 0", B, max_pages);
+  REQUIRE(P > 0 && P % 16 == 0 && P <= 256, UBS_ERR_UNSUPPORTED, "P=%d must be a multiple of 16 up to 256", P);
+  REQUIRE(Hq / Hkv <= 16 && pow2(Hq / Hkv), UBS_ERR_UNSUPPORTED, "Hq/Hkv=%d (supported: 1, 2, 4, 8, 16)",
+          Hq / Hkv);
+  REQUIRE(max_selected >= 0 && sink_tokens >= 0 && local_tokens >= 0, UBS_ERR_INVALID_ARGUMENT,
+          "max_selected=%d, sink_tokens=%d, local_tokens=%d must be >= 0", max_selected, sink_tokens,
+          local_tokens);
+  REQUIRE(sm_scale == sm_scale, UBS_ERR_INVALID_ARGUMENT, "sm_scale is NaN");
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  REQUIRE(q && k_cache && v_cache && page_table && seq_lens && out, UBS_ERR_INVALID_ARGUMENT,
+          "q, k_cache, v_cache, page_table, seq_lens and out must be non-NULL");
+  REQUIRE(dense.n == 0 || max_selected == 0 || (selected && num_selected), UBS_ERR_INVALID_ARGUMENT,
+          "selected / num_selected are NULL but a KV head is dense");
+  REQUIRE(dense.n == 0 || num_selected, UBS_ERR_INVALID_ARGUMENT, "num_selected is NULL but a KV head is dense");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache), UBS_ERR_INVALID_ARGUMENT,
+          "q, k_cache and v_cache must be 16-byte aligned");
+  const size_t need = sparse_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens);
+  REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
+          "workspace of %zu bytes, need %zu", workspace_bytes, need);
+  const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens);
+  const int64_t blocks = (int64_t)B * (dense.n * pl.splits_dense + streaming.n * pl.splits_stream);
+  REQUIRE(blocks < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large", (long long)blocks);
+  ubs::DecodeArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.selected = selected;
+  a.num_selected = num_selected;
+  a.B = B;
+  a.max_pages = max_pages;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.P = P;
+  a.max_selected = max_selected;
+  a.sink = sink_tokens;
+  a.local = local_tokens;
+  a.sm_scale = sm_scale;
+  a.dense = dense;
+  a.streaming = streaming;
+  a.splits_dense = pl.splits_dense;
+  a.splits_stream = pl.splits_stream;
+  a.chunks_per_wave = pl.chunks_per_wave;
+  a.out = out;
+  a.lse = lse;
+  a.counters = static_cast<uint32_t*>(workspace);
+  a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(B, Hkv));
+  a.max_splits = pl.max_splits;
+  return hip_status(ubs::launch_decode(a, stream), "sparse_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,355 @@
+// sparse_decode: GQA decode attention over the kept pages of dense KV heads, or the
+// sink + local tokens of streaming KV heads (blog "LServe -- Decode Phase" and
+// Figure 2: token-level attention only inside the selected pages; LServe abstract:
+// streaming heads in decode as well).
+//
+// Work split: (sequence b, KV head g, split s) per 256-thread work-group. The key set
+// of (b, g) is a list of chunks, each a token range inside one physical page (a
+// selected page, or a piece of the sink / local window); wave w of split s takes
+// chunks (s*4 + w)*cpw ... + cpw - 1. Inside a wave:
+//   S = Q_g K^T  : bf16 MFMA 16x16x32 (rows = the G query heads, columns = 16 keys),
+//                  K rows read straight from HBM, 64 contiguous bytes per lane;
+//   online softmax in the log2 domain (fp32);
+//   O += P V     : fp32 FMAs, each lane owning 8 channels of one key row, V read with
+//                  16-byte coalesced loads, P broadcast through LDS.
+// Partial (max, sum, output) triples of the 4 waves are merged through LDS; the
+// work-group writes one partial per split, and the last-arriving work-group of
+// (b, g) merges all splits (log-sum-exp combine staged in LDS) into the output.
+#include "common.h"
+#include "launch.h"
+
+namespace ubs {
+
+constexpr int kMaxSplits = 128;
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+struct Chunk {
+  int page;        // physical page id, -1 if none
+  int t0, t1;      // valid token range [t0, t1) in sequence positions
+  int row_base;    // sequence position of row 0 of the page
+};
+
+__device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streaming, int b, int g, int c,
+                                              int L, int nsel) {
+  Chunk ch{-1, 0, 0, 0};
+  const int P = a.P;
+  const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
+  if (!streaming) {
+    if (c >= nsel) return ch;
+    const int j = a.selected[((int64_t)b * a.Hkv + g) * a.max_selected + c];
+    if (j < 0 || (int64_t)j * P >= L) return ch;
+    ch.page = pt[j];
+    ch.row_base = j * P;
+    ch.t0 = j * P;
+    ch.t1 = min(j * P + P, L);
+    return ch;
+  }
+  const int A = min(a.sink, L);
+  const int Bs = max(A, L - a.local);
+  const int nsc = (A + P - 1) / P;
+  if (c < nsc) {
+    ch.page = pt[c];
+    ch.row_base = c * P;
+    ch.t0 = c * P;
+    ch.t1 = min(c * P + P, A);
+    return ch;
+  }
+  if (L <= Bs) return ch;
+  const int fl = Bs / P;
+  const int nlc = (L - 1) / P - fl + 1;
+  const int cl = c - nsc;
+  if (cl >= nlc) return ch;
+  const int j = fl + cl;
+  ch.page = pt[j];
+  ch.row_base = j * P;
+  ch.t0 = max(j * P, Bs);
+  ch.t1 = min(j * P + P, L);
+  return ch;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
+  constexpr int KK = D / 32;   // QK MFMA steps
+  constexpr int CH = D / 8;    // lanes per V row
+  constexpr int TG = 64 / CH;  // token groups in P.V
+  constexpr int GL = (G + 3) / 4;  // 16-lane groups that hold query heads
+  __shared__ float p_lds[4][64][G];
+  __shared__ float w_m[4][G], w_l[4][G];
+  __shared__ float w_o[4][G][D];
+  __shared__ float c_m[G][kMaxSplits], c_w[G][kMaxSplits];
+  __shared__ int last_flag;
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+
+  // ---- which (b, g, split)
+  const int per_b = a.dense.n * a.splits_dense + a.streaming.n * a.splits_stream;
+  const int b = blockIdx.x / per_b;
+  int r = blockIdx.x % per_b;
+  bool streaming;
+  int g, split, n_splits;
+  if (r < a.dense.n * a.splits_dense) {
+    streaming = false;
+    g = a.dense.h[r / a.splits_dense];
+    split = r % a.splits_dense;
+    n_splits = a.splits_dense;
+  } else {
+    r -= a.dense.n * a.splits_dense;
+    streaming = true;
+    g = a.streaming.h[r / a.splits_stream];
+    split = r % a.splits_stream;
+    n_splits = a.splits_stream;
+  }
+  const int L = a.seq_lens[b];
+  const int nsel = streaming ? 0 : min(a.num_selected[(int64_t)b * a.Hkv + g], a.max_selected);
+  const float scale_log2 = a.sm_scale * kLog2e;
+
+  // ---- Q as the MFMA A operand: row m = query head (zero rows past G); k-slot group
+  // qg = l/16 holds channels qg*D/4 + kk*8 + [0, 8) for step kk.
+  const int m = lane & 15;
+  const int qg = lane >> 4;
+  bf16x8 qa[KK];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + m) * D + qg * (D / 4);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qa[kk] = as_bf16x8((m < G) ? ld16(qrow + kk * 8) : u32x4{0, 0, 0, 0});
+  }
+
+  float m_run[4];   // running max of heads 4*qg + i (lane-replicated within a 16-lane group)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m_run[i] = kNegInf;
+  float o[G][8];
+  float lsum[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    lsum[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  }
+  const int cc = lane % CH;
+  const int tg = lane / CH;
+  const int64_t head_stride = (int64_t)a.P * D;  // one (page, KV head) slab
+
+  for (int t = 0; t < a.chunks_per_wave; ++t) {
+    const int c = (split * 4 + wave) * a.chunks_per_wave + t;
+    const Chunk ch = decode_chunk(a, streaming, b, g, c, L, nsel);
+    if (ch.page < 0) continue;  // wave-uniform
+    const uint16_t* kslab = a.k_cache + ((int64_t)ch.page * a.Hkv + g) * head_stride;
+    const uint16_t* vslab = a.v_cache + ((int64_t)ch.page * a.Hkv + g) * head_stride;
+    const int r_lo = ch.t0 - ch.row_base, r_hi = ch.t1 - ch.row_base;   // valid rows [r_lo, r_hi)
+    for (int r0 = (r_lo / 64) * 64; r0 < r_hi; r0 += 64) {
+      // ---- S for up to 4 blocks of 16 rows
+      f32x4 s[4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int rb = r0 + blk * 16;
+        s[blk] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+        if (rb < r_hi && rb + 16 > r_lo) {   // wave-uniform
+          const int row = rb + m;
+          const uint16_t* krow = kslab + (int64_t)row * D + qg * (D / 4);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(ld16(krow + kk * 8)), acc, 0, 0, 0);
+          const bool ok = row >= r_lo && row < r_hi;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
+        }
+      }
+      // ---- segment max per head (heads 4*qg + i), then running max and weights
+      float alpha_i[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mx = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
+#pragma unroll
+        for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, shfl_xor(mx, o2));
+        const float mn = fmaxf(m_run[i], mx);
+        alpha_i[i] = rescale_factor(m_run[i], mn);
+        m_run[i] = mn;
+      }
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = qg * 4 + i;
+          if (h < G) p_lds[wave][blk * 16 + m][h] = softmax_weight(s[blk][i], m_run[i]);
+        }
+      wave_sync_lds();
+      // ---- broadcast rescale factors and apply
+      float alpha[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) alpha[h] = readlane_f(alpha_i[h & 3], 16 * (h >> 2));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        lsum[h] *= alpha[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+      }
+      // ---- O += P V over the segment's rows tg, tg + TG, ...
+#pragma unroll 4
+      for (int rr = tg; rr < 64; rr += TG) {
+        const int row = r0 + rr;
+        if (row < r_lo || row >= r_hi) continue;
+        const u32x4 v = ld16(vslab + (int64_t)row * D + cc * 8);
+        float vf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[2 * e] = bf16_lo(v[e]);
+          vf[2 * e + 1] = bf16_hi(v[e]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = p_lds[wave][rr][h];
+          lsum[h] += p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+        }
+      }
+      wave_sync_lds();
+    }
+  }
+
+  // ---- reduce the token groups of the wave
+#pragma unroll
+  for (int x = CH; x < 64; x <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      lsum[h] += shfl_xor(lsum[h], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] += shfl_xor(o[h][e], x);
+    }
+  }
+  // ---- stage the wave's partial in LDS
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float mh = readlane_f(m_run[h & 3], 16 * (h >> 2));
+    if (lane == 0) {
+      w_m[wave][h] = mh;
+      w_l[wave][h] = lsum[h];
+    }
+    if (tg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w_o[wave][h][cc * 8 + e] = o[h][e];
+    }
+  }
+  (void)GL;
+  __syncthreads();
+
+  // ---- merge the 4 waves: element (h, c) per thread
+  const bool single = (n_splits == 1);
+  float* part = a.partials;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, c = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, w_m[w][h]);
+    float O = 0.f, S = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = fast_exp2(w_m[w][h] - M);
+        O = fmaf(f, w_o[w][h][c], O);
+        S = fmaf(f, w_l[w][h], S);
+      }
+    }
+    const int64_t qh = (int64_t)b * a.Hq + (int64_t)g * G + h;
+    if (single) {
+      a.out[qh * D + c] = (S > 0.f) ? O / S : 0.f;
+      if (c == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
+    } else {
+      float* pp = part + (qh * a.max_splits + split) * (D + 2);
+      pp[c] = O;
+      if (c == 0) {
+        pp[D] = M;
+        pp[D + 1] = S;
+      }
+    }
+  }
+  if (single) return;
+
+  // ---- arrival counter: the last work-group of (b, g) merges every split
+  __threadfence();
+  __syncthreads();
+  uint32_t* counter = a.counters + (int64_t)b * a.Hkv + g;
+  if (tid == 0) last_flag = (atomicAdd(counter, 1u) == (uint32_t)(n_splits - 1));
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  for (int idx = tid; idx < G * n_splits; idx += 256) {
+    const int h = idx / n_splits, sp = idx % n_splits;
+    const int64_t qh = (int64_t)b * a.Hq + (int64_t)g * G + h;
+    const float* pp = part + (qh * a.max_splits + sp) * (D + 2);
+    c_m[h][sp] = __builtin_nontemporal_load(pp + D);
+    c_w[h][sp] = __builtin_nontemporal_load(pp + D + 1);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, c = idx % D;
+    const int64_t qh = (int64_t)b * a.Hq + (int64_t)g * G + h;
+    float M = kNegInf;
+    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, c_m[h][sp]);
+    float O = 0.f, S = 0.f;
+    if (M != kNegInf) {
+      for (int sp = 0; sp < n_splits; ++sp) {
+        const float f = fast_exp2(c_m[h][sp] - M);
+        const float* pp = part + (qh * a.max_splits + sp) * (D + 2);
+        O = fmaf(f, __builtin_nontemporal_load(pp + c), O);
+        S = fmaf(f, c_w[h][sp], S);
+      }
+    }
+    a.out[qh * D + c] = (S > 0.f) ? O / S : 0.f;
+    if (c == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
+  }
+  if (tid == 0) *counter = 0u;
+}
+
+DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local) {
+  DecodePlan pl{};
+  pl.chunks_dense = max_selected;
+  pl.chunks_stream = (sink + P - 1) / P + (local + P - 1) / P + 1;
+  // one chunk per wave unless the split count would exceed what a work-group can merge
+  int cpw = 1;
+  for (;;) {
+    const int sd = n_dense > 0 ? (pl.chunks_dense + 4 * cpw - 1) / (4 * cpw) : 1;
+    const int ss = (Hkv - n_dense) > 0 ? (pl.chunks_stream + 4 * cpw - 1) / (4 * cpw) : 1;
+    if ((sd <= kMaxSplits && ss <= kMaxSplits) || cpw >= (1 << 20)) {
+      pl.chunks_per_wave = cpw;
+      pl.splits_dense = sd < 1 ? 1 : sd;
+      pl.splits_stream = ss < 1 ? 1 : ss;
+      break;
+    }
+    cpw *= 2;
+  }
+  pl.max_splits = pl.splits_dense > pl.splits_stream ? pl.splits_dense : pl.splits_stream;
+  (void)B;
+  return pl;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  const int per_b = a.dense.n * a.splits_dense + a.streaming.n * a.splits_stream;
+  const int64_t blocks = (int64_t)a.B * per_b;
+  if (blocks == 0) return hipSuccess;
+  const int G = a.Hq / a.Hkv;
+#define UBS_DECODE(DD, GG)                                                                     \
+  if (a.D == DD && G == GG) {                                                                  \
+    hipLaunchKernelGGL((decode_kernel<DD, GG>), dim3((unsigned)blocks), dim3(256), 0, s, a);   \
+    return hipGetLastError();                                                                  \
+  }
+  UBS_DECODE(64, 1) UBS_DECODE(64, 2) UBS_DECODE(64, 4) UBS_DECODE(64, 8) UBS_DECODE(64, 16)
+  UBS_DECODE(128, 1) UBS_DECODE(128, 2) UBS_DECODE(128, 4) UBS_DECODE(128, 8) UBS_DECODE(128, 16)
+#undef UBS_DECODE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ubs

@@ -1,0 +1,89 @@
+// Host-side launch descriptors shared by the C ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ubs {
+
+// A small list of head indices passed by value as a kernel argument.
+struct HeadList {
+  int n;
+  int16_t h[64];
+};
+
+// Query-head order for the prefill grid: dense heads first, then streaming.
+struct QHeadOrder {
+  int n_dense;
+  int n_total;
+  int16_t h[256];
+};
+
+struct BoundsArgs {
+  const uint16_t* k_cache;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int B, max_pages, Hkv, D, P, Lp;
+  HeadList dense;
+  uint16_t* bounds;
+};
+
+struct SelectArgs {
+  const uint16_t* q;
+  const uint16_t* bounds;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int B, max_pages, Hq, Hkv, D, P, Lp, k;
+  HeadList dense;
+  uint64_t streaming_mask;
+  int32_t* selected;
+  int32_t* num_selected;
+  float* scores;  // workspace [B][Hkv][max_pages]
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* selected;
+  const int32_t* num_selected;
+  int B, max_pages, Hq, Hkv, D, P, max_selected, sink, local;
+  float sm_scale;
+  HeadList dense, streaming;
+  int splits_dense, splits_stream, chunks_per_wave;
+  float* out;
+  float* lse;
+  uint32_t* counters;  // workspace [B][Hkv]
+  float* partials;     // workspace [B][Hq][max_splits][D + 2]
+  int max_splits;
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const uint8_t* block_mask;
+  int L, Hq, Hkv, D, P, T, sink_tiles, local_tiles;
+  float sm_scale;
+  QHeadOrder order;
+  float* out;
+  float* lse;
+};
+
+// Decode split planning (shared by the workspace query and the launch).
+struct DecodePlan {
+  int chunks_dense, chunks_stream;  // upper bounds of key chunks per (b, KV head)
+  int chunks_per_wave;
+  int splits_dense, splits_stream, max_splits;
+};
+DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local);
+
+hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+}  // namespace ubs

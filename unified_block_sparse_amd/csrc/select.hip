@@ -1,0 +1,270 @@
+// select_pages: query-aware page scores and top-k page selection for one decode
+// step (blog "LServe -- Decode Phase" and Figure 2; LServe abstract: hierarchical,
+// query-centric page selection under a constant page budget).
+//
+// Scoring. For sub-page u with channel-wise key bounds kmin/kmax and query head h,
+// the Quest bound sum_c max(q_c kmin_c, q_c kmax_c) equals, term by term,
+// q-_c kmin_c + q+_c kmax_c with q+ = max(q, 0) and q- = min(q, 0). Written over the
+// 2D-long record [kmin | kmax] that is one dot product with [q- | q+], so a group of
+// 16 sub-page records times the G query heads of a KV head is one 16x16x(2D)
+// product. bf16 x bf16 products are exact in fp32, and the kernel streams the bounds
+// straight from HBM into the MFMA B operand (16-byte loads, 64 contiguous bytes per
+// record per lane group).
+//
+// Top-k. One work-group per (sequence, KV head) finds the k-th largest score by a
+// bitwise binary search over order-preserving 32-bit keys (counts by wave ballots),
+// breaks ties toward the lower page index and compacts the kept indices in
+// ascending order with block-wide prefix sums.
+#include "common.h"
+#include "launch.h"
+
+namespace ubs {
+
+__device__ __forceinline__ uint32_t neg_part_bf16x2(uint32_t w) {
+  // keep each bf16 half whose sign bit is set (min(x, 0)), zero the others
+  uint32_t lo = (w & 0x8000u) ? (w & 0xffffu) : 0u;
+  uint32_t hi = (w & 0x80000000u) ? (w & 0xffff0000u) : 0u;
+  return lo | hi;
+}
+__device__ __forceinline__ uint32_t pos_part_bf16x2(uint32_t w) {
+  uint32_t lo = (w & 0x8000u) ? 0u : (w & 0xffffu);
+  uint32_t hi = (w & 0x80000000u) ? 0u : (w & 0xffff0000u);
+  return lo | hi;
+}
+
+// Grid: blockIdx.x = ((b * n_dense) + dense index) * chunks + chunk. Each wave scores
+// `gpw` groups of 16 consecutive sub-pages of its (b, g); with U = P/Lp sub-pages per
+// page a group covers 16/U whole pages.
+template <int D, int U, int G>
+__global__ __launch_bounds__(256) void score_kernel(const uint16_t* __restrict__ q,
+                                                    const uint16_t* __restrict__ bounds,
+                                                    const int32_t* __restrict__ page_table,
+                                                    const int32_t* __restrict__ seq_lens,
+                                                    int max_pages, int Hq, int Hkv, int P, int Lp,
+                                                    HeadList dense, int chunks, int gpw,
+                                                    float* __restrict__ scores) {
+  constexpr int KK = D / 16;  // MFMA steps over the 2D-long record (K = 32 each)
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x % chunks;
+  const int bd = blockIdx.x / chunks;
+  const int di = bd % dense.n;
+  const int b = bd / dense.n;
+  const int g = dense.h[di];
+  const int L = seq_lens[b];
+  const int n_pages = (L + P - 1) / P;
+  const int n_sub = n_pages * U;
+  const int first_group = (chunk * 4 + wave) * gpw;
+  if (first_group * 16 >= n_sub) return;
+
+  // A operand: row m = query head of the group, k-slot (l/16)*8 + i of step kk maps
+  // to record element kk*32 + (l/16)*8 + i.
+  const int m = lane & 15;
+  const int qg = lane >> 4;
+  bf16x8 a[KK];
+  {
+    u32x4 qv[D / 32];
+    const uint16_t* qrow = q + ((int64_t)b * Hq + (int64_t)g * G + m) * D + qg * 8;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) qv[t] = (m < G) ? ld16(qrow + t * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 w;
+      if (kk < D / 32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = neg_part_bf16x2(qv[kk][e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pos_part_bf16x2(qv[kk - D / 32][e]);
+      }
+      a[kk] = as_bf16x8(w);
+    }
+  }
+
+  const int32_t* pt = page_table + (int64_t)b * max_pages;
+  float* out = scores + ((int64_t)b * Hkv + g) * max_pages;
+  for (int t = 0; t < gpw; ++t) {
+    const int grp = first_group + t;
+    if (grp * 16 >= n_sub) break;  // wave-uniform
+    const int s = grp * 16 + m;   // this lane's sub-page (B column)
+    const int j = s / U;
+    const int u = s % U;
+    const bool ok = (s < n_sub) && (j * P + u * Lp < L);
+    u32x4 bv[KK];
+    if (ok) {
+      const uint16_t* rec = bounds + (((int64_t)pt[j] * Hkv + g) * U + u) * (2 * D) + qg * 8;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) bv[kk] = ld16(rec + kk * 32);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) bv[kk] = u32x4{0, 0, 0, 0};
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kk], as_bf16x8(bv[kk]), acc, 0, 0, 0);
+    // acc[i] = bound of query head 4*(l/16)+i on sub-page l%16
+    float v = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (qg * 4 + i < G) v = fmaxf(v, acc[i]);
+    if (G > 4) v = fmaxf(v, shfl_xor(v, 16));
+    if (G > 8) v = fmaxf(v, shfl_xor(v, 32));
+    if (!ok) v = kNegInf;
+#pragma unroll
+    for (int o = 1; o < U; o <<= 1) v = fmaxf(v, shfl_xor(v, o));
+    if (lane < 16 && (u == 0) && j < n_pages) out[j] = v;
+  }
+}
+
+// ----------------------------------------------------------------------------- top-k
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int& total) {
+  const int lane = lane_id(), w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tmp[i];
+    base += (i < w) ? t : 0;
+    total += t;
+  }
+  __syncthreads();
+  return base + x - v;
+}
+
+// One 256-thread work-group per (b, KV head). Thread t owns pages t*EPT .. t*EPT+EPT-1,
+// so thread order is page order.
+template <int EPT>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ scores,
+                                                   const int32_t* __restrict__ seq_lens,
+                                                   int max_pages, int Hkv, int P, int k,
+                                                   uint64_t streaming_mask,
+                                                   int32_t* __restrict__ selected,
+                                                   int32_t* __restrict__ num_selected) {
+  __shared__ int tmp[4];
+  __shared__ int cnt[2][4];
+  const int bg = blockIdx.x;
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
+  const int tid = threadIdx.x;
+  int32_t* sel = selected + (int64_t)bg * k;
+  const bool streaming = (streaming_mask >> g) & 1ull;
+  const int L = seq_lens[b];
+  const int n = streaming ? 0 : (L + P - 1) / P;
+  if (n <= k) {
+    for (int i = tid; i < k; i += 256) sel[i] = (i < n) ? i : -1;
+    if (tid == 0) num_selected[bg] = n;
+    return;
+  }
+  const float* sc = scores + (int64_t)bg * max_pages;
+  uint32_t key[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int j = tid * EPT + e;
+    key[e] = (j < n) ? float_order_key(sc[j]) : 0u;  // valid keys are > 0
+  }
+  // k-th largest key: the largest tau with #(key >= tau) >= k.
+  uint32_t tau = 0;
+  const int w = tid >> 6, lane = lane_id();
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) c += __popcll(__ballot(key[e] >= cand));
+    const int slot = bit & 1;
+    if (lane == 0) cnt[slot][w] = c;
+    __syncthreads();
+    const int total = cnt[slot][0] + cnt[slot][1] + cnt[slot][2] + cnt[slot][3];
+    if (total >= k) tau = cand;
+  }
+  // #(key > tau) < k <= #(key >= tau): take all keys above tau and the lowest-index ties.
+  int gt = 0, ties = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    gt += key[e] > tau;
+    ties += key[e] == tau;
+  }
+  int n_gt;
+  {
+    int tot;
+    block_exclusive_scan(gt, tmp, tot);
+    n_gt = tot;
+  }
+  int tie_total;
+  int tie_rank = block_exclusive_scan(ties, tmp, tie_total);
+  const int take_ties = k - n_gt;
+  bool keep[EPT];
+  int kept = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    bool kp = key[e] > tau;
+    if (key[e] == tau) {
+      kp = tie_rank < take_ties;
+      ++tie_rank;
+    }
+    keep[e] = kp;
+    kept += kp;
+  }
+  int kept_total;
+  int pos = block_exclusive_scan(kept, tmp, kept_total);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if (keep[e]) sel[pos++] = tid * EPT + e;
+  if (tid == 0) num_selected[bg] = k;
+}
+
+template <int D, int U>
+static hipError_t launch_score_du(const SelectArgs& a, int G, int chunks, int gpw, hipStream_t s) {
+  const dim3 grid((unsigned)(a.B * a.dense.n * chunks));
+#define UBS_SCORE_G(GG)                                                                          \
+  if (G == GG) {                                                                                 \
+    hipLaunchKernelGGL((score_kernel<D, U, GG>), grid, dim3(256), 0, s, a.q, a.bounds,           \
+                       a.page_table, a.seq_lens, a.max_pages, a.Hq, a.Hkv, a.P, a.Lp, a.dense,   \
+                       chunks, gpw, a.scores);                                                   \
+    return hipGetLastError();                                                                    \
+  }
+  UBS_SCORE_G(1) UBS_SCORE_G(2) UBS_SCORE_G(4) UBS_SCORE_G(8) UBS_SCORE_G(16)
+#undef UBS_SCORE_G
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const int G = a.Hq / a.Hkv;
+  const int U = a.P / a.Lp;
+  if (a.dense.n > 0) {
+    // groups of 16 sub-pages per (b, dense g); a wave takes gpw groups, a WG 4 waves
+    const int64_t groups = ((int64_t)a.max_pages * U + 15) / 16;
+    const int gpw = groups >= 256 ? 2 : 1;
+    const int chunks = (int)((groups + 4 * gpw - 1) / (4 * gpw));
+    hipError_t e = hipErrorInvalidValue;
+#define UBS_SCORE_DU(DD, UU) \
+    if (a.D == DD && U == UU) e = launch_score_du<DD, UU>(a, G, chunks, gpw, s);
+    UBS_SCORE_DU(64, 1) UBS_SCORE_DU(64, 2) UBS_SCORE_DU(64, 4) UBS_SCORE_DU(64, 8) UBS_SCORE_DU(64, 16)
+    UBS_SCORE_DU(128, 1) UBS_SCORE_DU(128, 2) UBS_SCORE_DU(128, 4) UBS_SCORE_DU(128, 8) UBS_SCORE_DU(128, 16)
+#undef UBS_SCORE_DU
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid((unsigned)(a.B * a.Hkv));
+  const int need = (a.max_pages + 255) / 256;
+#define UBS_TOPK(E)                                                                               \
+  if (need <= E) {                                                                                \
+    hipLaunchKernelGGL((topk_kernel<E>), grid, dim3(256), 0, s, a.scores, a.seq_lens, a.max_pages, \
+                       a.Hkv, a.P, a.k, a.streaming_mask, a.selected, a.num_selected);            \
+    return hipGetLastError();                                                                     \
+  }
+  UBS_TOPK(1) UBS_TOPK(2) UBS_TOPK(4) UBS_TOPK(8) UBS_TOPK(16) UBS_TOPK(32) UBS_TOPK(64)
+#undef UBS_TOPK
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ubs
