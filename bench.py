@@ -1,0 +1,294 @@
+"""Benchmark of the unified block-sparse attention hot path on one MI355X.
+
+A step is one pass of the whole path on the Llama-3-8B layer workload:
+  sparse_prefill     on prefill_llama8b (L=65536, Hq=32, Hkv=8, D=128, T=128; dense KV heads
+                     0-3 with the mean-pooled top-30% block mask, KV heads 4-7 streaming with
+                     1 sink + 8 local tiles; 707,216 kept 128x128 tiles),
+  build_page_bounds, select_pages, sparse_decode
+                     on decode_llama8b (B=4, L=32768, Hq=32, Hkv=8, D=128, P=64, budget 4096
+                     tokens, streaming 128 sink + 512 local tokens).
+Inputs are synthetic, seeded and resident in HBM before timing starts. The prefill of
+each step streams > 1.5 GB, which evicts the decode step's 41 MB from the caches, so
+every decode step reads cold HBM.
+
+value = 100 * (sum over the step's ops of their roofline time) / (measured step time),
+i.e. the step's speed as a percentage of the MI355X roofline: prefill counted as
+kept-tile flops against dense bf16 MFMA peak, bounds / selection / decode as their
+algorithmic HBM bytes against peak HBM bandwidth.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
+PEAK_HBM_GBPS = 8000.0
+METRIC = "sparse prefill TFLOP/s (kept tiles) + decode KV GB/s, as % of MI355X roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_llama8b_traffic.json")
+KERNEL_SOURCES = ["unified_block_sparse_amd/csrc/prefill.hip", "unified_block_sparse_amd/csrc/common.h",
+                  "unified_block_sparse_amd/csrc/launch.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=16)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- work accounting
+
+def kept_tile_count(c) -> int:
+    """Kept (query head, query tile, KV tile) triples: the tiles the kernel computes."""
+    import torch
+    nT = c.nT
+    total = 0
+    i = torch.arange(nT)
+    lam = (torch.clamp(i + 1, max=c.sink_tiles) +
+           torch.clamp(torch.clamp(i + 1 - c.sink_tiles, min=0), max=c.local_tiles)).sum().item()
+    for h in range(c.Hq):
+        if c.head_kind[h // c.G]:
+            total += int(lam)
+        else:
+            total += int(torch.tril(c.block_mask[h] != 0).sum().item())
+    return total
+
+
+def prefill_flops(c, kept_tiles: int) -> float:
+    return 4.0 * kept_tiles * c.T * c.T * c.D
+
+
+def decode_bytes(d, sel_pages):
+    """Algorithmic HBM bytes of bounds, selection and decode for one decode step.
+
+    bounds:    K rows of dense heads' valid tokens + the bounds written
+    selection: bounds of dense heads' valid sub-pages + q + selected indices
+    decode:    K and V rows of every attended token + q + out
+    """
+    G = d.Hq // d.Hkv
+    row = d.D * 2
+    dense = [g for g in range(d.Hkv) if not d.head_kind[g]]
+    stream = [g for g in range(d.Hkv) if d.head_kind[g]]
+    U = d.P // d.Lp
+    k_dense_tokens = sum(d.seq_lens) * len(dense)
+    n_sub = sum(sum(min(U, math.ceil((min(d.P, L - j * d.P)) / d.Lp)) for j in range(math.ceil(L / d.P)))
+                for L in d.seq_lens) * len(dense)
+    bounds_w = n_sub * 2 * row
+    b_bounds = k_dense_tokens * row + bounds_w
+    q_bytes = d.B * d.Hq * d.D * 2
+    b_select = bounds_w + q_bytes + d.B * d.Hkv * d.k_pages * 4
+    attended = 0
+    for b, L in enumerate(d.seq_lens):
+        for g in dense:
+            attended += sum(min(d.P, L - j * d.P) for j in sel_pages[b][g])
+        A = min(d.sink_tokens, L)
+        attended += len(stream) * (A + L - max(A, L - d.local_tokens))
+    b_decode = attended * 2 * row + q_bytes + d.B * d.Hq * d.D * 4
+    return b_bounds, b_select, b_decode
+
+
+# ----------------------------------------------------------------------------- cpu baseline
+
+def cpu_baseline(c, d, kept_tiles: int, rows_per_head: int, ideal_s: float):
+    """Time the fp64 oracle on a bounded sample of the same step; extrapolate to a step."""
+    import numpy as np
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    def bits(t):
+        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    rng = np.random.default_rng(11)
+    rows = sorted(rng.choice(c.L, size=rows_per_head, replace=False).tolist())
+    q_host = np.zeros(tuple(c.q.shape), dtype=np.uint16)
+    q_host[rows] = bits(c.q[torch.tensor(rows, device=c.q.device)])
+    kb, vb = bits(c.k_cache), bits(c.v_cache)
+    pt, mask = c.page_table.cpu().numpy(), c.block_mask.cpu().numpy()
+    # the oracle gathers the sequence's K/V once per call (fixed), then works per row
+    t0 = time.perf_counter()
+    oracle.prefill_ref(q_host, kb, vb, pt, c.L, c.Hq, c.Hkv, c.D, c.P, c.T, c.head_kind, mask, c.sink_tiles,
+                       c.local_tiles, c.sm_scale, rows=[])
+    t_fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.prefill_ref(q_host, kb, vb, pt, c.L, c.Hq, c.Hkv, c.D, c.P, c.T, c.head_kind, mask, c.sink_tiles,
+                       c.local_tiles, c.sm_scale, rows=rows)
+    t_pf = time.perf_counter() - t0
+    # one of the decode step's sequences, end to end (bounds -> selection -> decode)
+    b0 = [0]
+    dq = bits(d.q[:1])
+    n0 = (d.seq_lens[0] + d.P - 1) // d.P
+    idx = d.page_table[0, :n0].long()
+    dk, dv = bits(d.k_cache[idx]), bits(d.v_cache[idx])
+    dpt = np.arange(n0, dtype=np.int32)[None]
+    t0 = time.perf_counter()
+    sel, _ = oracle.select_ref(dq, dk, dpt, d.seq_lens[:1], d.Hq, d.Hkv, d.P, d.Lp, d.token_budget, d.head_kind)
+    oracle.decode_ref(dq, dk, dv, dpt, d.seq_lens[:1], d.Hq, d.Hkv, d.P, d.head_kind, sel, d.sink_tokens,
+                      d.local_tokens, d.sm_scale, batches=b0)
+    t_dec = time.perf_counter() - t0
+    step_s = t_fixed + max(t_pf - t_fixed, 0.0) * (c.L / len(rows)) + t_dec * d.B
+    return {
+        "value": 100.0 * ideal_s / step_s,
+        "unit": "% of MI355X roofline",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: prefill_llama8b {len(rows)} seeded rows x {c.Hq} heads "
+                   f"({t_pf:.2f} s incl. {t_fixed:.2f} s K/V gather; per-row part extrapolated "
+                   f"x{c.L // len(rows)} to all {c.L} rows) + decode_llama8b "
+                   f"bounds/selection/decode of 1 of {d.B} sequences ({t_dec:.2f} s, x{d.B}); "
+                   f"extrapolated step {step_s:.1f} s"),
+        "step_seconds_extrapolated": step_s,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(every workload here is a single-GPU shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import unified_block_sparse_amd as ubs
+    from workloads import cases
+
+    ubs.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = cases.prefill_llama8b(dev)
+    d = cases.decode_llama8b(dev)
+    kept = kept_tile_count(c)
+    out = torch.empty((c.L, c.Hq, c.D), dtype=torch.float32, device=dev)
+    bnd = torch.zeros((d.num_physical_pages, d.Hkv, d.P // d.Lp, 2, d.D), dtype=torch.bfloat16, device=dev)
+    sel = torch.empty((d.B, d.Hkv, d.k_pages), dtype=torch.int32, device=dev)
+    num = torch.empty((d.B, d.Hkv), dtype=torch.int32, device=dev)
+    dout = torch.empty((d.B, d.Hq, d.D), dtype=torch.float32, device=dev)
+
+    def op_prefill():
+        ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, c.head_kind, c.block_mask, c.sink_tiles,
+                           c.local_tiles, c.T, c.sm_scale, out=out)
+
+    def op_bounds():
+        ubs.build_page_bounds(d.k_cache, d.page_table, d.seq_lens_t, d.head_kind, d.Lp, bounds=bnd)
+
+    def op_select():
+        ubs.select_pages(d.q, bnd, d.page_table, d.seq_lens_t, d.head_kind, d.P, d.token_budget, selected=sel,
+                         num_selected=num)
+
+    def op_decode():
+        ubs.sparse_decode(d.q, d.k_cache, d.v_cache, d.page_table, d.seq_lens_t, d.head_kind, sel, num,
+                          d.sink_tokens, d.local_tokens, d.sm_scale, out=dout)
+
+    ops = [("sparse_prefill", op_prefill), ("build_page_bounds", op_bounds), ("select_pages", op_select),
+           ("sparse_decode", op_decode)]
+    for _ in range(args.warmup):
+        for _, f in ops:
+            f()
+    torch.cuda.synchronize(dev)
+    sel_h, num_h = sel.cpu().tolist(), num.cpu().tolist()
+    sel_pages = [[sel_h[b][g][:num_h[b][g]] for g in range(d.Hkv)] for b in range(d.B)]
+    flops = prefill_flops(c, kept)
+    b_bounds, b_select, b_decode = decode_bytes(d, sel_pages)
+
+    # ---- timed region: K whole steps, events between the ops (same stream as the kernels)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, (_, f) in enumerate(ops):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    per_op = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps * 1e-3
+              for i, (name, _) in enumerate(ops)}
+    ms_per_step = wall / args.steps * 1e3
+    step_s = wall / args.steps
+
+    ideal = {
+        "sparse_prefill": flops / (PEAK_BF16_TFLOPS * 1e12),
+        "build_page_bounds": b_bounds / (PEAK_HBM_GBPS * 1e9),
+        "select_pages": b_select / (PEAK_HBM_GBPS * 1e9),
+        "sparse_decode": b_decode / (PEAK_HBM_GBPS * 1e9),
+    }
+    ideal_s = sum(ideal.values())
+    value = 100.0 * ideal_s / step_s
+
+    t_pf = per_op["sparse_prefill"]
+    achieved = flops / t_pf / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "prefill_kernel<128,128> (sparse_prefill)", "flops_per_launch": flops,
+                "kept_tiles": kept, "avg_launch_ms": round(t_pf * 1e3, 4)}
+    t_dstep = per_op["select_pages"] + per_op["sparse_decode"]
+    breakdown = {
+        name: {"ms": round(per_op[name] * 1e3, 4), "roofline_ms": round(ideal[name] * 1e3, 4),
+               "frac": round(ideal[name] / per_op[name], 4)} for name, _ in ops}
+    breakdown["sparse_prefill"]["tflops"] = round(achieved, 2)
+    breakdown["build_page_bounds"]["gbps"] = round(b_bounds / per_op["build_page_bounds"] / 1e9, 1)
+    breakdown["select_pages"]["gbps"] = round(b_select / per_op["select_pages"] / 1e9, 1)
+    breakdown["sparse_decode"]["gbps"] = round(b_decode / per_op["sparse_decode"] / 1e9, 1)
+    breakdown["decode_step"] = {"ms": round(t_dstep * 1e3, 4), "bytes": b_select + b_decode,
+                                "gbps": round((b_select + b_decode) / t_dstep / 1e9, 1),
+                                "frac": round((b_select + b_decode) / t_dstep / 1e9 / PEAK_HBM_GBPS, 4)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "% of MI355X roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3_8b_layer: prefill_llama8b (L=65536, Hq=32, Hkv=8, D=128, T=128, "
+                               "half KV heads streaming) + decode_llama8b (B=4, L=32768, P=64, budget 4096)",
+                   "prefill_kept_tiles": kept, "prefill_tflop": round(flops / 1e12, 4),
+                   "decode_bytes": b_bounds + b_select + b_decode},
+        "roofline": roofline,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(c, d, kept, args.cpu_rows_per_head, ideal_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,7 +31,7 @@ struct PrefillSmem {
 };
 
 template <int T, int D>
-__global__ __launch_bounds__(2 * T) void prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(2 * T, 2) void prefill_kernel(const PrefillArgs a) {
   constexpr int NW = T / 32;
   constexpr int NT = 64 * NW;
   constexpr int KSTR = PrefillSmem<T, D>::KSTR;
