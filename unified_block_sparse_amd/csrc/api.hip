@@ -95,7 +95,8 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   if (rc) return rc;
   REQUIRE(L >= 0, UBS_ERR_INVALID_ARGUMENT, "L=%d is negative", L);
   REQUIRE(T == 64 || T == 128, UBS_ERR_UNSUPPORTED, "T=%d (supported: 64, 128)", T);
-  REQUIRE(P > 0 && P % 16 == 0, UBS_ERR_UNSUPPORTED, "P=%d must be a positive multiple of 16", P);
+  REQUIRE(P > 0, UBS_ERR_INVALID_ARGUMENT, "P=%d must be positive", P);
+  REQUIRE(pow2(P) && P >= 16 && P <= 4096, UBS_ERR_UNSUPPORTED, "P=%d (supported: powers of two 16..4096)", P);
   REQUIRE(Hq <= ubs::kMaxQHeads, UBS_ERR_UNSUPPORTED, "Hq=%d above %d", Hq, ubs::kMaxQHeads);
   REQUIRE(sink_tiles >= 0 && local_tiles >= 0, UBS_ERR_INVALID_ARGUMENT,
           "sink_tiles=%d, local_tiles=%d must be >= 0", sink_tiles, local_tiles);
@@ -111,6 +112,8 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), UBS_ERR_INVALID_ARGUMENT,
           "q, k_cache, v_cache and out must be 16-byte aligned");
   const int64_t nT = (L + T - 1) / T;
+  REQUIRE(nT <= ubs::kMaxTileList, UBS_ERR_UNSUPPORTED, "L=%d spans %lld tiles of %d (at most %d)", L,
+          (long long)nT, T, ubs::kMaxTileList);
   REQUIRE(nT * Hq < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large",
           (long long)(nT * Hq));
   ubs::PrefillArgs a{};
@@ -125,6 +128,7 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   a.D = D;
   a.P = P;
   a.T = T;
+  a.log2_P = __builtin_ctz((unsigned)P);
   a.sink_tiles = sink_tiles;
   a.local_tiles = local_tiles;
   a.sm_scale = sm_scale;

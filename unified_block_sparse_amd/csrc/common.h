@@ -18,6 +18,8 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // Largest KV-head count a head-kind bitmask can describe.
 constexpr int kMaxKvHeads = 64;
 constexpr int kMaxQHeads = 256;
+// Longest kept-tile list one prefill work-group holds (query tiles per sequence).
+constexpr int kMaxTileList = 4096;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -67,6 +67,7 @@ struct PrefillArgs {
   const int32_t* page_table;
   const uint8_t* block_mask;
   int L, Hq, Hkv, D, P, T, sink_tiles, local_tiles;
+  int log2_P;
   float sm_scale;
   QHeadOrder order;
   float* out;
