@@ -97,11 +97,11 @@ def prefill_ref(q_bits, k_cache_bits, v_cache_bits, page_table, L: int, Hq: int,
     G = Hq // Hkv
     rows = list(range(L)) if rows is None else [int(r) for r in rows]
     heads = list(range(Hq)) if heads is None else [int(h) for h in heads]
-    Kc = bf16_to_f64(k_cache_bits)
-    Vc = bf16_to_f64(v_cache_bits)
-    K = tokens_of_sequence(Kc, page_table, L, P)            # [L, Hkv, D]
-    V = tokens_of_sequence(Vc, page_table, L, P)
-    Q = bf16_to_f64(q_bits)                                  # [L, Hq, D]
+    # gather the sequence's tokens first, then decode only those (exact either way)
+    K = bf16_to_f64(tokens_of_sequence(np.asarray(k_cache_bits), page_table, L, P))  # [L, Hkv, D]
+    V = bf16_to_f64(tokens_of_sequence(np.asarray(v_cache_bits), page_table, L, P))
+    q_rows = np.asarray(q_bits)[rows]                        # [n_rows, Hq, D] bits
+    row_pos = {r: n for n, r in enumerate(rows)}
     mask = np.asarray(block_mask)
     out = np.zeros((len(rows), len(heads), D))
     lse = np.full((len(heads), len(rows)), -math.inf)
@@ -116,7 +116,8 @@ def prefill_ref(q_bits, k_cache_bits, v_cache_bits, page_table, L: int, Hq: int,
             keys = np.concatenate([np.arange(j * T, min((j + 1) * T, L)) for j in kept]) \
                 if kept else np.zeros(0, dtype=np.int64)
             rr = np.array([r for _, r in members])
-            s = sm_scale * (Q[rr, h, :] @ K[keys, g, :].T)   # [rows, keys]
+            Qh = bf16_to_f64(q_rows[[row_pos[r] for r in rr], h, :])
+            s = sm_scale * (Qh @ K[keys, g, :].T)              # [rows, keys]
             allowed = keys[None, :] <= rr[:, None]
             for (ri, r), srow, arow in zip(members, s, allowed):
                 o, z = _softmax_attend(srow[arow], V[keys[arow], g, :])
@@ -155,7 +156,7 @@ def bounds_ref(k_cache_bits, page_table, seq_lens, P: int, Lp: int, head_kind,
     1 = max) and a bool [NP, Hkv, P/Lp] marking the entries that are defined.
     pages restricts the work to the given (b, j) pairs.
     """
-    Kc = bf16_to_f64(k_cache_bits)
+    Kc = np.asarray(k_cache_bits)                            # bits; decoded per sub-page
     NP, Hkv, _, D = Kc.shape
     U = P // Lp
     values = np.zeros((NP, Hkv, U, 2, D))
@@ -174,7 +175,7 @@ def bounds_ref(k_cache_bits, page_table, seq_lens, P: int, Lp: int, head_kind,
                 lo, hi = u * Lp, min((u + 1) * Lp, valid)
                 if hi <= lo:
                     continue
-                kk = Kc[p, g, lo:hi, :]
+                kk = bf16_to_f64(Kc[p, g, lo:hi, :])
                 values[p, g, u, 0] = kk.min(axis=0)
                 values[p, g, u, 1] = kk.max(axis=0)
                 defined[p, g, u] = True
@@ -280,8 +281,8 @@ def decode_ref(q_bits, k_cache_bits, v_cache_bits, page_table, seq_lens, Hq: int
     key set gives out = 0 and lse = -inf. selected maps (b, g) of dense heads to page
     indices. Returns (out [nb, Hq, D], lse [nb, Hq]) for the batches given."""
     G = Hq // Hkv
-    Kc = bf16_to_f64(k_cache_bits)
-    Vc = bf16_to_f64(v_cache_bits)
+    Kc = np.asarray(k_cache_bits)                            # bits; decoded per key set
+    Vc = np.asarray(v_cache_bits)
     Q = bf16_to_f64(q_bits)
     pt = np.asarray(page_table)
     lens = [int(x) for x in seq_lens]
@@ -295,8 +296,8 @@ def decode_ref(q_bits, k_cache_bits, v_cache_bits, page_table, seq_lens, Hq: int
             streaming = bool(head_kind[g])
             keys = decode_keys_ref(L, P, streaming, [] if streaming else selected[(b, g)],
                                    sink_tokens, local_tokens)
-            Kt = tokens_of_sequence(Kc, pt[b], L, P, keys)[:, g, :]
-            Vt = tokens_of_sequence(Vc, pt[b], L, P, keys)[:, g, :]
+            Kt = bf16_to_f64(tokens_of_sequence(Kc, pt[b], L, P, keys)[:, g, :])
+            Vt = bf16_to_f64(tokens_of_sequence(Vc, pt[b], L, P, keys)[:, g, :])
             for h in range(g * G, (g + 1) * G):
                 o, z = _softmax_attend(sm_scale * (Kt @ Q[b, h]), Vt)
                 out[bi, h] = o
