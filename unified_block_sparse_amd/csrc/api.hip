@@ -134,14 +134,8 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   a.sm_scale = sm_scale;
   a.out = out;
   a.lse = lse;
-  const int G = Hq / Hkv;
-  int n = 0;
-  for (int d = 0; d < dense.n; ++d)
-    for (int x = 0; x < G; ++x) a.order.h[n++] = (int16_t)(dense.h[d] * G + x);
-  a.order.n_dense = n;
-  for (int d = 0; d < streaming.n; ++d)
-    for (int x = 0; x < G; ++x) a.order.h[n++] = (int16_t)(streaming.h[d] * G + x);
-  a.order.n_total = n;
+  a.dense_kv_mask = ~smask & (Hkv == 64 ? ~0ull : ((1ull << Hkv) - 1));
+  a.n_dense_kv = dense.n;
   return hip_status(ubs::launch_prefill(a, stream), "sparse_prefill launch");
 }
 

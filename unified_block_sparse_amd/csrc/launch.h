@@ -12,12 +12,6 @@ struct HeadList {
   int16_t h[64];
 };
 
-// Query-head order for the prefill grid: dense heads first, then streaming.
-struct QHeadOrder {
-  int n_dense;
-  int n_total;
-  int16_t h[256];
-};
 
 struct BoundsArgs {
   const uint16_t* k_cache;
@@ -69,7 +63,8 @@ struct PrefillArgs {
   int L, Hq, Hkv, D, P, T, sink_tiles, local_tiles;
   int log2_P;
   float sm_scale;
-  QHeadOrder order;
+  uint64_t dense_kv_mask;  // bit g set: KV head g is dense
+  int n_dense_kv;
   float* out;
   float* lse;
 };

@@ -4,22 +4,30 @@
 // plus a local window and never visit the tiles in between; one kernel serves both
 // head kinds).
 //
-// One work-group per (query head h, query tile i), T/32 waves of 32 query rows each,
-// two work-groups resident per CU. Dense heads compact their mask row into an LDS list
-// of kept tiles once (block-wide scan); streaming heads enumerate the Lambda set
-// arithmetically. Skipped tiles are never loaded.
+// One work-group per (query head h, query tile i), one work-group per CU. Its 2T/32
+// waves form T/32 query groups of 32 rows times 2 key halves: wave (qg, kh) owns
+// query rows qg*32..+32 against keys kh*T/2..+T/2 of every kept tile, with its own
+// running (max, sum, O); the two halves merge through LDS at the end.
 //
-// Data movement per kept KV tile j (K and V each have one T x D bf16 LDS buffer):
-//   V_j    global -> LDS by direct-to-LDS 16-byte loads, issued before S is computed
-//   S^T    = K_j Q^T on bf16 MFMA 32x32x16 (Q resident in registers as the B operand)
-//   softmax per query row in the log2 domain; causal cut on the diagonal tile only
-//   K_next global -> LDS, issued once every wave has finished reading K_j
-//   O^T   += V_j^T P^T on bf16 MFMA 32x32x16; V_j^T is read from the row-major tile
-//            with the LDS transpose read (ds_read_b64_tr_b16), P stays in registers
-// so each tile's loads overlap the other half of the previous tile's math. Rows of
-// both buffers are XOR-swizzled at 16-byte granularity so the MFMA operand reads are
-// free of bank conflicts; the direct-to-LDS loads write the swizzled layout by
+// Kept tiles: dense heads compact their mask row into an LDS list once (block-wide
+// scan); streaming heads enumerate the Lambda set arithmetically. Skipped tiles are
+// never loaded.
+//
+// Per kept tile (K and V are double-buffered in LDS, T x D bf16 each):
+//   K, V:  global -> LDS with direct-to-LDS 16-byte loads, two phases ahead of use
+//   S^T  = K Q^T on bf16 MFMA 32x32x16 (Q resident in registers as the B operand)
+//   online softmax per query row in the log2 domain; causal cut on the diagonal tile
+//   O^T += V^T P^T on bf16 MFMA 32x32x16; V^T comes from the row-major tile through
+//          the LDS transpose read (ds_read_b64_tr_b16); P stays in registers
+// The two waves that share a SIMD (one per key half) run these in ping-pong: while
+// one issues matrix work the other runs its softmax (see the schedule below).
+// Rows of both buffers are XOR-swizzled at 16-byte granularity so the operand reads
+// are free of bank conflicts; the direct-to-LDS loads write the swizzled layout by
 // choosing which global chunk each lane fetches.
+//
+// Work order: dense heads first, query tiles from the last (longest rows) to the
+// first; blocks are renumbered so that the G heads of one KV group at one query tile
+// run back to back on the same XCD and share its L2 for their K/V tiles.
 #include "common.h"
 #include "launch.h"
 
@@ -40,7 +48,7 @@ __device__ __forceinline__ int v_swz(int r) {
 
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
-// Block-wide exclusive scan of one int per thread (NT threads, NT/64 waves).
+// Block-wide exclusive scan of one int per thread (NT threads).
 template <int NT>
 __device__ __forceinline__ int block_scan(int v, int* tmp, int& total) {
   const int lane = lane_id(), w = threadIdx.x >> 6;
@@ -64,78 +72,113 @@ __device__ __forceinline__ int block_scan(int v, int* tmp, int& total) {
 }
 
 template <int T, int D>
-__global__ __launch_bounds__(2 * T, 2) void prefill_kernel(const PrefillArgs a) {
-  constexpr int NW = T / 32;          // waves
-  constexpr int CPR = D / 8;          // 16-byte chunks per row
-  constexpr int IT = D / 16;          // direct-to-LDS loads per lane per tile
-  constexpr int QK = D / 16;          // MFMA steps over channels
-  constexpr int TB = T / 32;          // 32-key blocks per tile
-  constexpr int CB = D / 32;          // 32-channel blocks of the output
+struct PrefillShared {
+  uint16_t k[2][T * D];
+  uint16_t v[2][T * D];
+  int16_t tlist[kMaxTileList];
+  int scan_tmp[16];
+};
+
+template <int T, int D>
+__global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) {
+  constexpr int QG = T / 32;          // query groups of 32 rows
+  constexpr int NW = 2 * QG;          // waves: query group x key half
   constexpr int NT = 64 * NW;         // threads
+  constexpr int KH = T / 2;           // keys per half tile
+  constexpr int TBH = KH / 32;        // 32-key blocks per half
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int IT = T * CPR / NT;    // direct-to-LDS loads per lane per tile and tensor
+  constexpr int RPI = 64 / CPR;       // rows per load instruction
+  constexpr int QK = D / 16;          // MFMA steps over channels
+  constexpr int CB = D / 32;          // 32-channel blocks of the output
   constexpr int MB = kMaxTileList / NT;  // mask bytes scanned per thread
-  __shared__ __attribute__((aligned(1024))) uint16_t ks[T * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t vs[T * D];
-  __shared__ int16_t tlist[kMaxTileList];
-  __shared__ int scan_tmp[NW];
+  __shared__ __attribute__((aligned(1024))) PrefillShared<T, D> sm;
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
+  const int qgrp = wave % QG;
+  const int kh = wave / QG;
   const int L = a.L;
   const int G = a.Hq / a.Hkv;
   const int nT = (L + T - 1) / T;
 
-  // ---- (head, query tile): dense heads first, longest rows (largest i) first
-  int idx = blockIdx.x;
-  const int nd = a.order.n_dense;
+  // ---- work item: XCD-aware renumbering of the block index (blocks go to XCDs
+  // round-robin), then dense heads first, query tiles from the last to the first,
+  // the G heads of a KV group adjacent.
+  const int nblk = gridDim.x;
+  int w;
+  {
+    const int b = blockIdx.x;
+    const int span = (nblk / (8 * G)) * (8 * G);   // whole rounds of 8 chunks of G items
+    if (b < span) {
+      const int x = b % 8, r = b / 8;  // XCD x, its r-th block
+      w = ((r / G) * 8 + x) * G + r % G;
+    } else {
+      w = b;
+    }
+  }
+  // query heads in order: the G heads of each dense KV head (ascending), then those of
+  // each streaming KV head; the k-th KV head of a kind is the k-th set bit of its mask
+  const uint64_t dmask = a.dense_kv_mask;
+  const uint64_t smask = ~dmask & (a.Hkv == 64 ? ~0ull : ((1ull << a.Hkv) - 1));
+  auto nth_bit = [](uint64_t m, int k) {
+    for (; k > 0; --k) m &= m - 1;
+    return __builtin_ctzll(m);
+  };
+  const int nd = a.n_dense_kv * G;
   bool streaming;
   int h, i;
-  if (idx < nd * nT) {
+  if (w < nd * nT) {
     streaming = false;
-    i = nT - 1 - idx / nd;
-    h = a.order.h[idx % nd];
+    i = nT - 1 - w / nd;
+    const int x = w % nd;
+    h = nth_bit(dmask, x / G) * G + x % G;
   } else {
-    idx -= nd * nT;
-    const int ns = a.order.n_total - nd;
+    const int w2 = w - nd * nT;
+    const int ns = a.Hq - nd;
     streaming = true;
-    i = nT - 1 - idx / ns;
-    h = a.order.h[nd + idx % ns];
+    i = nT - 1 - w2 / ns;
+    const int x = w2 % ns;
+    h = nth_bit(smask, x / G) * G + x % G;
   }
   const int g = h / G;
 
-  // ---- direct-to-LDS tile loader: slot s = (wave*IT + it)*64 + lane holds row s/CPR,
-  // physical chunk s%CPR, i.e. logical chunk (s%CPR) ^ swizzle(row). The 64/CPR rows of
-  // one load instruction never straddle a page (P >= 16), so the page id is wave-uniform
-  // and comes from a scalar load; the loads issued never wait on a vector memory result.
+  // ---- direct-to-LDS tile loader. Slot s = (wave*IT + it)*64 + lane holds row s/CPR,
+  // physical chunk s%CPR, i.e. logical chunk (s%CPR) ^ swizzle(row). One instruction's
+  // RPI rows never straddle a page (P >= 16), so page ids are wave-uniform scalar loads.
   typedef const int32_t __attribute__((address_space(4)))* const_i32p;
   const const_i32p ptab = (const_i32p)a.page_table;
   const int lp = a.log2_P;
   const int pmask = (1 << lp) - 1;
-  constexpr int RPI = 64 / CPR;  // rows per load instruction
-  auto lookup_pages = [&](int j, int32_t (&pg)[IT]) {
+  // Each wave loads 16 consecutive rows of a tile (IT * RPI == 16), which lie in one page
+  // (P >= 16), so one page-table entry per wave and tile serves its K and V loads; in the
+  // last, partial tile the rows past L-1 are redirected to row L-1 (valid data, never
+  // weighted), which lies in the same 16-row block and hence the same page.
+  static_assert(IT * RPI == 16, "a wave's share of a tile must be 16 rows");
+  // Loads are issued in 16-row blocks (one page: P >= 16). Wave (qg, kh) owns block
+  // rb = qg + (1 - kh) * QG: key-half-1 waves load rows 0..T/2-1 (used first, by key
+  // half 0), key-half-0 waves load rows T/2..T-1.
+  const int rb = qgrp + (1 - kh) * QG;
+  auto slot_of = [&](int j) { return min(j * T + rb * 16, L - 1) >> lp; };
+  auto issue = [&](const uint16_t* cache, uint16_t* dst, int j, int32_t page, int is_k) {
+    const int t0 = j * T + rb * 16;
+    const uint64_t slab = (((uint64_t)(uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << lp);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int r0 = (wave * IT + it) * RPI;
-      const int pidx = __builtin_amdgcn_readfirstlane(min(j * T + r0, L - 1) >> lp);
-      pg[it] = ptab[pidx];
-    }
-  };
-  auto issue_tile = [&](const uint16_t* cache, uint16_t* buf, int j, const int32_t (&pg)[IT], bool is_k) {
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int r = (wave * IT + it) * RPI + lane / CPR;
+      const int rr = it * RPI + lane / CPR;                 // row within the block
+      const int r = rb * 16 + rr;                           // row within the tile
       const int c = (lane % CPR) ^ (is_k ? k_swz<D>(r) : v_swz<D>(r));
-      const int t = min(j * T + r, L - 1);  // rows past the end: any valid row (never weighted)
-      const uint32_t row = (((uint32_t)pg[it] * (uint32_t)a.Hkv + (uint32_t)g) << lp) + (uint32_t)(t & pmask);
-      const uint16_t* src = cache + (uint64_t)row * D + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(buf + (wave * IT + it) * 512),
+      const int t = min(t0 + rr, L - 1);
+      __builtin_amdgcn_global_load_lds(cache + (slab + (uint32_t)(t & pmask)) * D + c * 8,
+                                       (__attribute__((address_space(3))) void*)(dst + (rb * IT + it) * 512),
                                        16, 0, 0);
     }
   };
+  auto issue_k = [&](int j, int buf, int32_t page) { issue(a.k_cache, sm.k[buf], j, page, 1); };
+  auto issue_v = [&](int j, int buf, int32_t page) { issue(a.v_cache, sm.v[buf], j, page, 0); };
 
-  // ---- kept KV tiles, ascending. Dense heads: compact the mask row into LDS once
-  // (each thread scans MB bytes, block-wide scan for the positions). Streaming heads:
-  // sink tiles, then the local window ending at the diagonal.
+  // ---- kept KV tiles, ascending
   int n_tiles;
   const int lo_local = max(a.sink_tiles, i - a.local_tiles + 1);
   const int n_sink = min(a.sink_tiles, i + 1);
@@ -150,32 +193,41 @@ __global__ __launch_bounds__(2 * T, 2) void prefill_kernel(const PrefillArgs a) 
     }
 #pragma unroll
     for (int e = 0; e < MB; ++e) cnt += flag[e] != 0;
-    int pos = block_scan<NT>(cnt, scan_tmp, n_tiles);
+    int pos = block_scan<NT>(cnt, sm.scan_tmp, n_tiles);
 #pragma unroll
     for (int e = 0; e < MB; ++e)
-      if (flag[e]) tlist[pos++] = (int16_t)(tid * MB + e);
-    __syncthreads();
+      if (flag[e]) sm.tlist[pos++] = (int16_t)(tid * MB + e);
   } else {
     n_tiles = n_sink + max(0, i + 1 - lo_local);
   }
   auto tile_at = [&](int n) -> int {
-    if (!streaming) return tlist[n];
+    if (!streaming) return sm.tlist[n];
     return n < n_sink ? n : lo_local + (n - n_sink);
   };
+  __syncthreads();
+  // K and V of tile 0 (every wave its 16-row block) before the loop
+  if (n_tiles > 0) {
+    const int j0 = tile_at(0);
+    const int32_t p0 = ptab[__builtin_amdgcn_readfirstlane(slot_of(j0))];
+    issue_k(j0, 0, p0);
+    issue_v(j0, 0, p0);
+  }
+  const int32_t* __restrict__ ptab_v = a.page_table;
+  int32_t pn_lane = 0;
 
   // ---- Q rows of this wave as the B operand: query n = lane % 32, k-slot group
-  // qg = lane / 32 holds channels qg*D/2 + kk*8 + [0, 8) for step kk.
+  // q2 = lane / 32 holds channels q2*D/2 + kk*8 + [0, 8) for step kk.
   const int qn = lane & 31;
-  const int qg = lane >> 5;
-  const int qrow = i * T + wave * 32 + qn;
+  const int q2 = lane >> 5;
+  const int qrow = i * T + qgrp * 32 + qn;
   bf16x8 qb[QK];
   {
-    const uint16_t* qp = a.q + ((int64_t)qrow * a.Hq + h) * D + qg * (D / 2);
+    const uint16_t* qp = a.q + ((int64_t)qrow * a.Hq + h) * D + q2 * (D / 2);
 #pragma unroll
     for (int kk = 0; kk < QK; ++kk) qb[kk] = as_bf16x8(qrow < L ? ld16(qp + kk * 8) : u32x4{0, 0, 0, 0});
   }
   const float c2 = a.sm_scale * kLog2e;  // scores -> log2 domain
-  const int qi = wave * 32 + qn;         // query index inside the tile
+  const int qi = qgrp * 32 + qn;         // query index inside the tile
 
   f32x16 oacc[CB];
 #pragma unroll
@@ -183,51 +235,64 @@ __global__ __launch_bounds__(2 * T, 2) void prefill_kernel(const PrefillArgs a) 
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[cb][e] = 0.f;
   float m_run = kNegInf, l_run = 0.f;  // m_run: running max of raw scores
+  wait_vm_all();
+  __syncthreads();
+  const int G16 = lane >> 4, j16 = lane & 15;
 
-  int32_t pg_cur[IT], pg_next[IT];
-  if (n_tiles > 0) {
-    const int j0 = tile_at(0);
-    lookup_pages(j0, pg_cur);
-    issue_tile(a.k_cache, ks, j0, pg_cur, true);
-    wait_vm_all();
-    __syncthreads();
-  }
-  for (int n = 0; n < n_tiles; ++n) {
-    const int j = tile_at(n);
-    issue_tile(a.v_cache, vs, j, pg_cur, false);
-    const int jn = (n + 1 < n_tiles) ? tile_at(n + 1) : -1;
-    if (jn >= 0) lookup_pages(jn, pg_next);
-
-    // ---- S^T = K_j Q^T: lane holds query qn, keys tb*32 + 8*jj + 4*qg + ii (reg 4*jj + ii)
-    f32x16 st[TB];
+  // ---- the three pieces of work on one tile
+  f32x16 st[TBH];      // scores of the current tile (between QK and softmax)
+  bf16x8 pb[TBH][2];   // bf16 weights of the previous tile (between softmax and PV)
+  auto qk = [&](int buf) {
+    // S^T = K Q^T over this wave's key half: lane holds query qn, keys
+    // kh*KH + tb*32 + 8*jj + 4*q2 + ii (reg 4*jj + ii). The TBH accumulators are
+    // advanced in turn (independent MFMA chains issue back to back), with the LDS
+    // reads kept ahead of the MFMAs that consume them.
+    const uint16_t* ks = sm.k[buf];
+    const uint16_t* kr[TBH];
+    int sw[TBH];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
+    for (int tb = 0; tb < TBH; ++tb) {
+      const int r = kh * KH + tb * 32 + qn;
+      kr[tb] = ks + r * D;
+      sw[tb] = k_swz<D>(r);
+    }
+    u32x4 kf[QK][TBH];
+#pragma unroll
+    for (int kk = 0; kk < QK; ++kk)
+#pragma unroll
+      for (int tb = 0; tb < TBH; ++tb)
+        kf[kk][tb] = *reinterpret_cast<const u32x4*>(kr[tb] + (((q2 * (D / 16) + kk) ^ sw[tb]) * 8));
+#pragma unroll
+    for (int tb = 0; tb < TBH; ++tb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[tb][e] = 0.f;
-      const int r = tb * 32 + qn;
-      const uint16_t* kr = ks + r * D;
-      const int sw = k_swz<D>(r);
-      u32x4 kf[QK];
 #pragma unroll
-      for (int kk = 0; kk < QK; ++kk)
-        kf[kk] = *reinterpret_cast<const u32x4*>(kr + (((qg * (D / 16) + kk) ^ sw) * 8));
+    for (int kk = 0; kk < QK; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < QK; ++kk)
-        st[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk]), qb[kk], st[tb], 0, 0, 0);
+      for (int tb = 0; tb < TBH; ++tb)
+        st[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk][tb]), qb[kk], st[tb], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TBH, 0);
+#pragma unroll
+    for (int x = 0; x < QK * TBH - 2 * TBH; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    // ---- causal cut on the diagonal tile, online softmax (row max on raw scores)
-    if (j == i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TBH, 0);
+  };
+  auto softmax = [&](bool diag) {
+    // causal cut on the diagonal tile, online softmax (row max on raw scores)
+    if (diag) {
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+      for (int tb = 0; tb < TBH; ++tb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = tb * 32 + 8 * (e >> 2) + 4 * qg + (e & 3);
+          const int key = kh * KH + tb * 32 + 8 * (e >> 2) + 4 * q2 + (e & 3);
           if (key > qi) st[tb][e] = kNegInf;
         }
     }
     float mx = kNegInf;
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+    for (int tb = 0; tb < TBH; ++tb)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(st[tb][e], st[tb][e + 1]));
     mx = fmaxf(mx, shfl_xor(mx, 32));
@@ -243,88 +308,134 @@ __global__ __launch_bounds__(2 * T, 2) void prefill_kernel(const PrefillArgs a) 
     }
     const float mofs = (m_run == kNegInf) ? 0.f : -m_run * c2;
     float psum = 0.f;
-    bf16x8 pb[TB][2];
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
+    for (int tb = 0; tb < TBH; ++tb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 w;
+        u32x4 wv;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = fast_exp2(fmaf(st[tb][8 * s2 + 2 * e2], c2, mofs));
           const float p1 = fast_exp2(fmaf(st[tb][8 * s2 + 2 * e2 + 1], c2, mofs));
           psum += p0 + p1;
-          w[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
+          wv[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
         }
-        pb[tb][s2] = as_bf16x8(w);
+        pb[tb][s2] = as_bf16x8(wv);
       }
     l_run += psum;
-
-    // ---- V_j has landed and every wave is done with K_j: prefetch the next K tile
-    wait_vm_all();
-    __syncthreads();
-    if (jn >= 0) issue_tile(a.k_cache, ks, jn, pg_next, true);
-
-    // ---- O^T += V_j^T P^T. A operand (row = channel, k-slots = keys
-    //      tb*32 + 16*s2 + 4*qg + [0,4) and the same + 8) by two transpose reads:
-    //      lane (group G16 = lane/16, j16 = lane%16) fetches key tok0 + j16/4,
-    //      channels chb + 4*(j16%4) + [0,4); it receives channel chb + j16, keys tok0 + [0,4).
-    const int G16 = lane >> 4, j16 = lane & 15;
+  };
+  auto pv = [&](int buf) {
+    // O^T += V^T P^T. A operand (row = channel, k-slots = keys
+    // kh*KH + tb*32 + 16*s2 + 4*q2 + [0,4) and the same + 8) by two transpose reads:
+    // lane (G16, j16) fetches key tok0 + j16/4, channels chb + 4*(j16%4) + [0,4)
+    // and receives channel chb + j16, keys tok0 + [0,4). The CB output accumulators
+    // are advanced in turn; the reads stay one key step ahead of the MFMAs.
+    const uint16_t* vs = sm.v[buf];
+    u32x4 vf[TBH * 2][CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int ch = cb * 32 + 16 * (G16 & 1) + 4 * (j16 & 3);
-      u32x4 vf[TB][2];
+    for (int tb = 0; tb < TBH; ++tb)
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int r1 = kh * KH + tb * 32 + 16 * s2 + 4 * (G16 >> 1) + (j16 >> 2);
+        const int r2 = r1 + 8;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int r1 = tb * 32 + 16 * s2 + 4 * (G16 >> 1) + (j16 >> 2);
-          const int r2 = r1 + 8;
+        for (int cb = 0; cb < CB; ++cb) {
+          const int ch = cb * 32 + 16 * (G16 & 1) + 4 * (j16 & 3);
           const uint16_t* p1 = vs + r1 * D + (((ch >> 3) ^ v_swz<D>(r1)) * 8) + (ch & 7);
           const uint16_t* p2 = vs + r2 * D + (((ch >> 3) ^ v_swz<D>(r2)) * 8) + (ch & 7);
           const i16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p1);
           const i16x4 t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p2);
-          vf[tb][s2] = u32x4{__builtin_bit_cast(u32x2, t1)[0], __builtin_bit_cast(u32x2, t1)[1],
-                             __builtin_bit_cast(u32x2, t2)[0], __builtin_bit_cast(u32x2, t2)[1]};
+          vf[tb * 2 + s2][cb] = u32x4{__builtin_bit_cast(u32x2, t1)[0], __builtin_bit_cast(u32x2, t1)[1],
+                                      __builtin_bit_cast(u32x2, t2)[0], __builtin_bit_cast(u32x2, t2)[1]};
         }
+      }
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+    for (int tb = 0; tb < TBH; ++tb)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[tb][s2]), pb[tb][s2], oacc[cb], 0, 0, 0);
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[tb * 2 + s2][cb]), pb[tb][s2], oacc[cb], 0, 0, 0);
+    constexpr int NM = TBH * 2 * CB;   // MFMAs (two transpose reads each)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * CB, 0);
+#pragma unroll
+    for (int x = 0; x < NM - CB; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    // ---- the next K tile has landed and every wave is done with V_j
+    __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
+  };
+
+  // ---- per kept tile n (double-buffered K and V): wait for tile n, then issue tile
+  // n+1's loads (every wave its 16-row block) and compute tile n: QK, softmax, PV.
+  if (n_tiles > 1) pn_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(1)));
+  for (int n = 0; n < n_tiles; ++n) {
+    const int j = tile_at(n);
+    const int buf = n & 1;
     wait_vm_all();
     __syncthreads();
-#pragma unroll
-    for (int it = 0; it < IT; ++it) pg_cur[it] = pg_next[it];
+    if (n + 1 < n_tiles) {
+      const int jn = tile_at(n + 1);
+      const int32_t pn = __builtin_amdgcn_readfirstlane(pn_lane);
+      issue_k(jn, buf ^ 1, pn);
+      issue_v(jn, buf ^ 1, pn);
+      if (n + 2 < n_tiles) pn_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(n + 2)));
+    }
+    qk(buf);
+    softmax(j == i);
+    pv(buf);
   }
 
-  // ---- epilogue: O / l, lse
-  const float l_tot = l_run + shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qrow < L) {
-    float* op = a.out + ((int64_t)qrow * a.Hq + h) * D + 4 * qg;
+  // ---- merge the two key halves of each query group through LDS, then O / l, lse.
+  // Half 1 parks (max, sum, O) in the K/V buffers; half 0 combines and writes out.
+  float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [QG][64 lanes][CB*16 + 2]
+  constexpr int PSTR = CB * 16 + 2;
+  static_assert(QG * 64 * PSTR * 4 <= 4 * T * D * 2, "park area exceeds the tile buffers");
+  __syncthreads();  // every wave is done with the tile buffers
+  const float l_half = l_run + shfl_xor(l_run, 32);   // both lanes of a row hold the row sum
+  if (kh == 1) {
+    float* pk = park + ((size_t)qgrp * 64 + lane) * PSTR;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        f32x4 v = {oacc[cb][4 * jj] * inv, oacc[cb][4 * jj + 1] * inv, oacc[cb][4 * jj + 2] * inv,
-                   oacc[cb][4 * jj + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + cb * 32 + 8 * jj) = v;
-      }
-    if (qg == 0 && a.lse)
-      a.lse[(int64_t)h * L + qrow] = l_tot > 0.f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : kNegInf;
+      for (int e = 0; e < 16; ++e) pk[cb * 16 + e] = oacc[cb][e];
+    pk[CB * 16] = m_run;
+    pk[CB * 16 + 1] = l_half;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float* pk = park + ((size_t)qgrp * 64 + lane) * PSTR;
+    const float m1 = pk[CB * 16], l1 = pk[CB * 16 + 1];
+    const float M = fmaxf(m_run, m1);
+    const float f0 = (M == kNegInf) ? 0.f : fast_exp2((m_run - M) * c2);
+    const float f1 = (M == kNegInf) ? 0.f : fast_exp2((m1 - M) * c2);
+    const float l_tot = f0 * l_half + f1 * l1;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (qrow < L) {
+      float* op = a.out + ((int64_t)qrow * a.Hq + h) * D + 4 * q2;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (f0 * oacc[cb][4 * jj + e] + f1 * pk[cb * 16 + 4 * jj + e]) * inv;
+          *reinterpret_cast<f32x4*>(op + cb * 32 + 8 * jj) = v;
+        }
+      if (q2 == 0 && a.lse)
+        a.lse[(int64_t)h * L + qrow] = l_tot > 0.f ? (M * c2 + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const int nT = (a.L + a.T - 1) / a.T;
-  const int64_t blocks = (int64_t)nT * a.order.n_total;
+  const int64_t blocks = (int64_t)nT * a.Hq;
   if (blocks == 0) return hipSuccess;
 #define UBS_PREFILL(TT, DD)                                                                    \
   if (a.T == TT && a.D == DD) {                                                                \
-    hipLaunchKernelGGL((prefill_kernel<TT, DD>), dim3((unsigned)blocks), dim3(2 * TT), 0, s, a); \
+    hipLaunchKernelGGL((prefill_kernel<TT, DD>), dim3((unsigned)blocks), dim3(4 * TT), 0, s, a); \
     return hipGetLastError();                                                                  \
   }
   UBS_PREFILL(64, 64) UBS_PREFILL(64, 128) UBS_PREFILL(128, 64) UBS_PREFILL(128, 128)
