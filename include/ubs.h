@@ -85,8 +85,8 @@ int ubs_version(void);
  *   lse         fp32 [Hq][L] or NULL      (fully written when given)
  * Arithmetic: bf16 MFMA products with fp32 accumulation; the softmax weights
  * are rounded to bf16 before the P.V product.
- * Supported: D in {64, 128}; T in {64, 128}; P a multiple of 16; L >= 0
- * (L = 0 is a no-op); Hq % Hkv == 0.
+ * Supported: D in {64, 128}; T in {64, 128}; P a power of two in [16, 4096];
+ * nT <= 4096; Hq <= 256; L >= 0 (L = 0 is a no-op); Hq % Hkv == 0.
  */
 int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
                    const int32_t* page_table, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
@@ -113,7 +113,7 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
  *   seq_lens    int32 [B], 0 <= seq_lens[b] <= max_pages * P
  *   bounds      bf16 [NP][Hkv][P/Lp][2][D]
  * A physical page referenced by several sequences must hold the same valid
- * tokens in each. Supported: D in {64, 128}; P a multiple of 16, <= 256;
+ * tokens in each. Supported: D in {64, 128}; P in {16, 32, 64, 128};
  * Lp divides P.
  */
 int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, const int32_t* seq_lens,
@@ -143,9 +143,9 @@ int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, cons
  *                 ascending order, unused slots -1; streaming heads get all -1
  *   num_selected  int32 [B][Hkv]: min(k, ceil(seq_lens[b]/P)); 0 for streaming
  *   workspace     >= select_pages_workspace_size(...) bytes, any contents
- * Supported: D in {64, 128}; Hq/Hkv <= 16; P a multiple of 16, <= 256;
+ * Supported: D in {64, 128}; Hq/Hkv in {1, 2, 4, 8, 16}; P in {16, 32, 64, 128};
  * P/Lp in {1, 2, 4, 8, 16}; token_budget a positive multiple of P;
- * max_pages <= 65536.
+ * max_pages <= 16384.
  */
 size_t select_pages_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv);
 int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* page_table,
@@ -176,10 +176,10 @@ int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* p
  *   num_selected  int32 [B][Hkv], each <= max_selected
  *   out           fp32 [B][Hq][D]        (fully written)
  *   lse           fp32 [B][Hq] or NULL
- *   workspace     >= sparse_decode_workspace_size(...) bytes. Its first
- *                 4 * B * Hkv bytes are arrival counters that must be zero
- *                 before the first call; every call leaves them zero.
- * Supported: D in {64, 128}; Hq/Hkv <= 16; P a multiple of 16, <= 256.
+ *   workspace     >= sparse_decode_workspace_size(...) bytes, any contents
+ *                 (holds the split partials between the two launches)
+ * Supported: D in {64, 128}; Hq/Hkv in {1, 2, 4, 8, 16}; P a multiple of 16,
+ * <= 256.
  */
 size_t sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                                     int32_t max_selected, int32_t sink_tokens, int32_t local_tokens);

@@ -106,10 +106,9 @@ _ws_cache = {}
 
 
 def _workspace(kind: str, device, stream: int, nbytes: int) -> torch.Tensor:
-    """Per (kind, device, stream) zero-initialised workspace, grown on demand.
+    """Per (kind, device, stream) workspace, grown on demand.
 
-    sparse_decode's arrival counters must start at zero and every call leaves them
-    zero, so a cached buffer stays valid across calls ordered on one stream.
+    Calls ordered on one stream may share it; calls on different streams get their own.
     """
     key = (kind, device, stream)
     buf = _ws_cache.get(key)

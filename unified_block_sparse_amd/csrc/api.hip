@@ -215,8 +215,6 @@ int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* p
   return hip_status(ubs::launch_select(a, stream), "select_pages launch");
 }
 
-static size_t decode_counter_bytes(int B, int Hkv) { return ((size_t)B * Hkv * 4 + 255) / 256 * 256; }
-
 size_t sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                                     int32_t max_selected, int32_t sink_tokens, int32_t local_tokens) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_selected < 0 || sink_tokens < 0 ||
@@ -226,7 +224,7 @@ size_t sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t 
   const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, Hkv, P, max_selected, sink_tokens, local_tokens);
   const ubs::DecodePlan ps = ubs::plan_decode(B, Hkv, 0, P, max_selected, sink_tokens, local_tokens);
   const int ms = pl.max_splits > ps.max_splits ? pl.max_splits : ps.max_splits;
-  return decode_counter_bytes(B, Hkv) + (size_t)B * Hq * ms * (D + 2) * sizeof(float);
+  return ((size_t)B * Hq * ms * (D + 2) * sizeof(float) + 255) / 256 * 256;
 }
 
 int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
@@ -288,8 +286,7 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
   a.chunks_per_wave = pl.chunks_per_wave;
   a.out = out;
   a.lse = lse;
-  a.counters = static_cast<uint32_t*>(workspace);
-  a.partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(B, Hkv));
+  a.partials = static_cast<float*>(workspace);
   a.max_splits = pl.max_splits;
   return hip_status(ubs::launch_decode(a, stream), "sparse_decode launch");
 }

@@ -13,8 +13,9 @@
 //   O += P V     : fp32 FMAs, each lane owning 8 channels of one key row, V read with
 //                  16-byte coalesced loads, P broadcast through LDS.
 // Partial (max, sum, output) triples of the 4 waves are merged through LDS; the
-// work-group writes one partial per split, and the last-arriving work-group of
-// (b, g) merges all splits (log-sum-exp combine staged in LDS) into the output.
+// work-group writes one partial per split (or the output when the key set has one
+// split), and a second launch merges the splits of each (b, g) with a log-sum-exp
+// combine staged in LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -85,8 +86,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   __shared__ float p_lds[4][64][G];
   __shared__ float w_m[4][G], w_l[4][G];
   __shared__ float w_o[4][G][D];
-  __shared__ float c_m[G][kMaxSplits], c_w[G][kMaxSplits];
-  __shared__ int last_flag;
 
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -149,23 +148,34 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     const uint16_t* vslab = a.v_cache + ((int64_t)ch.page * a.Hkv + g) * head_stride;
     const int r_lo = ch.t0 - ch.row_base, r_hi = ch.t1 - ch.row_base;   // valid rows [r_lo, r_hi)
     for (int r0 = (r_lo / 64) * 64; r0 < r_hi; r0 += 64) {
-      // ---- S for up to 4 blocks of 16 rows
+      // ---- issue every K and V load of the segment first (rows are clamped into the
+      // page; rows outside [r_lo, r_hi) are loaded but never weighted)
+      u32x4 kreg[4][KK];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int row = min(r0 + blk * 16 + m, a.P - 1);
+        const uint16_t* krow = kslab + (int64_t)row * D + qg * (D / 4);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) kreg[blk][kk] = ld16(krow + kk * 8);
+      }
+      u32x4 vreg[64 / TG];
+#pragma unroll
+      for (int x = 0; x < 64 / TG; ++x) {
+        const int row = min(r0 + tg + TG * x, a.P - 1);
+        vreg[x] = ld16(vslab + (int64_t)row * D + cc * 8);
+      }
+      // ---- S for 4 blocks of 16 rows
       f32x4 s[4];
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const int rb = r0 + blk * 16;
-        s[blk] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
-        if (rb < r_hi && rb + 16 > r_lo) {   // wave-uniform
-          const int row = rb + m;
-          const uint16_t* krow = kslab + (int64_t)row * D + qg * (D / 4);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(ld16(krow + kk * 8)), acc, 0, 0, 0);
-          const bool ok = row >= r_lo && row < r_hi;
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(kreg[blk][kk]), acc, 0, 0, 0);
+        const int row = r0 + blk * 16 + m;
+        const bool ok = row >= r_lo && row < r_hi;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
-        }
+        for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
       }
       // ---- segment max per head (heads 4*qg + i), then running max and weights
       float alpha_i[4];
@@ -196,17 +206,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
       }
-      // ---- O += P V over the segment's rows tg, tg + TG, ...
-#pragma unroll 4
-      for (int rr = tg; rr < 64; rr += TG) {
+      // ---- O += P V over the segment's rows tg, tg + TG, ... (weights of rows outside
+      // [r_lo, r_hi) are zero and their V values are replaced by zero)
+#pragma unroll
+      for (int x = 0; x < 64 / TG; ++x) {
+        const int rr = tg + TG * x;
         const int row = r0 + rr;
-        if (row < r_lo || row >= r_hi) continue;
-        const u32x4 v = ld16(vslab + (int64_t)row * D + cc * 8);
+        const bool ok = row >= r_lo && row < r_hi;
         float vf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vf[2 * e] = bf16_lo(v[e]);
-          vf[2 * e + 1] = bf16_hi(v[e]);
+          vf[2 * e] = ok ? bf16_lo(vreg[x][e]) : 0.f;
+          vf[2 * e + 1] = ok ? bf16_hi(vreg[x][e]) : 0.f;
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -276,22 +287,30 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       }
     }
   }
-  if (single) return;
+}
 
-  // ---- arrival counter: the last work-group of (b, g) merges every split
-  __threadfence();
-  __syncthreads();
-  uint32_t* counter = a.counters + (int64_t)b * a.Hkv + g;
-  if (tid == 0) last_flag = (atomicAdd(counter, 1u) == (uint32_t)(n_splits - 1));
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
+// Merge of the split partials of one (b, KV head): log-sum-exp combine staged in LDS.
+// A separate launch (rather than a last-arriving work-group) so that no work-group has
+// to publish its partials with a device-scope fence, which on this GPU writes back and
+// invalidates a whole L2.
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
+  __shared__ float c_m[G][kMaxSplits], c_w[G][kMaxSplits];
+  const int tid = threadIdx.x;
+  // blocks: (b, dense KV head) if dense heads are split, then (b, streaming KV head)
+  const int nd = a.splits_dense > 1 ? a.dense.n : 0;
+  const int ns = a.splits_stream > 1 ? a.streaming.n : 0;
+  const int b = blockIdx.x / (nd + ns);
+  const int r = blockIdx.x % (nd + ns);
+  const int g = r < nd ? a.dense.h[r] : a.streaming.h[r - nd];
+  const int n_splits = r < nd ? a.splits_dense : a.splits_stream;
+  const float* part = a.partials;
   for (int idx = tid; idx < G * n_splits; idx += 256) {
     const int h = idx / n_splits, sp = idx % n_splits;
     const int64_t qh = (int64_t)b * a.Hq + (int64_t)g * G + h;
     const float* pp = part + (qh * a.max_splits + sp) * (D + 2);
-    c_m[h][sp] = __builtin_nontemporal_load(pp + D);
-    c_w[h][sp] = __builtin_nontemporal_load(pp + D + 1);
+    c_m[h][sp] = pp[D];
+    c_w[h][sp] = pp[D + 1];
   }
   __syncthreads();
   for (int idx = tid; idx < G * D; idx += 256) {
@@ -304,14 +323,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       for (int sp = 0; sp < n_splits; ++sp) {
         const float f = fast_exp2(c_m[h][sp] - M);
         const float* pp = part + (qh * a.max_splits + sp) * (D + 2);
-        O = fmaf(f, __builtin_nontemporal_load(pp + c), O);
+        O = fmaf(f, pp[c], O);
         S = fmaf(f, c_w[h][sp], S);
       }
     }
     a.out[qh * D + c] = (S > 0.f) ? O / S : 0.f;
     if (c == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
   }
-  if (tid == 0) *counter = 0u;
 }
 
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local) {
@@ -341,10 +359,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.B * per_b;
   if (blocks == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
-#define UBS_DECODE(DD, GG)                                                                     \
-  if (a.D == DD && G == GG) {                                                                  \
-    hipLaunchKernelGGL((decode_kernel<DD, GG>), dim3((unsigned)blocks), dim3(256), 0, s, a);   \
-    return hipGetLastError();                                                                  \
+  const int merge_per_b = (a.splits_dense > 1 ? a.dense.n : 0) + (a.splits_stream > 1 ? a.streaming.n : 0);
+  const int64_t merge_blocks = (int64_t)a.B * merge_per_b;
+#define UBS_DECODE(DD, GG)                                                                            \
+  if (a.D == DD && G == GG) {                                                                         \
+    hipLaunchKernelGGL((decode_kernel<DD, GG>), dim3((unsigned)blocks), dim3(256), 0, s, a);          \
+    hipError_t e = hipGetLastError();                                                                 \
+    if (e != hipSuccess || merge_blocks == 0) return e;                                               \
+    hipLaunchKernelGGL((decode_merge_kernel<DD, GG>), dim3((unsigned)merge_blocks), dim3(256), 0, s, a); \
+    return hipGetLastError();                                                                         \
   }
   UBS_DECODE(64, 1) UBS_DECODE(64, 2) UBS_DECODE(64, 4) UBS_DECODE(64, 8) UBS_DECODE(64, 16)
   UBS_DECODE(128, 1) UBS_DECODE(128, 2) UBS_DECODE(128, 4) UBS_DECODE(128, 8) UBS_DECODE(128, 16)

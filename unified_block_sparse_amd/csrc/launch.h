@@ -49,7 +49,6 @@ struct DecodeArgs {
   int splits_dense, splits_stream, chunks_per_wave;
   float* out;
   float* lse;
-  uint32_t* counters;  // workspace [B][Hkv]
   float* partials;     // workspace [B][Hq][max_splits][D + 2]
   int max_splits;
 };

@@ -14,13 +14,15 @@
 // never loaded.
 //
 // Per kept tile (K and V are double-buffered in LDS, T x D bf16 each):
-//   K, V:  global -> LDS with direct-to-LDS 16-byte loads, two phases ahead of use
+//   K, V:  global -> LDS with direct-to-LDS 16-byte loads, issued one tile ahead so
+//          they stream in while the current tile is computed
 //   S^T  = K Q^T on bf16 MFMA 32x32x16 (Q resident in registers as the B operand)
 //   online softmax per query row in the log2 domain; causal cut on the diagonal tile
 //   O^T += V^T P^T on bf16 MFMA 32x32x16; V^T comes from the row-major tile through
 //          the LDS transpose read (ds_read_b64_tr_b16); P stays in registers
-// The two waves that share a SIMD (one per key half) run these in ping-pong: while
-// one issues matrix work the other runs its softmax (see the schedule below).
+// The two waves that share a SIMD overlap each other's softmax and matrix work
+// through the hardware's wave interleaving; within a wave, independent MFMA chains
+// are interleaved with the LDS operand reads (sched_group_barrier).
 // Rows of both buffers are XOR-swizzled at 16-byte granularity so the operand reads
 // are free of bank conflicts; the direct-to-LDS loads write the swizzled layout by
 // choosing which global chunk each lane fetches.
