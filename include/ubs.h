@@ -142,12 +142,12 @@ int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, cons
  *   selected      int32 [B][Hkv][k]: page indices j (into page_table[b]) in
  *                 ascending order, unused slots -1; streaming heads get all -1
  *   num_selected  int32 [B][Hkv]: min(k, ceil(seq_lens[b]/P)); 0 for streaming
- *   workspace     >= select_pages_workspace_size(...) bytes, any contents
+ *   workspace     >= ubs_select_workspace_size(...) bytes, any contents
  * Supported: D in {64, 128}; Hq/Hkv in {1, 2, 4, 8, 16}; P in {16, 32, 64, 128};
  * P/Lp in {1, 2, 4, 8, 16}; token_budget a positive multiple of P;
  * max_pages <= 16384.
  */
-size_t select_pages_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv);
+size_t ubs_select_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv);
 int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* page_table,
                  const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv,
                  int32_t D, int32_t P, int32_t Lp, int32_t token_budget,
@@ -176,12 +176,12 @@ int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* p
  *   num_selected  int32 [B][Hkv], each <= max_selected
  *   out           fp32 [B][Hq][D]        (fully written)
  *   lse           fp32 [B][Hq] or NULL
- *   workspace     >= sparse_decode_workspace_size(...) bytes, any contents
+ *   workspace     >= ubs_decode_workspace_size(...) bytes, any contents
  *                 (holds the split partials between the two launches)
  * Supported: D in {64, 128}; Hq/Hkv in {1, 2, 4, 8, 16}; P a multiple of 16,
  * <= 256.
  */
-size_t sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                                     int32_t max_selected, int32_t sink_tokens, int32_t local_tokens);
 int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
                   const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,

@@ -96,7 +96,7 @@ def _select(**kw):
              kind=KIND, sel=A, nsel=A, ws=A, wsb=None, stream=NULL)
     a.update(kw)
     if a["wsb"] is None:
-        a["wsb"] = lib.select_pages_workspace_size(a["B"], a["maxp"], a["Hkv"])
+        a["wsb"] = lib.ubs_select_workspace_size(a["B"], a["maxp"], a["Hkv"])
     return lib.select_pages(a["q"], a["bnd"], a["pt"], a["sl"], a["B"], a["maxp"], a["Hq"], a["Hkv"], a["D"],
                             a["P"], a["Lp"], a["budget"], a["kind"], a["sel"], a["nsel"], a["ws"], a["wsb"],
                             a["stream"])
@@ -113,8 +113,8 @@ def test_select_validation(kw, code):
 
 def test_select_workspace_size():
     lib = ubs.load()
-    assert lib.select_pages_workspace_size(4, 512, 8) >= 4 * 512 * 8 * 4
-    assert lib.select_pages_workspace_size(4, 512, 8) % 256 == 0
+    assert lib.ubs_select_workspace_size(4, 512, 8) >= 4 * 512 * 8 * 4
+    assert lib.ubs_select_workspace_size(4, 512, 8) % 256 == 0
 
 
 def _decode(**kw):
@@ -123,7 +123,7 @@ def _decode(**kw):
              ms=64, sink=128, local=512, scale=0.088, out=A, lse=NULL, ws=A, wsb=None, stream=NULL)
     a.update(kw)
     if a["wsb"] is None:
-        a["wsb"] = lib.sparse_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["ms"],
+        a["wsb"] = lib.ubs_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["ms"],
                                                     a["sink"], a["local"])
     return lib.sparse_decode(a["q"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["maxp"], a["Hq"], a["Hkv"],
                              a["D"], a["P"], a["kind"], a["sel"], a["nsel"], a["ms"], a["sink"], a["local"],
@@ -141,8 +141,8 @@ def test_decode_validation(kw, code):
 
 def test_decode_workspace_grows_with_budget():
     lib = ubs.load()
-    small = lib.sparse_decode_workspace_size(4, 32, 8, 128, 64, 16, 128, 512)
-    big = lib.sparse_decode_workspace_size(4, 32, 8, 128, 64, 1024, 128, 512)
+    small = lib.ubs_decode_workspace_size(4, 32, 8, 128, 64, 16, 128, 512)
+    big = lib.ubs_decode_workspace_size(4, 32, 8, 128, 64, 1024, 128, 512)
     assert big > small >= 4 * 8 * 4
 
 

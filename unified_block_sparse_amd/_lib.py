@@ -19,8 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libubs.so")
 
 UBS_OK = 0
 ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
-EXPORTED = ("sparse_prefill", "build_page_bounds", "select_pages", "select_pages_workspace_size",
-            "sparse_decode", "sparse_decode_workspace_size", "ubs_last_error", "ubs_version")
+EXPORTED = ("sparse_prefill", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
+            "sparse_decode", "ubs_decode_workspace_size", "ubs_last_error", "ubs_version")
 
 
 class UBSError(RuntimeError):
@@ -55,12 +55,12 @@ def load() -> ctypes.CDLL:
         lib.sparse_prefill.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _i, _f, _p, _p, _p]
         lib.build_page_bounds.restype = ctypes.c_int
         lib.build_page_bounds.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p]
-        lib.select_pages_workspace_size.restype = _sz
-        lib.select_pages_workspace_size.argtypes = [_i, _i, _i]
+        lib.ubs_select_workspace_size.restype = _sz
+        lib.ubs_select_workspace_size.argtypes = [_i, _i, _i]
         lib.select_pages.restype = ctypes.c_int
         lib.select_pages.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _sz, _p]
-        lib.sparse_decode_workspace_size.restype = _sz
-        lib.sparse_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
+        lib.ubs_decode_workspace_size.restype = _sz
+        lib.ubs_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i]
         lib.sparse_decode.restype = ctypes.c_int
         lib.sparse_decode.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _i,
                                       _f, _p, _p, _p, _sz, _p]
@@ -210,7 +210,7 @@ def select_pages(q: torch.Tensor, bounds: torch.Tensor, page_table: torch.Tensor
     _need(selected, "selected", torch.int32, shape=(B, Hkv, k), device=dev)
     _need(num_selected, "num_selected", torch.int32, shape=(B, Hkv), device=dev)
     st = _stream(dev)
-    need = lib.select_pages_workspace_size(B, max_pages, Hkv)
+    need = lib.ubs_select_workspace_size(B, max_pages, Hkv)
     if workspace is None:
         workspace = _workspace("select", dev, st, need)
     rc = lib.select_pages(_ptr(q), _ptr(bounds), _ptr(page_table), _ptr(seq_lens), B, max_pages, Hq, Hkv, D, P,
@@ -255,7 +255,7 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if lse is not None:
         _need(lse, "lse", torch.float32, shape=(B, Hq), device=dev)
     st = _stream(dev)
-    need = lib.sparse_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens)
+    need = lib.ubs_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens)
     if workspace is None:
         workspace = _workspace("decode", dev, st, need)
     rc = lib.sparse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), B, max_pages,

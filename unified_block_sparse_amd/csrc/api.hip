@@ -160,7 +160,7 @@ int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, cons
   return hip_status(ubs::launch_bounds(a, stream), "build_page_bounds launch");
 }
 
-size_t select_pages_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv) {
+size_t ubs_select_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv) {
   if (B <= 0 || max_pages <= 0 || Hkv <= 0) return 256;
   return ((size_t)B * Hkv * max_pages * sizeof(float) + 255) / 256 * 256;
 }
@@ -191,7 +191,7 @@ int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* p
   REQUIRE(dense.n == 0 || bounds, UBS_ERR_INVALID_ARGUMENT, "bounds is NULL but a KV head is dense");
   REQUIRE(aligned16(q) && (bounds == nullptr || aligned16(bounds)), UBS_ERR_INVALID_ARGUMENT,
           "q and bounds must be 16-byte aligned");
-  const size_t need = select_pages_workspace_size(B, max_pages, Hkv);
+  const size_t need = ubs_select_workspace_size(B, max_pages, Hkv);
   REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
           "workspace of %zu bytes, need %zu", workspace_bytes, need);
   ubs::SelectArgs a{};
@@ -215,7 +215,7 @@ int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* p
   return hip_status(ubs::launch_select(a, stream), "select_pages launch");
 }
 
-size_t sparse_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                                     int32_t max_selected, int32_t sink_tokens, int32_t local_tokens) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_selected < 0 || sink_tokens < 0 ||
       local_tokens < 0)
@@ -255,7 +255,7 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
   REQUIRE(dense.n == 0 || num_selected, UBS_ERR_INVALID_ARGUMENT, "num_selected is NULL but a KV head is dense");
   REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache), UBS_ERR_INVALID_ARGUMENT,
           "q, k_cache and v_cache must be 16-byte aligned");
-  const size_t need = sparse_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens);
+  const size_t need = ubs_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens);
   REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
           "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens);
