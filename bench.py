@@ -53,8 +53,24 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows-per-head", type=int, default=16)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=384)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (5 times) and exit: "
+                         "the known-size kernel that scales the HBM byte counters")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """A plain copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counter readings."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
 # ----------------------------------------------------------------------------- work accounting
@@ -139,28 +155,30 @@ def cpu_baseline(c, d, kept_tiles: int, rows_per_head: int, ideal_s: float):
     oracle.prefill_ref(q_host, kb, vb, pt, c.L, c.Hq, c.Hkv, c.D, c.P, c.T, c.head_kind, mask, c.sink_tiles,
                        c.local_tiles, c.sm_scale, rows=rows)
     t_pf = time.perf_counter() - t0
-    # one of the decode step's sequences, end to end (bounds -> selection -> decode)
-    b0 = [0]
-    dq = bits(d.q[:1])
-    n0 = (d.seq_lens[0] + d.P - 1) // d.P
-    idx = d.page_table[0, :n0].long()
-    dk, dv = bits(d.k_cache[idx]), bits(d.v_cache[idx])
-    dpt = np.arange(n0, dtype=np.int32)[None]
-    t0 = time.perf_counter()
-    sel, _ = oracle.select_ref(dq, dk, dpt, d.seq_lens[:1], d.Hq, d.Hkv, d.P, d.Lp, d.token_budget, d.head_kind)
-    oracle.decode_ref(dq, dk, dv, dpt, d.seq_lens[:1], d.Hq, d.Hkv, d.P, d.head_kind, sel, d.sink_tokens,
-                      d.local_tokens, d.sm_scale, batches=b0)
-    t_dec = time.perf_counter() - t0
-    step_s = t_fixed + max(t_pf - t_fixed, 0.0) * (c.L / len(rows)) + t_dec * d.B
+    # every sequence of the decode step, end to end (bounds -> selection -> decode)
+    t_dec = 0.0
+    for b in range(d.B):
+        dq = bits(d.q[b:b + 1])
+        nb = (d.seq_lens[b] + d.P - 1) // d.P
+        idx = d.page_table[b, :nb].long()
+        dk, dv = bits(d.k_cache[idx]), bits(d.v_cache[idx])
+        dpt = np.arange(nb, dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        sel, _ = oracle.select_ref(dq, dk, dpt, d.seq_lens[b:b + 1], d.Hq, d.Hkv, d.P, d.Lp, d.token_budget,
+                                   d.head_kind)
+        oracle.decode_ref(dq, dk, dv, dpt, d.seq_lens[b:b + 1], d.Hq, d.Hkv, d.P, d.head_kind, sel,
+                          d.sink_tokens, d.local_tokens, d.sm_scale, batches=[0])
+        t_dec += time.perf_counter() - t0
+    step_s = t_fixed + max(t_pf - t_fixed, 0.0) * (c.L / len(rows)) + t_dec
     return {
         "value": 100.0 * ideal_s / step_s,
         "unit": "% of MI355X roofline",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: prefill_llama8b {len(rows)} seeded rows x {c.Hq} heads "
+        "sample": (f"fp64 NumPy oracle: {c.name} {len(rows)} seeded rows x {c.Hq} heads "
                    f"({t_pf:.2f} s incl. {t_fixed:.2f} s K/V gather; per-row part extrapolated "
-                   f"x{c.L // len(rows)} to all {c.L} rows) + decode_llama8b "
-                   f"bounds/selection/decode of 1 of {d.B} sequences ({t_dec:.2f} s, x{d.B}); "
+                   f"x{c.L / len(rows):.1f} to all {c.L} rows) + {d.name} "
+                   f"bounds/selection/decode of all {d.B} sequences ({t_dec:.2f} s); "
                    f"extrapolated step {step_s:.1f} s"),
         "step_seconds_extrapolated": step_s,
         "host_cpus": os.cpu_count(),
@@ -175,6 +193,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(every workload here is a single-GPU shard).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
+        return
     import torch
     import unified_block_sparse_amd as ubs
     from workloads import cases
