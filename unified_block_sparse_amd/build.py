@@ -27,6 +27,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}",
 ]
+# Per-source additions (none at present).
+EXTRA_FLAGS = {}
 
 
 def sources():
@@ -35,7 +37,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,6 +62,12 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # hipcc can silently omit a kernel's host-side launch stub (the library then fails
+    # to load with an undefined symbol); name the culprit here instead
+    r = subprocess.run(["nm", "-C", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split(None, 1)[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("launch stubs missing from the build: " + "; ".join(missing))
     os.replace(tmp, OUT)
     return OUT
 

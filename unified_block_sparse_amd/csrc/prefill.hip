@@ -14,8 +14,9 @@
 // never loaded.
 //
 // Per kept tile (K and V are double-buffered in LDS, T x D bf16 each):
-//   K, V:  global -> LDS with direct-to-LDS 16-byte loads, issued one tile ahead so
-//          they stream in while the current tile is computed
+//   K, V:  global -> LDS with direct-to-LDS 16-byte buffer loads (scalar resource per
+//          group of rows, per-lane offsets fixed for the whole loop), issued one tile
+//          ahead so they stream in while the current tile is computed
 //   S^T  = K Q^T on bf16 MFMA 32x32x16 (Q resident in registers as the B operand)
 //   online softmax per query row in the log2 domain; causal cut on the diagonal tile
 //   O^T += V^T P^T on bf16 MFMA 32x32x16; V^T comes from the row-major tile through
@@ -32,6 +33,8 @@
 // run back to back on the same XCD and share its L2 for their K/V tiles.
 #include "common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace ubs {
 
@@ -74,14 +77,6 @@ __device__ __forceinline__ int block_scan(int v, int* tmp, int& total) {
 }
 
 template <int T, int D>
-struct PrefillShared {
-  uint16_t k[2][T * D];
-  uint16_t v[2][T * D];
-  int16_t tlist[kMaxTileList];
-  int scan_tmp[16];
-};
-
-template <int T, int D>
 __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) {
   constexpr int QG = T / 32;          // query groups of 32 rows
   constexpr int NW = 2 * QG;          // waves: query group x key half
@@ -94,11 +89,20 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   constexpr int QK = D / 16;          // MFMA steps over channels
   constexpr int CB = D / 32;          // 32-channel blocks of the output
   constexpr int MB = kMaxTileList / NT;  // mask bytes scanned per thread
-  __shared__ __attribute__((aligned(1024))) PrefillShared<T, D> sm;
+  // K and V tiles, double-buffered; every buffer is its own LDS object and the buffer
+  // of each access is known at compile time (the tile loop is unrolled by parity).
+  // The compiler can then tell the direct-to-LDS loads into one buffer from the reads
+  // of the other, and does not make those reads wait for the loads in flight.
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k0[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_k1[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v0[T * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_v1[T * D];
+  __shared__ __attribute__((aligned(16))) int16_t lds_tlist[kMaxTileList];
+  __shared__ int lds_scan[16];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (and known to be)
   const int qgrp = wave % QG;
   const int kh = wave / QG;
   const int L = a.L;
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   // each streaming KV head; the k-th KV head of a kind is the k-th set bit of its mask
   const uint64_t dmask = a.dense_kv_mask;
   const uint64_t smask = ~dmask & (a.Hkv == 64 ? ~0ull : ((1ull << a.Hkv) - 1));
-  auto nth_bit = [](uint64_t m, int k) {
+  auto nth_bit = [](uint64_t m, int k) __attribute__((always_inline)) {
     for (; k > 0; --k) m &= m - 1;
     return __builtin_ctzll(m);
   };
@@ -162,23 +166,38 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   // rb = qg + (1 - kh) * QG: key-half-1 waves load rows 0..T/2-1 (used first, by key
   // half 0), key-half-0 waves load rows T/2..T-1.
   const int rb = qgrp + (1 - kh) * QG;
-  auto slot_of = [&](int j) { return min(j * T + rb * 16, L - 1) >> lp; };
-  auto issue = [&](const uint16_t* cache, uint16_t* dst, int j, int32_t page, int is_k) {
+  auto slot_of = [&](int j) __attribute__((always_inline)) { return min(j * T + rb * 16, L - 1) >> lp; };
+  // Loads go through buffer resources: one per group of RPI rows (wave-uniform base:
+  // the group's first row in its page; size: the rows of the group below L), with
+  // per-lane byte offsets that are constant over the loop (row lane/CPR of the group,
+  // logical chunk (lane % CPR) ^ swizzle; the swizzle depends on the row only through
+  // its place in the 16-row block, which starts at a multiple of 16). No vector ALU
+  // work per load; rows at or past L read as zeros (the resource's bounds check),
+  // which the causal cut never weights.
+  auto issue = [&](const uint16_t* cache, uint16_t* dst, int j, int32_t page, int is_k) __attribute__((always_inline)) {
     const int t0 = j * T + rb * 16;
-    const uint64_t slab = (((uint64_t)(uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << lp);
+    const uint64_t row = (((uint64_t)(uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << lp) + (uint32_t)(t0 & pmask);
+    const int nrows = L - t0;  // valid rows from t0 on (may be <= 0)
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int rr = it * RPI + lane / CPR;                 // row within the block
-      const int r = rb * 16 + rr;                           // row within the tile
-      const int c = (lane % CPR) ^ (is_k ? k_swz<D>(r) : v_swz<D>(r));
-      const int t = min(t0 + rr, L - 1);
-      __builtin_amdgcn_global_load_lds(cache + (slab + (uint32_t)(t & pmask)) * D + c * 8,
-                                       (__attribute__((address_space(3))) void*)(dst + (rb * IT + it) * 512),
-                                       16, 0, 0);
+      // (every input of the resource made explicitly wave-uniform: otherwise the
+      // compiler may loop over the lanes to build it)
+      const int nr = __builtin_amdgcn_readfirstlane(min(max(nrows - it * RPI, 0), RPI));
+      const uint64_t addr = (uint64_t)(cache + (row + it * RPI) * D);
+      const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, nr * D * 2, 0x00020000);
+      // lane offset: row lane/CPR of the group, logical chunk (lane % CPR) ^ swizzle
+      // (written out here: a helper lambda called from this one makes the host
+      // compilation pass drop the kernel's launch stub)
+      const int r = rb * 16 + it * RPI + lane / CPR;
+      const int sw = is_k ? (D == 128 ? (r & 15) : ((r >> 1) & 7)) : (D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1));
+      const uint32_t lo = (uint32_t)((lane / CPR) * D + ((lane % CPR) ^ sw) * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (rb * IT + it) * 512),
+                                               16, lo, 0, 0, 0);
     }
   };
-  auto issue_k = [&](int j, int buf, int32_t page) { issue(a.k_cache, sm.k[buf], j, page, 1); };
-  auto issue_v = [&](int j, int buf, int32_t page) { issue(a.v_cache, sm.v[buf], j, page, 0); };
 
   // ---- kept KV tiles, ascending
   int n_tiles;
@@ -195,15 +214,17 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
     }
 #pragma unroll
     for (int e = 0; e < MB; ++e) cnt += flag[e] != 0;
-    int pos = block_scan<NT>(cnt, sm.scan_tmp, n_tiles);
+    int pos = block_scan<NT>(cnt, lds_scan, n_tiles);
 #pragma unroll
     for (int e = 0; e < MB; ++e)
-      if (flag[e]) sm.tlist[pos++] = (int16_t)(tid * MB + e);
+      if (flag[e]) lds_tlist[pos++] = (int16_t)(tid * MB + e);
   } else {
     n_tiles = n_sink + max(0, i + 1 - lo_local);
   }
-  auto tile_at = [&](int n) -> int {
-    if (!streaming) return sm.tlist[n];
+  // (the tile index is wave-uniform; saying so keeps the address and buffer-resource
+  // arithmetic that depends on it on the scalar unit)
+  auto tile_at = [&](int n) __attribute__((always_inline)) -> int {
+    if (!streaming) return __builtin_amdgcn_readfirstlane(lds_tlist[n]);
     return n < n_sink ? n : lo_local + (n - n_sink);
   };
   __syncthreads();
@@ -211,8 +232,8 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   if (n_tiles > 0) {
     const int j0 = tile_at(0);
     const int32_t p0 = ptab[__builtin_amdgcn_readfirstlane(slot_of(j0))];
-    issue_k(j0, 0, p0);
-    issue_v(j0, 0, p0);
+    issue(a.k_cache, lds_k0, j0, p0, 1);
+    issue(a.v_cache, lds_v0, j0, p0, 0);
   }
   const int32_t* __restrict__ ptab_v = a.page_table;
   int32_t pn_lane = 0;
@@ -244,12 +265,11 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   // ---- the three pieces of work on one tile
   f32x16 st[TBH];      // scores of the current tile (between QK and softmax)
   bf16x8 pb[TBH][2];   // bf16 weights of the previous tile (between softmax and PV)
-  auto qk = [&](int buf) {
+  auto qk = [&](const uint16_t* ks) __attribute__((always_inline)) {
     // S^T = K Q^T over this wave's key half: lane holds query qn, keys
     // kh*KH + tb*32 + 8*jj + 4*q2 + ii (reg 4*jj + ii). The TBH accumulators are
     // advanced in turn (independent MFMA chains issue back to back), with the LDS
     // reads kept ahead of the MFMAs that consume them.
-    const uint16_t* ks = sm.k[buf];
     const uint16_t* kr[TBH];
     int sw[TBH];
 #pragma unroll
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * TBH, 0);
   };
-  auto softmax = [&](bool diag) {
+  auto softmax = [&](bool diag) __attribute__((always_inline)) {
     // causal cut on the diagonal tile, online softmax (row max on raw scores)
     if (diag) {
 #pragma unroll
@@ -326,13 +346,12 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
       }
     l_run += psum;
   };
-  auto pv = [&](int buf) {
+  auto pv = [&](const uint16_t* vs) __attribute__((always_inline)) {
     // O^T += V^T P^T. A operand (row = channel, k-slots = keys
     // kh*KH + tb*32 + 16*s2 + 4*q2 + [0,4) and the same + 8) by two transpose reads:
     // lane (G16, j16) fetches key tok0 + j16/4, channels chb + 4*(j16%4) + [0,4)
     // and receives channel chb + j16, keys tok0 + [0,4). The CB output accumulators
     // are advanced in turn; the reads stay one key step ahead of the MFMAs.
-    const uint16_t* vs = sm.v[buf];
     u32x4 vf[TBH * 2][CB];
 #pragma unroll
     for (int tb = 0; tb < TBH; ++tb)
@@ -370,44 +389,64 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
 
   // ---- per kept tile n (double-buffered K and V): wait for tile n, then issue tile
   // n+1's loads (every wave its 16-row block) and compute tile n: QK, softmax, PV.
-  if (n_tiles > 1) pn_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(1)));
-  for (int n = 0; n < n_tiles; ++n) {
+  // The loop is unrolled by two so that the buffer parity of every access is a
+  // compile-time constant (tag par).
+  auto kbuf = [&](auto par) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(par)::value == 0) return lds_k0; else return lds_k1;
+  };
+  auto vbuf = [&](auto par) __attribute__((always_inline)) -> uint16_t* {
+    if constexpr (decltype(par)::value == 0) return lds_v0; else return lds_v1;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto body = [&](int n, auto par) __attribute__((always_inline)) {
+    using Q = std::integral_constant<int, 1 - decltype(par)::value>;
     const int j = tile_at(n);
-    const int buf = n & 1;
     wait_vm_all();
     __syncthreads();
     if (n + 1 < n_tiles) {
       const int jn = tile_at(n + 1);
       const int32_t pn = __builtin_amdgcn_readfirstlane(pn_lane);
-      issue_k(jn, buf ^ 1, pn);
-      issue_v(jn, buf ^ 1, pn);
+      issue(a.k_cache, kbuf(Q{}), jn, pn, 1);
+      issue(a.v_cache, vbuf(Q{}), jn, pn, 0);
       if (n + 2 < n_tiles) pn_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(n + 2)));
     }
-    qk(buf);
+    qk(kbuf(par));
     softmax(j == i);
-    pv(buf);
+    pv(vbuf(par));
+  };
+  if (n_tiles > 1) pn_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(1)));
+  int n = 0;
+  for (; n + 1 < n_tiles; n += 2) {
+    body(n, P0{});
+    body(n + 1, P1{});
   }
+  if (n < n_tiles) body(n, P0{});
 
   // ---- merge the two key halves of each query group through LDS, then O / l, lse.
-  // Half 1 parks (max, sum, O) in the K/V buffers; half 0 combines and writes out.
-  float* park = reinterpret_cast<float*>(&sm.k[0][0]);   // [QG][64 lanes][CB*16 + 2]
-  constexpr int PSTR = CB * 16 + 2;
-  static_assert(QG * 64 * PSTR * 4 <= 4 * T * D * 2, "park area exceeds the tile buffers");
-  __syncthreads();  // every wave is done with the tile buffers
+  // Half 1 parks O in the K buffers (query group g in region g: 16-byte chunk c of
+  // lane l at float (c*64 + l)*4) and (max, sum) in the tile-list area; half 0
+  // combines and writes out.
+  constexpr int RS = 64 * CB * 16;   // floats per region
+  constexpr int RPB = T * D * 2 / (RS * 4);  // regions per K buffer
+  static_assert(RPB >= 1 && 2 * RPB >= QG, "park regions exceed the K buffers");
+  float* rg = reinterpret_cast<float*>(qgrp / RPB == 0 ? lds_k0 : lds_k1) + (qgrp % RPB) * RS;
+  float* ml = reinterpret_cast<float*>(lds_tlist) + (qgrp * 64 + lane) * 2;
+  __syncthreads();  // every wave is done with the tile buffers and the tile list
   const float l_half = l_run + shfl_xor(l_run, 32);   // both lanes of a row hold the row sum
   if (kh == 1) {
-    float* pk = park + ((size_t)qgrp * 64 + lane) * PSTR;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pk[cb * 16 + e] = oacc[cb][e];
-    pk[CB * 16] = m_run;
-    pk[CB * 16 + 1] = l_half;
+      for (int e = 0; e < 16; e += 4)
+        *reinterpret_cast<f32x4*>(rg + ((cb * 4 + e / 4) * 64 + lane) * 4) =
+            f32x4{oacc[cb][e], oacc[cb][e + 1], oacc[cb][e + 2], oacc[cb][e + 3]};
+    ml[0] = m_run;
+    ml[1] = l_half;
   }
   __syncthreads();
   if (kh == 0) {
-    const float* pk = park + ((size_t)qgrp * 64 + lane) * PSTR;
-    const float m1 = pk[CB * 16], l1 = pk[CB * 16 + 1];
+    const float m1 = ml[0], l1 = ml[1];
     const float M = fmaxf(m_run, m1);
     const float f0 = (M == kNegInf) ? 0.f : fast_exp2((m_run - M) * c2);
     const float f1 = (M == kNegInf) ? 0.f : fast_exp2((m1 - M) * c2);
@@ -419,10 +458,10 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(rg + ((cb * 4 + jj) * 64 + lane) * 4);
           f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = (f0 * oacc[cb][4 * jj + e] + f1 * pk[cb * 16 + 4 * jj + e]) * inv;
+          for (int e = 0; e < 4; ++e) v[e] = (f0 * oacc[cb][4 * jj + e] + f1 * o1[e]) * inv;
           *reinterpret_cast<f32x4*>(op + cb * 32 + 8 * jj) = v;
         }
       if (q2 == 0 && a.lse)
