@@ -167,33 +167,33 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   // half 0), key-half-0 waves load rows T/2..T-1.
   const int rb = qgrp + (1 - kh) * QG;
   auto slot_of = [&](int j) __attribute__((always_inline)) { return min(j * T + rb * 16, L - 1) >> lp; };
-  // Loads go through buffer resources: one per group of RPI rows (wave-uniform base:
-  // the group's first row in its page; size: the rows of the group below L), with
-  // per-lane byte offsets that are constant over the loop (row lane/CPR of the group,
+  // Loads go through a buffer resource per 16-row block (wave-uniform base: the block's
+  // first row in its page; size: the rows of the block below L), with per-lane byte
+  // offsets that are constant over the loop (row it*RPI + lane/CPR of the block,
   // logical chunk (lane % CPR) ^ swizzle; the swizzle depends on the row only through
-  // its place in the 16-row block, which starts at a multiple of 16). No vector ALU
-  // work per load; rows at or past L read as zeros (the resource's bounds check),
-  // which the causal cut never weights.
+  // its place in the block, which starts at a multiple of 16). No vector ALU work per
+  // load; rows at or past L read as zeros (the resource's bounds check), which the
+  // causal cut never weights.
   auto issue = [&](const uint16_t* cache, uint16_t* dst, int j, int32_t page, int is_k) __attribute__((always_inline)) {
     const int t0 = j * T + rb * 16;
     const uint64_t row = (((uint64_t)(uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << lp) + (uint32_t)(t0 & pmask);
-    const int nrows = L - t0;  // valid rows from t0 on (may be <= 0)
+    // one resource for the 16-row block: base = its first row, size = its rows below L
+    // (every input made explicitly wave-uniform: otherwise the compiler may loop over
+    // the lanes to build the resource)
+    const int nr = __builtin_amdgcn_readfirstlane(min(max(L - t0, 0), 16));
+    const uint64_t addr = (uint64_t)(cache + row * D);
+    const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, nr * D * 2, 0x00020000);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      // (every input of the resource made explicitly wave-uniform: otherwise the
-      // compiler may loop over the lanes to build it)
-      const int nr = __builtin_amdgcn_readfirstlane(min(max(nrows - it * RPI, 0), RPI));
-      const uint64_t addr = (uint64_t)(cache + (row + it * RPI) * D);
-      const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
-                              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, nr * D * 2, 0x00020000);
-      // lane offset: row lane/CPR of the group, logical chunk (lane % CPR) ^ swizzle
-      // (written out here: a helper lambda called from this one makes the host
-      // compilation pass drop the kernel's launch stub)
-      const int r = rb * 16 + it * RPI + lane / CPR;
+      // lane offset: row rr = it*RPI + lane/CPR of the block, logical chunk
+      // (lane % CPR) ^ swizzle (written out here: a helper lambda called from this one
+      // makes the host compilation pass drop the kernel's launch stub)
+      const int rr = it * RPI + lane / CPR;
+      const int r = rb * 16 + rr;
       const int sw = is_k ? (D == 128 ? (r & 15) : ((r >> 1) & 7)) : (D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1));
-      const uint32_t lo = (uint32_t)((lane / CPR) * D + ((lane % CPR) ^ sw) * 8) * 2;
+      const uint32_t lo = (uint32_t)(rr * D + ((lane % CPR) ^ sw) * 8) * 2;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (rb * IT + it) * 512),
                                                16, lo, 0, 0, 0);
     }
