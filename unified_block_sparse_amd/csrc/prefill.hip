@@ -51,6 +51,18 @@ __device__ __forceinline__ int v_swz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
+// Largest growth of the row max (log2 domain) absorbed without rescaling O: weights
+// stay below 2^8, far inside the range of fp32 sums and of the bf16 weights.
+constexpr float kRescaleLog2 = 8.0f;
+
+// max of x over lanes l and l ^ 32: one swap of the wave's halves, then the max of
+// the two swapped registers (each lane holds its own value in one and the partner's
+// in the other)
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }  // vmcnt(0)
 
 // Block-wide exclusive scan of one int per thread (NT threads).
@@ -312,23 +324,33 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
           if (key > qi) st[tb][e] = kNegInf;
         }
     }
+    // tile max per query row (scores are finite or -inf: the NaN-propagating maximum
+    // needs no operand canonicalisation and folds into three-input max instructions)
     float mx = kNegInf;
 #pragma unroll
     for (int tb = 0; tb < TBH; ++tb)
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(st[tb][e], st[tb][e + 1]));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    if (__ballot(m_new != m_run)) {  // rescale only when some row's max moved
-      const float alpha = (m_new == kNegInf) ? 1.0f : fast_exp2((m_run - m_new) * c2);
+      for (int e = 0; e < 16; e += 2)
+        mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, st[tb][e]), st[tb][e + 1]);
+    mx = max_xor32(mx);
+    // Lazy rescaling: the weights of a tile are taken against the max in use, m_run,
+    // which moves only when the tile max exceeds it by more than kRescaleLog2 (log2
+    // domain). Weights then stay below 2^kRescaleLog2, the result O / l is unchanged,
+    // and most tiles skip the rescale of O. (m_run = -inf: any finite max moves it;
+    // mx = -inf never does: the difference is NaN or -inf.)
+    const bool grow = (mx - m_run) * c2 > kRescaleLog2;
+    if (__ballot(grow)) {
+      const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[cb][e] *= alpha;
-      m_run = m_new;
+      m_run = grow ? mx : m_run;
     }
     const float mofs = (m_run == kNegInf) ? 0.f : -m_run * c2;
+    // weights rounded to bf16; the row sum adds the rounded weights (two per dot2)
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float psum = 0.f;
 #pragma unroll
     for (int tb = 0; tb < TBH; ++tb)
@@ -339,8 +361,9 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
         for (int e2 = 0; e2 < 4; ++e2) {
           const float p0 = fast_exp2(fmaf(st[tb][8 * s2 + 2 * e2], c2, mofs));
           const float p1 = fast_exp2(fmaf(st[tb][8 * s2 + 2 * e2 + 1], c2, mofs));
-          psum += p0 + p1;
-          wv[e2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0, p1}), bf16x2));
+          const bf16x2 pp = __builtin_convertvector((f32x2{p0, p1}), bf16x2);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
+          wv[e2] = __builtin_bit_cast(uint32_t, pp);
         }
         pb[tb][s2] = as_bf16x8(wv);
       }
