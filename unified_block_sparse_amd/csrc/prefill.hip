@@ -186,13 +186,16 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   // its place in the block, which starts at a multiple of 16). No vector ALU work per
   // load; rows at or past L read as zeros (the resource's bounds check), which the
   // causal cut never weights.
-  auto issue = [&](const uint16_t* cache, uint16_t* dst, int j, int32_t page, int is_k) __attribute__((always_inline)) {
+  // (valid = false: an empty resource, the loads write zeros and read nothing; lets the
+  // caller issue branch-free)
+  auto issue = [&](const uint16_t* cache, uint16_t* dst, int j, int32_t page, int is_k, bool valid = true)
+      __attribute__((always_inline)) {
     const int t0 = j * T + rb * 16;
     const uint64_t row = (((uint64_t)(uint32_t)page * (uint32_t)a.Hkv + (uint32_t)g) << lp) + (uint32_t)(t0 & pmask);
     // one resource for the 16-row block: base = its first row, size = its rows below L
     // (every input made explicitly wave-uniform: otherwise the compiler may loop over
     // the lanes to build the resource)
-    const int nr = __builtin_amdgcn_readfirstlane(min(max(L - t0, 0), 16));
+    const int nr = __builtin_amdgcn_readfirstlane(valid ? min(max(L - t0, 0), 16) : 0);
     const uint64_t addr = (uint64_t)(cache + row * D);
     const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
@@ -232,12 +235,12 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
       if (flag[e]) lds_tlist[pos++] = (int16_t)(tid * MB + e);
   } else {
     n_tiles = n_sink + max(0, i + 1 - lo_local);
+    for (int e = tid; e < n_tiles; e += NT) lds_tlist[e] = (int16_t)(e < n_sink ? e : lo_local + (e - n_sink));
   }
   // (the tile index is wave-uniform; saying so keeps the address and buffer-resource
   // arithmetic that depends on it on the scalar unit)
   auto tile_at = [&](int n) __attribute__((always_inline)) -> int {
-    if (!streaming) return __builtin_amdgcn_readfirstlane(lds_tlist[n]);
-    return n < n_sink ? n : lo_local + (n - n_sink);
+    return __builtin_amdgcn_readfirstlane(lds_tlist[n]);
   };
   __syncthreads();
   // K and V of tile 0 (every wave its 16-row block) before the loop
@@ -248,7 +251,6 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
     issue(a.v_cache, lds_v0, j0, p0, 0);
   }
   const int32_t* __restrict__ ptab_v = a.page_table;
-  int32_t pn_lane = 0;
 
   // ---- Q rows of this wave as the B operand: query n = lane % 32, k-slot group
   // q2 = lane / 32 holds channels q2*D/2 + kk*8 + [0, 8) for step kk.
@@ -269,19 +271,18 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
   for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[cb][e] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;  // m_run: running max of raw scores
-  wait_vm_all();
-  __syncthreads();
+  float m_run = kNegInf, l_run = 0.f;  // m_run: the max in use (raw scores)
   const int G16 = lane >> 4, j16 = lane & 15;
 
-  // ---- the three pieces of work on one tile
-  f32x16 st[TBH];      // scores of the current tile (between QK and softmax)
-  bf16x8 pb[TBH][2];   // bf16 weights of the previous tile (between softmax and PV)
-  auto qk = [&](const uint16_t* ks) __attribute__((always_inline)) {
-    // S^T = K Q^T over this wave's key half: lane holds query qn, keys
-    // kh*KH + tb*32 + 8*jj + 4*q2 + ii (reg 4*jj + ii). The TBH accumulators are
-    // advanced in turn (independent MFMA chains issue back to back), with the LDS
-    // reads kept ahead of the MFMAs that consume them.
+  // ---- the pieces of work on one tile
+  f32x16 s0[TBH], s1[TBH];  // scores of two consecutive tiles (by parity)
+  bf16x8 pb[TBH][2];        // bf16 weights of the tile being finished
+  float alpha = 1.f;        // its rescale factor of O (1 where the max in use stayed)
+  bool grow = false;
+  // S^T = K Q^T over this wave's key half into st: lane holds query qn, keys
+  // kh*KH + tb*32 + 8*jj + 4*q2 + ii (reg 4*jj + ii). Emits the LDS reads and the
+  // MFMAs only; the caller's scheduling pattern orders them.
+  auto qk_emit = [&](const uint16_t* ks, f32x16 (&st)[TBH]) __attribute__((always_inline)) {
     const uint16_t* kr[TBH];
     int sw[TBH];
 #pragma unroll
@@ -305,27 +306,18 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
 #pragma unroll
       for (int tb = 0; tb < TBH; ++tb)
         st[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk][tb]), qb[kk], st[tb], 0, 0, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TBH, 0);
-#pragma unroll
-    for (int x = 0; x < QK * TBH - 2 * TBH; ++x) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TBH, 0);
   };
-  auto softmax = [&](bool diag) __attribute__((always_inline)) {
-    // causal cut on the diagonal tile, online softmax (row max on raw scores)
-    if (diag) {
-#pragma unroll
-      for (int tb = 0; tb < TBH; ++tb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kh * KH + tb * 32 + 8 * (e >> 2) + 4 * q2 + (e & 3);
-          if (key > qi) st[tb][e] = kNegInf;
-        }
-    }
-    // tile max per query row (scores are finite or -inf: the NaN-propagating maximum
-    // needs no operand canonicalisation and folds into three-input max instructions)
+  // Online softmax of one tile's scores in two parts. softmax_max: row max, then lazy
+  // rescaling: the max in use, m_run, moves only when the tile max exceeds it by more
+  // than kRescaleLog2 in the log2 domain, so weights stay below 2^kRescaleLog2 and
+  // most tiles leave O alone (m_run = -inf: any finite max moves it; a row max of -inf
+  // never does, the difference being NaN or -inf); rescale_o applies the factor to O.
+  // softmax_p: bf16 weights into pb and the row sum of the rounded weights (two per
+  // dot2) into l_run; branch-free, so that it can share a basic block with MFMA work.
+  float mofs = 0.f;
+  auto softmax_max = [&](f32x16 (&st)[TBH]) __attribute__((always_inline)) {
+    // (scores are finite or -inf: the NaN-propagating maximum needs no operand
+    // canonicalisation and folds into three-input max instructions)
     float mx = kNegInf;
 #pragma unroll
     for (int tb = 0; tb < TBH; ++tb)
@@ -333,23 +325,20 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
       for (int e = 0; e < 16; e += 2)
         mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, st[tb][e]), st[tb][e + 1]);
     mx = max_xor32(mx);
-    // Lazy rescaling: the weights of a tile are taken against the max in use, m_run,
-    // which moves only when the tile max exceeds it by more than kRescaleLog2 (log2
-    // domain). Weights then stay below 2^kRescaleLog2, the result O / l is unchanged,
-    // and most tiles skip the rescale of O. (m_run = -inf: any finite max moves it;
-    // mx = -inf never does: the difference is NaN or -inf.)
-    const bool grow = (mx - m_run) * c2 > kRescaleLog2;
+    grow = (mx - m_run) * c2 > kRescaleLog2;
+    alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.0f;
+    m_run = grow ? mx : m_run;
+    mofs = (m_run == kNegInf) ? 0.f : -m_run * c2;
+  };
+  auto rescale_o = [&]() __attribute__((always_inline)) {
     if (__ballot(grow)) {
-      const float alpha = grow ? fast_exp2((m_run - mx) * c2) : 1.0f;
-      l_run *= alpha;
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[cb][e] *= alpha;
-      m_run = grow ? mx : m_run;
     }
-    const float mofs = (m_run == kNegInf) ? 0.f : -m_run * c2;
-    // weights rounded to bf16; the row sum adds the rounded weights (two per dot2)
+  };
+  auto softmax_p = [&](f32x16 (&st)[TBH]) __attribute__((always_inline)) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     float psum = 0.f;
 #pragma unroll
@@ -367,9 +356,19 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
         }
         pb[tb][s2] = as_bf16x8(wv);
       }
-    l_run += psum;
+    l_run = fmaf(l_run, alpha, psum);
   };
-  auto pv = [&](const uint16_t* vs) __attribute__((always_inline)) {
+  auto qk_only = [&](const uint16_t* ks, f32x16 (&sn)[TBH]) __attribute__((always_inline)) {
+    qk_emit(ks, sn);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TBH, 0);
+#pragma unroll
+    for (int x = 0; x < QK * TBH - 2 * TBH; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TBH, 0);
+  };
+  auto pv_emit = [&](const uint16_t* vs) __attribute__((always_inline)) {
     // O^T += V^T P^T. A operand (row = channel, k-slots = keys
     // kh*KH + tb*32 + 16*s2 + 4*q2 + [0,4) and the same + 8) by two transpose reads:
     // lane (G16, j16) fetches key tok0 + j16/4, channels chb + 4*(j16%4) + [0,4)
@@ -400,7 +399,11 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vf[tb * 2 + s2][cb]), pb[tb][s2], oacc[cb], 0, 0, 0);
-    constexpr int NM = TBH * 2 * CB;   // MFMAs (two transpose reads each)
+  };
+  constexpr int NQ = QK * TBH;       // QK MFMAs (one LDS read each)
+  constexpr int NM = TBH * 2 * CB;   // PV MFMAs (two transpose reads each)
+  auto pv = [&](const uint16_t* vs) __attribute__((always_inline)) {
+    pv_emit(vs);
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * CB, 0);
 #pragma unroll
     for (int x = 0; x < NM - CB; ++x) {
@@ -409,42 +412,116 @@ __global__ __launch_bounds__(4 * T, 1) void prefill_kernel(const PrefillArgs a) 
     }
     __builtin_amdgcn_sched_group_barrier(0x008, CB, 0);
   };
+  // One basic block: the step's tile loads (emitted by the caller just before), S(n+1)
+  // = K_{n+1} Q^T on the matrix cores while the vector ALUs turn S(n) into bf16
+  // weights, then O += P(n) V_n. Scheduled as rounds of 1 QK MFMA, 1 LDS read, NV
+  // vector instructions and (in the first NVM rounds) 1 global load, the last rounds
+  // starting the V reads; then rounds of 1 PV MFMA and 2 transpose reads. The loads
+  // leave one by one between the MFMAs: issued back to back by every wave at once they
+  // queue in the texture unit and stall each wave until its last one is accepted.
+  constexpr int NVM = 2 * IT + 1;   // tile loads (K and V) + the page-table load
+  auto qk_p_pv = [&](const uint16_t* ks, f32x16 (&sn)[TBH], f32x16 (&sc)[TBH], const uint16_t* vs)
+      __attribute__((always_inline)) {
+    qk_emit(ks, sn);
+    softmax_p(sc);
+    pv_emit(vs);
+    constexpr int NV = 7;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TBH, 0);
+#pragma unroll
+    for (int x = 0; x < NQ; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (x < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      if (x < NQ - 2 * TBH) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);
+    }
+#pragma unroll
+    for (int x = 0; x < NM; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (NQ + x < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  };
 
-  // ---- per kept tile n (double-buffered K and V): wait for tile n, then issue tile
-  // n+1's loads (every wave its 16-row block) and compute tile n: QK, softmax, PV.
-  // The loop is unrolled by two so that the buffer parity of every access is a
-  // compile-time constant (tag par).
+  // ---- software-pipelined loop over the kept tiles. Step n (after a barrier):
+  //   issue K of tile n+2 (into tile n's K buffer) and V of tile n+1 (into tile n-1's
+  //   V buffer); S(n+1) = K_{n+1} Q^T interleaved with the softmax of S(n); rescale O;
+  //   O += P(n) V_n.
+  // The barrier of step n follows every wave's reads of K_n (step n-1's QK) and V_{n-1}
+  // (step n-1's PV), and every wave's wait for its loads of K_{n+1} and V_n. The last
+  // step has no next tile: softmax (with the causal cut if it is the diagonal tile,
+  // which when kept is always the last) and PV only. The loop is unrolled by two so
+  // that buffer and score-register parities are compile-time constants (tag par).
   auto kbuf = [&](auto par) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (decltype(par)::value == 0) return lds_k0; else return lds_k1;
   };
   auto vbuf = [&](auto par) __attribute__((always_inline)) -> uint16_t* {
     if constexpr (decltype(par)::value == 0) return lds_v0; else return lds_v1;
   };
+  auto sbuf = [&](auto par) __attribute__((always_inline)) -> f32x16 (&)[TBH] {
+    if constexpr (decltype(par)::value == 0) return s0; else return s1;
+  };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  auto body = [&](int n, auto par) __attribute__((always_inline)) {
+  // page of tile n+1 (scalar) and a lane copy of the page of tile n+2 (loaded one step
+  // ahead of its use)
+  int32_t pg1 = 0, pg2_lane = 0;
+  wait_vm_all();
+  __syncthreads();
+  if (n_tiles > 1) {
+    const int j1 = tile_at(1);
+    pg1 = ptab[__builtin_amdgcn_readfirstlane(slot_of(j1))];
+    issue(a.k_cache, lds_k1, j1, pg1, 1);
+    if (n_tiles > 2) pg2_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(2)));
+  }
+  if (n_tiles > 0) qk_only(lds_k0, s0);
+  auto step = [&](int n, auto par) __attribute__((always_inline)) {
     using Q = std::integral_constant<int, 1 - decltype(par)::value>;
-    const int j = tile_at(n);
     wait_vm_all();
     __syncthreads();
-    if (n + 1 < n_tiles) {
-      const int jn = tile_at(n + 1);
-      const int32_t pn = __builtin_amdgcn_readfirstlane(pn_lane);
-      issue(a.k_cache, kbuf(Q{}), jn, pn, 1);
-      issue(a.v_cache, vbuf(Q{}), jn, pn, 0);
-      if (n + 2 < n_tiles) pn_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(n + 2)));
+    const int32_t pgk = __builtin_amdgcn_readfirstlane(pg2_lane);
+    const int j1 = tile_at(n + 1);
+    const int j2 = tile_at(min(n + 2, n_tiles - 1));
+    const int j3 = tile_at(min(n + 3, n_tiles - 1));
+    softmax_max(sbuf(par));
+    rescale_o();
+    // from here one basic block (the loads are issued branch-free: past the last tile,
+    // K goes out as an empty load into the free buffer, the page entry is re-read)
+    issue(a.k_cache, kbuf(par), j2, pgk, 1, n + 2 < n_tiles);
+    issue(a.v_cache, vbuf(Q{}), j1, pg1, 0);
+    pg2_lane = __builtin_nontemporal_load(ptab_v + slot_of(j3));
+    qk_p_pv(kbuf(Q{}), sbuf(Q{}), sbuf(par), vbuf(par));
+    pg1 = pgk;
+  };
+  auto last = [&](int n, auto par) __attribute__((always_inline)) {
+    wait_vm_all();
+    __syncthreads();
+    if (tile_at(n) == i) {  // causal cut on the diagonal tile
+      f32x16(&st)[TBH] = sbuf(par);
+#pragma unroll
+      for (int tb = 0; tb < TBH; ++tb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kh * KH + tb * 32 + 8 * (e >> 2) + 4 * q2 + (e & 3);
+          if (key > qi) st[tb][e] = kNegInf;
+        }
     }
-    qk(kbuf(par));
-    softmax(j == i);
+    softmax_max(sbuf(par));
+    rescale_o();
+    softmax_p(sbuf(par));
     pv(vbuf(par));
   };
-  if (n_tiles > 1) pn_lane = __builtin_nontemporal_load(ptab_v + slot_of(tile_at(1)));
   int n = 0;
-  for (; n + 1 < n_tiles; n += 2) {
-    body(n, P0{});
-    body(n + 1, P1{});
+  for (; n + 2 < n_tiles; n += 2) {
+    step(n, P0{});
+    step(n + 1, P1{});
   }
-  if (n < n_tiles) body(n, P0{});
+  if (n + 1 < n_tiles) {
+    step(n, P0{});
+    last(n + 1, P1{});
+  } else if (n < n_tiles) {
+    last(n, P0{});
+  }
 
   // ---- merge the two key halves of each query group through LDS, then O / l, lse.
   // Half 1 parks O in the K buffers (query group g in region g: 16-byte chunk c of
