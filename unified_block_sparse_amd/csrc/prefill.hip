@@ -4,26 +4,27 @@
 // plus a local window and never visit the tiles in between; one kernel serves both
 // head kinds).
 //
-// One work-group per (query head h, query tile i), one work-group per CU. Its 2T/32
-// waves form T/32 query groups of 32 rows times 2 key halves: wave (qg, kh) owns
-// query rows qg*32..+32 against keys kh*T/2..+T/2 of every kept tile, with its own
-// running (max, sum, O); the two halves merge through LDS at the end.
+// One work-group per (query head h, query tile i), two work-groups per CU. Its T/32
+// waves each own 32 query rows against every key of the kept tiles, with their own
+// running (max, sum, O). Keys go by in steps of 64 (a kept tile is T/64 steps), so the
+// K and V of a step take 16 KiB each at D = 128 and two work-groups fit in LDS with
+// their buffers doubled; each synchronises only its own waves, so the barrier and
+// softmax phases of one overlap the matrix work of the other.
 //
 // Kept tiles: dense heads compact their mask row into an LDS list once (block-wide
-// scan); streaming heads enumerate the Lambda set arithmetically. Skipped tiles are
-// never loaded.
+// scan); streaming heads write their Lambda set there arithmetically. Skipped tiles
+// are never loaded.
 //
-// Per kept tile (K and V are double-buffered in LDS, T x D bf16 each):
-//   K, V:  global -> LDS with direct-to-LDS 16-byte buffer loads (scalar resource per
-//          group of rows, per-lane offsets fixed for the whole loop), issued one tile
-//          ahead so they stream in while the current tile is computed
-//   S^T  = K Q^T on bf16 MFMA 32x32x16 (Q resident in registers as the B operand)
-//   online softmax per query row in the log2 domain; causal cut on the diagonal tile
-//   O^T += V^T P^T on bf16 MFMA 32x32x16; V^T comes from the row-major tile through
-//          the LDS transpose read (ds_read_b64_tr_b16); P stays in registers
-// The two waves that share a SIMD overlap each other's softmax and matrix work
-// through the hardware's wave interleaving; within a wave, independent MFMA chains
-// are interleaved with the LDS operand reads (sched_group_barrier).
+// Per step s (software-pipelined; K and V double-buffered in LDS):
+//   loads:  K of step s+2 and V of step s+1, global -> LDS with direct-to-LDS 16-byte
+//           buffer loads (scalar resource per 16-row block, per-lane offsets fixed for
+//           the whole loop), spread one by one between the MFMAs
+//   S^T  = K Q^T of step s+1 on bf16 MFMA 32x32x16 (Q resident in registers as the B
+//           operand), interleaved with
+//   the online softmax of step s per query row in the log2 domain (lazy rescaling of
+//           O, bf16 weights, causal cut on the diagonal tile), then
+//   O^T += V^T P^T of step s on bf16 MFMA 32x32x16; V^T comes from the row-major tile
+//           through the LDS transpose read (ds_read_b64_tr_b16); P stays in registers.
 // Rows of both buffers are XOR-swizzled at 16-byte granularity so the operand reads
 // are free of bank conflicts; the direct-to-LDS loads write the swizzled layout by
 // choosing which global chunk each lane fetches.
@@ -427,17 +428,19 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   };
   // One basic block: the step's loads (emitted by the caller just before), S(s+1) =
   // K_{s+1} Q^T on the matrix cores while the vector ALUs turn S(s) into bf16 weights,
-  // then O += P(s) V_s. Scheduled as rounds of 1 QK MFMA, 1 LDS read, NV vector
-  // instructions and (in the first NVM rounds) 1 global load, the last rounds starting
-  // the V reads; then rounds of 1 PV MFMA and 2 transpose reads. The loads leave one by
-  // one between the MFMAs: issued back to back by every wave at once they queue in the
-  // texture unit and stall each wave until its last one is accepted.
+  // then O += P(s) V_s while they take the row max of S(s+1). Scheduled as rounds of
+  // 1 QK MFMA, 1 LDS read, NV vector instructions and (in the first NVM rounds) 1
+  // global load, the last rounds starting the V reads; then rounds of 1 PV MFMA, 2
+  // transpose reads and 2 vector instructions. The loads leave one by one between the
+  // MFMAs: issued back to back by every wave at once they queue in the texture unit and
+  // stall each wave until its last one is accepted.
   constexpr int NVM = 2 * RB * IT + 1;   // tile loads (K and V) + the page-table load
   auto qk_p_pv = [&](const uint16_t* ks, f32x16 (&sn)[TB], f32x16 (&sc)[TB], const uint16_t* vs)
       __attribute__((always_inline)) {
     qk_emit(ks, sn);
     softmax_p(sc);
     pv_emit(vs);
+    softmax_max(sn);   // the next step's row max, in the PV rounds
     constexpr int NV = 7;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * TB, 0);
 #pragma unroll
@@ -453,6 +456,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (NQ + x < NVM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
     }
   };
 
@@ -475,41 +479,52 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  // lane-held page-table entries of steps s+1 and s+2 (each loaded a step before use)
+  // lane-held page-table entries of steps s+1 and s+2 (each loaded a step before use),
+  // and the kept-tile ids of steps s+1 and s+2 (carried from step to step)
   int32_t pg1 = 0, pg2 = 0;
+  int jt1 = 0, jt2 = 0;
   wait_vm_all();
   __syncthreads();
   if (n_steps > 1) {
-    const int j1 = tile_at(1 / NS);
-    pg1 = page_lanes(j1, 1 % NS);
-    issue_step(a.k_cache, lds_k1, j1, 1 % NS, pg1, 1, true);
-    if (n_steps > 2) pg2 = page_lanes(tile_at(2 / NS), 2 % NS);
+    jt1 = tile_at(1 / NS);
+    jt2 = tile_at(min(2, n_steps - 1) / NS);
+    pg1 = page_lanes(jt1, 1 % NS);
+    issue_step(a.k_cache, lds_k1, jt1, 1 % NS, pg1, 1, true);
+    if (n_steps > 2) pg2 = page_lanes(jt2, 2 % NS);
   }
-  if (n_steps > 0) qk_only(lds_k0, s0);
+  // Invariant at the top of step s: S(s) is cut (if diagonal) and its row max taken
+  // (m_run, alpha, grow, mofs are those of step s).
+  if (n_steps > 0) {
+    qk_only(lds_k0, s0);
+    if (diag_last && 0 >= n_steps - NS) diag_cut(s0, 0);
+    softmax_max(s0);
+  }
   auto step = [&](int s, auto par) __attribute__((always_inline)) {
     using Q = std::integral_constant<int, 1 - decltype(par)::value>;
+    const int s3c = min(s + 3, n_steps - 1);
+    const int jt3 = tile_at(s3c / NS);   // (the tile list is read-only: before the wait)
     wait_vm_all();
     __syncthreads();
-    const int s2c = min(s + 2, n_steps - 1), s3c = min(s + 3, n_steps - 1);
-    const int j1 = tile_at((s + 1) / NS);
-    const int j2 = tile_at(s2c / NS);
-    const int j3 = tile_at(s3c / NS);
-    if (diag_last && s >= n_steps - NS) diag_cut(sbuf(par), s % NS);
-    softmax_max(sbuf(par));
     rescale_o();
     // from here one basic block (the loads are issued branch-free: past the last step,
     // K goes out as an empty load into the free buffer, the page entry is re-read)
-    issue_step(a.k_cache, kbuf(par), j2, s2c % NS, pg2, 1, s + 2 < n_steps);
-    issue_step(a.v_cache, vbuf(Q{}), j1, (s + 1) % NS, pg1, 0, true);
+    issue_step(a.k_cache, kbuf(par), jt2, min(s + 2, n_steps - 1) % NS, pg2, 1, s + 2 < n_steps);
+    issue_step(a.v_cache, vbuf(Q{}), jt1, (s + 1) % NS, pg1, 0, true);
     pg1 = pg2;
-    pg2 = page_lanes(j3, s3c % NS);
+    pg2 = page_lanes(jt3, s3c % NS);
+    const float m_prev = m_run;
     qk_p_pv(kbuf(Q{}), sbuf(Q{}), sbuf(par), vbuf(par));
+    jt1 = jt2;
+    jt2 = jt3;
+    if (diag_last && s + 1 >= n_steps - NS) {  // S(s+1) is on the diagonal tile: cut, then redo its max
+      m_run = m_prev;
+      diag_cut(sbuf(Q{}), (s + 1) % NS);
+      softmax_max(sbuf(Q{}));
+    }
   };
   auto last = [&](int s, auto par) __attribute__((always_inline)) {
     wait_vm_all();
     __syncthreads();
-    if (diag_last) diag_cut(sbuf(par), s % NS);
-    softmax_max(sbuf(par));
     rescale_o();
     softmax_p(sbuf(par));
     pv(vbuf(par));
