@@ -12,12 +12,16 @@ build_page_bounds, sparse_prefill, select_pages, sparse_decode in that order: th
 streams > 1.5 GB, which evicts the bounds and K/V pages from L2 and the 256 MB Infinity
 Cache, so selection and decode read cold HBM.
 
+The line also reports, outside the step and outside `value`, selection + decode on
+decode_ragged (B=64 sequences of 16K-128K tokens, Lp=16): the decode path at a batch large
+enough to amortise launches (--no-ragged skips it).
+
 value = 100 * (sum over the step's ops of their roofline time) / (measured step time),
 i.e. the step's speed as a percentage of the MI355X roofline: prefill counted as
 kept-tile flops against dense bf16 MFMA peak, bounds / selection / decode as their
 algorithmic HBM bytes against peak HBM bandwidth.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ragged]
 """
 from __future__ import annotations
 
@@ -54,6 +58,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows-per-head", type=int, default=384)
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the separate decode_ragged step measurement (64 sequences, 16K-128K tokens)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times) and exit: "
                          "the known-size kernel that scales the HBM byte counters")
@@ -185,6 +191,66 @@ def cpu_baseline(c, d, kept_tiles: int, rows_per_head: int, ideal_s: float):
     }
 
 
+# ----------------------------------------------------------------------------- ragged decode
+
+def ragged_decode_step(steps: int, warmup: int):
+    """Selection + decode on decode_ragged (B=64, L_b in [16384, 131072], Lp=16), timed alone.
+
+    Not part of the step above (and not of `value`): it reports the decode path at a batch
+    large enough to amortise launches. Bounds are built once beforehand (they are updated
+    when pages fill, not every step). The 19 GB cache and 0.6 GB of bounds exceed the
+    Infinity Cache, so every step reads mostly HBM.
+    """
+    import torch
+    import unified_block_sparse_amd as ubs
+    from workloads import cases
+    dev = torch.device("cuda:0")
+    r = cases.decode_ragged(dev)
+    bnd = torch.zeros((r.num_physical_pages, r.Hkv, r.P // r.Lp, 2, r.D), dtype=torch.bfloat16, device=dev)
+    sel = torch.empty((r.B, r.Hkv, r.k_pages), dtype=torch.int32, device=dev)
+    num = torch.empty((r.B, r.Hkv), dtype=torch.int32, device=dev)
+    out = torch.empty((r.B, r.Hq, r.D), dtype=torch.float32, device=dev)
+    ubs.build_page_bounds(r.k_cache, r.page_table, r.seq_lens_t, r.head_kind, r.Lp, bounds=bnd)
+
+    def op_select():
+        ubs.select_pages(r.q, bnd, r.page_table, r.seq_lens_t, r.head_kind, r.P, r.token_budget, selected=sel,
+                         num_selected=num)
+
+    def op_decode():
+        ubs.sparse_decode(r.q, r.k_cache, r.v_cache, r.page_table, r.seq_lens_t, r.head_kind, sel, num,
+                          r.sink_tokens, r.local_tokens, r.sm_scale, out=out)
+
+    for _ in range(warmup):
+        op_select()
+        op_decode()
+    torch.cuda.synchronize(dev)
+    sel_h, num_h = sel.cpu().tolist(), num.cpu().tolist()
+    sel_pages = [[sel_h[b][g][:num_h[b][g]] for g in range(r.Hkv)] for b in range(r.B)]
+    _, b_select, b_decode = decode_bytes(r, sel_pages)
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s_ in range(steps):
+        ev[s_][0].record(stream)
+        op_select()
+        ev[s_][1].record(stream)
+        op_decode()
+        ev[s_][2].record(stream)
+    torch.cuda.synchronize(dev)
+    t_sel = sum(e[0].elapsed_time(e[1]) for e in ev) / steps * 1e-3
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / steps * 1e-3
+    t = t_sel + t_dec
+    res = {"workload": "decode_ragged (B=64, L_b uniform in [16384, 131072], Hq=32, Hkv=8, D=128, P=64, Lp=16, "
+                       "budget 4096, streaming 128 + 1024)",
+           "ms": round(t * 1e3, 4), "bytes": b_select + b_decode,
+           "gbps": round((b_select + b_decode) / t / 1e9, 1),
+           "frac": round((b_select + b_decode) / t / 1e9 / PEAK_HBM_GBPS, 4),
+           "select_pages": {"ms": round(t_sel * 1e3, 4), "bytes": b_select, "gbps": round(b_select / t_sel / 1e9, 1)},
+           "sparse_decode": {"ms": round(t_dec * 1e3, 4), "bytes": b_decode, "gbps": round(b_decode / t_dec / 1e9, 1)}}
+    del r, bnd
+    torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -309,6 +375,8 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
     }
+    if not args.no_ragged:
+        breakdown["decode_ragged_step"] = ragged_decode_step(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, d, kept, args.cpu_rows_per_head, ideal_s)
     print(json.dumps(result), flush=True)
