@@ -220,10 +220,13 @@ size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_selected < 0 || sink_tokens < 0 ||
       local_tokens < 0)
     return 256;
-  // the split plan depends only on these sizes; all heads dense is the largest case
-  const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, Hkv, P, max_selected, sink_tokens, local_tokens);
-  const ubs::DecodePlan ps = ubs::plan_decode(B, Hkv, 0, P, max_selected, sink_tokens, local_tokens);
-  const int ms = pl.max_splits > ps.max_splits ? pl.max_splits : ps.max_splits;
+  // the split plan depends only on these sizes and the number of dense KV heads: take
+  // the largest over every count
+  int ms = 1;
+  for (int nd = 0; nd <= Hkv; ++nd) {
+    const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, nd, P, max_selected, sink_tokens, local_tokens);
+    ms = pl.max_splits > ms ? pl.max_splits : ms;
+  }
   return ((size_t)B * Hq * ms * (D + 2) * sizeof(float) + 255) / 256 * 256;
 }
 

@@ -4,20 +4,25 @@
 // streaming heads in decode as well).
 //
 // Work split: (sequence b, KV head g, split s) per 256-thread work-group. The key set
-// of (b, g) is a list of chunks, each a token range inside one physical page (a
-// selected page, or a piece of the sink / local window); wave w of split s takes
-// chunks (s*4 + w)*cpw ... + cpw - 1. Inside a wave:
+// of (b, g) is a list of 32-token chunks, each inside one physical page (a part of a
+// selected page, or of a page of the sink / local window); wave w of split s streams
+// chunks (s*4 + w)*cpw ... + cpw - 1. It first resolves all their pages (one round
+// trip through the selection and the page table for up to 64 chunks), then keeps the
+// K/V loads of chunk t+1 in flight while it computes chunk t:
 //   S = Q_g K^T  : bf16 MFMA 16x16x32 (rows = the G query heads, columns = 16 keys),
-//                  K rows read straight from HBM, 64 contiguous bytes per lane;
+//                  K rows read straight from HBM, each load instruction 64 contiguous
+//                  bytes of each of 16 rows;
 //   online softmax in the log2 domain (fp32);
 //   O += P V     : fp32 FMAs, each lane owning 8 channels of one key row, V read with
-//                  16-byte coalesced loads, P broadcast through LDS.
+//                  16-byte loads that cover whole rows, P broadcast through LDS.
 // Partial (max, sum, output) triples of the 4 waves are merged through LDS; the
 // work-group writes one partial per split (or the output when the key set has one
 // split), and a second launch merges the splits of each (b, g) with a log-sum-exp
 // combine staged in LDS.
 #include "common.h"
 #include "launch.h"
+
+#include <algorithm>
 
 namespace ubs {
 
@@ -79,11 +84,13 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
 
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
-  constexpr int KK = D / 32;   // QK MFMA steps
-  constexpr int CH = D / 8;    // lanes per V row
+  constexpr int KK = D / 32;   // QK MFMA steps (16x16x32)
+  constexpr int CH = D / 8;    // lanes per V row (16-byte pieces)
   constexpr int TG = 64 / CH;  // token groups in P.V
-  constexpr int GL = (G + 3) / 4;  // 16-lane groups that hold query heads
-  __shared__ float p_lds[4][64][G];
+  constexpr int CT = 32;       // tokens per chunk
+  constexpr int NB = CT / 16;  // 16-key MFMA blocks per chunk
+  constexpr int VR = CT / TG;  // V rows per lane and chunk
+  __shared__ float p_lds[4][CT][G];
   __shared__ float w_m[4][G], w_l[4][G];
   __shared__ float w_o[4][G][D];
 
@@ -113,16 +120,24 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   const int nsel = streaming ? 0 : min(a.num_selected[(int64_t)b * a.Hkv + g], a.max_selected);
   const float scale_log2 = a.sm_scale * kLog2e;
 
+  // ---- this wave's chunks c0 .. c0 + cpw - 1 (chunk c: part c % CPP of page-level
+  // chunk c / CPP, CT tokens)
+  const int P = a.P;
+  const int CPP = (P + CT - 1) / CT;
+  const int cpw = a.chunks_per_wave;
+  const int c0 = (split * 4 + wave) * cpw;
+
   // ---- Q as the MFMA A operand: row m = query head (zero rows past G); k-slot group
-  // qg = l/16 holds channels qg*D/4 + kk*8 + [0, 8) for step kk.
+  // qg = l/16 holds channels kk*32 + qg*8 + [0, 8) for step kk (so that one K load
+  // instruction reads 64 contiguous bytes of each of its 16 rows).
   const int m = lane & 15;
   const int qg = lane >> 4;
   bf16x8 qa[KK];
   {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + m) * D + qg * (D / 4);
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + m) * D + qg * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qa[kk] = as_bf16x8((m < G) ? ld16(qrow + kk * 8) : u32x4{0, 0, 0, 0});
+      qa[kk] = as_bf16x8((m < G) ? ld16(qrow + kk * 32) : u32x4{0, 0, 0, 0});
   }
 
   float m_run[4];   // running max of heads 4*qg + i (lane-replicated within a 16-lane group)
@@ -138,96 +153,144 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   }
   const int cc = lane % CH;
   const int tg = lane / CH;
-  const int64_t head_stride = (int64_t)a.P * D;  // one (page, KV head) slab
+  const int64_t head_stride = (int64_t)P * D;  // one (page, KV head) slab
+  int d_page = -1, d_r0 = 0, d_lo = 0, d_hi = 0;   // chunk descriptors, one chunk per lane
 
-  for (int t = 0; t < a.chunks_per_wave; ++t) {
-    const int c = (split * 4 + wave) * a.chunks_per_wave + t;
-    const Chunk ch = decode_chunk(a, streaming, b, g, c, L, nsel);
-    if (ch.page < 0) continue;  // wave-uniform
-    const uint16_t* kslab = a.k_cache + ((int64_t)ch.page * a.Hkv + g) * head_stride;
-    const uint16_t* vslab = a.v_cache + ((int64_t)ch.page * a.Hkv + g) * head_stride;
-    const int r_lo = ch.t0 - ch.row_base, r_hi = ch.t1 - ch.row_base;   // valid rows [r_lo, r_hi)
-    for (int r0 = (r_lo / 64) * 64; r0 < r_hi; r0 += 64) {
-      // ---- issue every K and V load of the segment first (rows are clamped into the
-      // page; rows outside [r_lo, r_hi) are loaded but never weighted)
-      u32x4 kreg[4][KK];
+  // ---- K and V of one chunk into registers, branch-free: each tensor through a buffer
+  // resource over its (page, KV head) slab, of size zero for an empty chunk (the loads
+  // then read nothing and return zeros). Without a branch the compiler can count the
+  // loads in flight and wait for chunk t alone while chunk t+1's are outstanding. Rows
+  // are clamped into the page; rows outside [lo, hi) are loaded but never weighted.
+  auto slab_rsrc = [&](const uint16_t* cache, int page) __attribute__((always_inline)) {
+    const uint64_t addr = (uint64_t)(cache + ((int64_t)max(page, 0) * a.Hkv + g) * head_stride);
+    const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, page >= 0 ? P * D * 2 : 0, 0x00020000);
+  };
+  auto load = [&](int t, int nt, u32x4 (&kr)[NB][KK], u32x4 (&vr)[VR]) __attribute__((always_inline)) {
+    const int page = t < nt ? __builtin_amdgcn_readlane(d_page, min(t, 63)) : -1;
+    const int r0 = __builtin_amdgcn_readlane(d_r0, min(t, 63));
+    const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache, page);
+    const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache, page);
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const int row = min(r0 + blk * 16 + m, a.P - 1);
-        const uint16_t* krow = kslab + (int64_t)row * D + qg * (D / 4);
+    for (int blk = 0; blk < NB; ++blk) {
+      const int row = min(r0 + blk * 16 + m, P - 1);
+      const int off = (row * D + qg * 8) * 2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kreg[blk][kk] = ld16(krow + kk * 8);
-      }
-      u32x4 vreg[64 / TG];
+      for (int kk = 0; kk < KK; ++kk) kr[blk][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 64, 0, 0);
+    }
 #pragma unroll
-      for (int x = 0; x < 64 / TG; ++x) {
-        const int row = min(r0 + tg + TG * x, a.P - 1);
-        vreg[x] = ld16(vslab + (int64_t)row * D + cc * 8);
-      }
-      // ---- S for 4 blocks of 16 rows
-      f32x4 s[4];
+    for (int x = 0; x < VR; ++x) {
+      const int row = min(r0 + tg + TG * x, P - 1);
+      vr[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * D + cc * 8) * 2, 0, 0);
+    }
+  };
+  // ---- online softmax and P.V over one chunk already in registers
+  auto compute = [&](int t, int nt, const u32x4 (&kr)[NB][KK], const u32x4 (&vr)[VR]) __attribute__((always_inline)) {
+    const int page = t < nt ? __builtin_amdgcn_readlane(d_page, min(t, 63)) : -1;
+    if (page < 0) return;
+    const int r0 = __builtin_amdgcn_readlane(d_r0, t);
+    const int lo = __builtin_amdgcn_readlane(d_lo, t), hi = __builtin_amdgcn_readlane(d_hi, t);
+    // S for NB blocks of 16 rows
+    f32x4 s[NB];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(kreg[blk][kk]), acc, 0, 0, 0);
-        const int row = r0 + blk * 16 + m;
-        const bool ok = row >= r_lo && row < r_hi;
+      for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(kr[blk][kk]), acc, 0, 0, 0);
+      const int row = r0 + blk * 16 + m;
+      const bool ok = row >= lo && row < hi;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
-      }
-      // ---- segment max per head (heads 4*qg + i), then running max and weights
-      float alpha_i[4];
+      for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
+    }
+    // chunk max per head (heads 4*qg + i), then running max and weights
+    float alpha_i[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float mx = s[0][i];
+#pragma unroll
+      for (int blk = 1; blk < NB; ++blk) mx = fmaxf(mx, s[blk][i]);
+#pragma unroll
+      for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, shfl_xor(mx, o2));
+      const float mn = fmaxf(m_run[i], mx);
+      alpha_i[i] = rescale_factor(m_run[i], mn);
+      m_run[i] = mn;
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float mx = fmaxf(fmaxf(s[0][i], s[1][i]), fmaxf(s[2][i], s[3][i]));
-#pragma unroll
-        for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, shfl_xor(mx, o2));
-        const float mn = fmaxf(m_run[i], mx);
-        alpha_i[i] = rescale_factor(m_run[i], mn);
-        m_run[i] = mn;
+        const int h = qg * 4 + i;
+        if (h < G) p_lds[wave][blk * 16 + m][h] = softmax_weight(s[blk][i], m_run[i]);
       }
+    wave_sync_lds();
+    float alpha[G];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+    for (int h = 0; h < G; ++h) alpha[h] = readlane_f(alpha_i[h & 3], 16 * (h >> 2));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = qg * 4 + i;
-          if (h < G) p_lds[wave][blk * 16 + m][h] = softmax_weight(s[blk][i], m_run[i]);
-        }
-      wave_sync_lds();
-      // ---- broadcast rescale factors and apply
-      float alpha[G];
+    for (int h = 0; h < G; ++h) {
+      lsum[h] *= alpha[h];
 #pragma unroll
-      for (int h = 0; h < G; ++h) alpha[h] = readlane_f(alpha_i[h & 3], 16 * (h >> 2));
+      for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+    }
+    // O += P V over the chunk's rows tg, tg + TG, ... (weights of rows outside [lo, hi)
+    // are zero and their V values are replaced by zero)
+#pragma unroll
+    for (int x = 0; x < VR; ++x) {
+      const int rr = tg + TG * x;
+      const int row = r0 + rr;
+      const bool ok = row >= lo && row < hi;
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = ok ? bf16_lo(vr[x][e]) : 0.f;
+        vf[2 * e + 1] = ok ? bf16_hi(vr[x][e]) : 0.f;
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        lsum[h] *= alpha[h];
+        const float p = p_lds[wave][rr][h];
+        lsum[h] += p;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
       }
-      // ---- O += P V over the segment's rows tg, tg + TG, ... (weights of rows outside
-      // [r_lo, r_hi) are zero and their V values are replaced by zero)
-#pragma unroll
-      for (int x = 0; x < 64 / TG; ++x) {
-        const int rr = tg + TG * x;
-        const int row = r0 + rr;
-        const bool ok = row >= r_lo && row < r_hi;
-        float vf[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[2 * e] = ok ? bf16_lo(vreg[x][e]) : 0.f;
-          vf[2 * e + 1] = ok ? bf16_hi(vreg[x][e]) : 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = p_lds[wave][rr][h];
-          lsum[h] += p;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
-        }
+    }
+    wave_sync_lds();
+  };
+  // ---- the wave's chunks, 64 at a time. Lane t resolves chunk c0 + t0 + t to its
+  // physical page and valid rows [lo, hi) of the page, so the index chain (selection ->
+  // page table) costs one round trip per 64 chunks, before any of their K/V loads. Then
+  // the loads of chunk t+1 are in flight while chunk t is computed (register double
+  // buffer; unrolled by two so each buffer is a fixed register set).
+  u32x4 ka[NB][KK], va[VR], kb[NB][KK], vb[VR];
+  for (int t0 = 0; t0 < cpw; t0 += 64) {
+    const int nt = min(64, cpw - t0);
+    d_page = -1;
+    if (lane < nt) {
+      const int c = c0 + t0 + lane;
+      const Chunk ch = decode_chunk(a, streaming, b, g, c / CPP, L, nsel);
+      const int r0 = (c % CPP) * CT;                    // first row of the part in the page
+      const int lo = max(ch.t0 - ch.row_base, r0), hi = min(ch.t1 - ch.row_base, r0 + CT);
+      if (ch.page >= 0 && lo < hi) {
+        d_page = ch.page;
+        d_r0 = r0;
+        d_lo = lo;
+        d_hi = hi;
       }
-      wave_sync_lds();
+    }
+    // (chunks past nt are empty: their loads read nothing and their compute is skipped;
+    // the scheduling barriers keep each chunk's loads after the previous compute, so
+    // at most two chunks' registers are live)
+    load(0, nt, ka, va);
+    for (int t = 0; t < nt; t += 2) {
+      load(t + 1, nt, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t, nt, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      load(t + 2, nt, ka, va);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(t + 1, nt, kb, vb);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -254,7 +317,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       for (int e = 0; e < 8; ++e) w_o[wave][h][cc * 8 + e] = o[h][e];
     }
   }
-  (void)GL;
   __syncthreads();
 
   // ---- merge the 4 waves: element (h, c) per thread
@@ -334,10 +396,17 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
 
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local) {
   DecodePlan pl{};
-  pl.chunks_dense = max_selected;
-  pl.chunks_stream = (sink + P - 1) / P + (local + P - 1) / P + 1;
-  // one chunk per wave unless the split count would exceed what a work-group can merge
-  int cpw = 1;
+  const int cpp = (P + 31) / 32;   // 32-token chunks per page
+  pl.chunks_dense = max_selected * cpp;
+  pl.chunks_stream = ((sink + P - 1) / P + (local + P - 1) / P + 1) * cpp;
+  // Chunks per wave: 4 to 8, so that each wave streams several chunks (the loads of the
+  // next overlap the compute of this one and the index chain is paid once per wave);
+  // 8 once the batch fills two work-groups per CU with 4 (measured on MI355X: 4 is best
+  // for 4 x 32K-token sequences, 8 for 64 sequences of 16K-128K tokens). More if the split
+  // count would exceed what the merge can combine.
+  const int64_t total = (int64_t)B * ((int64_t)n_dense * pl.chunks_dense + (int64_t)(Hkv - n_dense) * pl.chunks_stream);
+  constexpr int64_t kWaveSlots = 4 * 2 * 256;
+  int cpw = (int)std::min<int64_t>(8, std::max<int64_t>(4, (total + kWaveSlots - 1) / kWaveSlots));
   for (;;) {
     const int sd = n_dense > 0 ? (pl.chunks_dense + 4 * cpw - 1) / (4 * cpw) : 1;
     const int ss = (Hkv - n_dense) > 0 ? (pl.chunks_stream + 4 * cpw - 1) / (4 * cpw) : 1;
@@ -350,7 +419,6 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
     cpw *= 2;
   }
   pl.max_splits = pl.splits_dense > pl.splits_stream ? pl.splits_dense : pl.splits_stream;
-  (void)B;
   return pl;
 }
 
