@@ -125,3 +125,29 @@ def test_decode_ragged_sampled_sequences():
     longest = int(np.argmax(c.seq_lens))
     batches = sorted(set([longest] + rng.choice(c.B, size=3, replace=False).tolist()))
     _decode_parity(c, batches, "decode_ragged")
+
+
+def test_decode_reused_selection():
+    """Selection reused across decode steps (LServe, Decode Phase: the page selection of
+    one step serves the next ones): select with one step's queries, then decode R = 4
+    steps, each with fresh queries, against the cached selection. Every step must equal
+    the oracle's decode of that step's queries over exactly the cached pages."""
+    from workloads import gen
+    c = cases.decode_llama8b(DEV)
+    bnd = ubs.build_page_bounds(c.k_cache, c.page_table, c.seq_lens_t, c.head_kind, c.Lp)
+    sel, num = ubs.select_pages(c.q, bnd, c.page_table, c.seq_lens_t, c.head_kind, c.P, c.token_budget)
+    _sync()
+    batches = list(range(c.B))
+    _, kb, vb, pt, lens = decode_subset(c, batches)
+    sel_h, num_h = sel.cpu().numpy(), num.cpu().numpy()
+    cached = {(i, g): [int(x) for x in sel_h[i, g, :num_h[i, g]]]
+              for i in range(c.B) for g in range(c.Hkv) if not c.head_kind[g]}
+    for step in range(4):
+        q = gen.normal_bf16((c.B, c.Hq, c.D), 1002, 90 + step, DEV)
+        out, lse = ubs.sparse_decode(q, c.k_cache, c.v_cache, c.page_table, c.seq_lens_t, c.head_kind, sel, num,
+                                     c.sink_tokens, c.local_tokens, c.sm_scale, return_lse=True)
+        _sync()
+        ref, ref_lse = oracle.decode_ref(bits(q), kb, vb, pt, lens, c.Hq, c.Hkv, c.P, c.head_kind, cached,
+                                         c.sink_tokens, c.local_tokens, c.sm_scale)
+        mx, mn = assert_attention_close(out.cpu().numpy(), ref, f"reused selection, step {step}")
+        assert_lse_close(lse.cpu().numpy(), ref_lse, f"reused selection, step {step} lse")
