@@ -141,6 +141,74 @@ def prefill_kept_tile_count(nT: int, Hq: int, Hkv: int, head_kind, block_mask, s
     return total
 
 
+# ----------------------------------------------------------------------------- block-mask estimation
+
+def tile_means_ref(x: np.ndarray, T: int) -> np.ndarray:
+    """Mean over the rows of every T-row tile of x [L, D] (fp64); a last, partial tile
+    averages the rows it has."""
+    L, D = x.shape
+    nT = (L + T - 1) // T
+    out = np.empty((nT, D))
+    for i in range(nT):
+        out[i] = x[i * T:min((i + 1) * T, L)].mean(axis=0)
+    return out
+
+
+def keep_count(i: int, keep_num: int, keep_den: int) -> int:
+    """Tiles kept in query-tile row i, the diagonal included: ceil(keep_num*(i+1)/keep_den)."""
+    return (keep_num * (i + 1) + keep_den - 1) // keep_den
+
+
+def meanpool_mask_ref(q_bits, k_cache_bits, page_table, L: int, Hq: int, Hkv: int, D: int, P: int,
+                      T: int, head_kind, keep_num: int = 3, keep_den: int = 10,
+                      heads: Optional[Sequence[int]] = None):
+    """Block mask of the dense heads from mean-pooled tile scores, fp64.
+
+    The dense heads' mask rule of the Llama-3-8B prefill workload, a query-tile-level
+    estimate of the block sparsity that the blog's LServe prefill section applies (a KV
+    tile computed or skipped whole per query tile). For dense query head h (KV head
+    g = h // (Hq/Hkv)) and query tile i:
+        score[i, j] = mean over the rows of Q_h tile i . mean over the rows of K_g tile j
+        (j < i), n_i = ceil(keep_num*(i+1)/keep_den) tiles kept, the diagonal included:
+        the diagonal and the n_i - 1 strictly-lower tiles of largest score, equal scores
+        going to the lower j. Entries above the diagonal are 0.
+    A last, partial tile averages the rows it has. heads: the query heads to evaluate
+    (default: every dense one). Returns (mask [n, nT, nT] uint8, score [n, nT, nT] with
+    -inf outside j < i, mag [n, nT, nT] = sum_c |qbar_c * kbar_c|, the scale of a score's
+    rounding error in lower precision), in the order of heads.
+    """
+    G = Hq // Hkv
+    nT = (L + T - 1) // T
+    if heads is None:
+        heads = [h for h in range(Hq) if not head_kind[h // G]]
+    heads = [int(h) for h in heads]
+    K = tokens_of_sequence(np.asarray(k_cache_bits), page_table, L, P)        # [L, Hkv, D] bits
+    kmeans: Dict[int, np.ndarray] = {}
+    mask = np.zeros((len(heads), nT, nT), dtype=np.uint8)
+    score = np.full((len(heads), nT, nT), -math.inf)
+    mag = np.zeros((len(heads), nT, nT))
+    qb = np.asarray(q_bits)
+    for n, h in enumerate(heads):
+        g = h // G
+        if g not in kmeans:
+            kmeans[g] = tile_means_ref(bf16_to_f64(K[:, g, :]), T)
+        km = kmeans[g]
+        qm = tile_means_ref(bf16_to_f64(qb[:, h, :]), T)
+        s = qm @ km.T
+        m = np.abs(qm) @ np.abs(km).T
+        for i in range(nT):
+            mask[n, i, i] = 1
+            lower = s[i, :i]
+            score[n, i, :i] = lower
+            mag[n, i, :i] = m[i, :i]
+            take = keep_count(i, keep_num, keep_den) - 1
+            if take > 0:
+                # descending score, then ascending j: lexsort's last key is the primary one
+                order = np.lexsort((np.arange(i), -lower))
+                mask[n, i, order[:take]] = 1
+    return mask, score, mag
+
+
 # ----------------------------------------------------------------------------- page bounds
 
 def bounds_ref(k_cache_bits, page_table, seq_lens, P: int, Lp: int, head_kind,

@@ -372,3 +372,104 @@ def test_decode_empty_sequence():
     out, lse = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.numpy(),
                                  [0, 5], 2, 1, 4, [0], {(0, 0): [], (1, 0): [0, 1]}, 1, 1, 1.0)
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0]))
+
+
+# ----------------------------------------------------------------------------- block-mask estimation pins
+
+def _paged(tok_bits, P, seed):
+    """Scatter token-major bits [L, Hkv, D] into a paged cache with a seeded permuted page table."""
+    L, Hkv, D = tok_bits.shape
+    n = (L + P - 1) // P
+    rng = np.random.default_rng(seed)
+    pt = rng.permutation(n + 2)[:n].astype(np.int32)
+    cache = rng.integers(0, 1 << 16, size=(n + 2, Hkv, P, D), dtype=np.uint16)   # noise elsewhere
+    for t in range(L):
+        cache[pt[t // P], :, t % P, :] = tok_bits[t]
+    return cache, pt
+
+
+def _bits_of(x):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("keep", [(3, 10), (1, 2)])
+def test_meanpool_mask_brute_force(keep):
+    """Plain loops over rows, channels and candidates, with Python's sort on (-score, j)."""
+    L, Hq, Hkv, D, P, T = 200, 4, 2, 8, 16, 32        # 7 tiles, the last one 8 rows
+    rng = np.random.default_rng(7)
+    qb = _bits_of(rng.standard_normal((L, Hq, D)))
+    kb_tok = _bits_of(rng.standard_normal((L, Hkv, D)))
+    cache, pt = _paged(kb_tok, P, 8)
+    mask, score, _ = oracle.meanpool_mask_ref(qb, cache, pt, L, Hq, Hkv, D, P, T, [0, 0], keep[0], keep[1])
+    qf = oracle.bf16_to_f64(qb)
+    kf = oracle.bf16_to_f64(kb_tok)
+    nT = (L + T - 1) // T
+    G = Hq // Hkv
+
+    def mean_rows(x, lo, hi):
+        out = [0.0] * D
+        for r in range(lo, hi):
+            for c in range(D):
+                out[c] += float(x[r, c])
+        return [v / (hi - lo) for v in out]
+
+    for h in range(Hq):
+        g = h // G
+        km = [mean_rows(kf[:, g, :], j * T, min((j + 1) * T, L)) for j in range(nT)]
+        for i in range(nT):
+            qm = mean_rows(qf[:, h, :], i * T, min((i + 1) * T, L))
+            s = [sum(qm[c] * km[j][c] for c in range(D)) for j in range(i)]
+            n_i = -(-(keep[0] * (i + 1)) // keep[1])
+            kept = set(sorted(range(i), key=lambda j: (-s[j], j))[:n_i - 1]) | {i}
+            want = [1 if j in kept else 0 for j in range(nT)]
+            assert mask[h, i].tolist() == want, (h, i)
+            for j in range(i):
+                assert abs(score[h, i, j] - s[j]) <= 1e-12 * (1 + abs(s[j]))
+
+
+def test_meanpool_mask_monotone_scores_give_closed_forms():
+    """Queries along channel 0 and key tiles whose channel-0 mean is +-(j+1): scores rise
+    (or fall) with j, so the kept tiles are the n_i - 1 nearest (or the first) ones."""
+    L, Hq, Hkv, D, P, T = 16 * 20, 2, 1, 4, 16, 16
+    nT = L // T
+    q = np.zeros((L, Hq, D)); q[:, :, 0] = 1.0
+    for sign in (1.0, -1.0):
+        k = np.zeros((L, Hkv, D))
+        for t in range(L):
+            k[t, 0, 0] = sign * (t // T + 1)
+        cache, pt = _paged(_bits_of(k), P, 3)
+        mask, _, _ = oracle.meanpool_mask_ref(_bits_of(q), cache, pt, L, Hq, Hkv, D, P, T, [0])
+        for h in range(Hq):
+            for i in range(nT):
+                n_i = oracle.keep_count(i, 3, 10)
+                lower = range(i - n_i + 1, i) if sign > 0 else range(0, n_i - 1)
+                want = np.zeros(nT, dtype=np.uint8)
+                want[list(lower)] = 1
+                want[i] = 1
+                assert np.array_equal(mask[h, i], want), (sign, h, i)
+
+
+def test_meanpool_mask_ties_go_to_lower_tiles_and_counts():
+    """Identical key tiles give equal scores: the kept tiles are the lowest ones. On random
+    data every row keeps exactly n_i tiles and nothing above the diagonal."""
+    L, Hq, Hkv, D, P, T = 32 * 12, 2, 1, 8, 32, 32
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((L, Hq, D))
+    row = rng.standard_normal(D)
+    k = np.tile(row, (L, Hkv, 1))
+    cache, pt = _paged(_bits_of(k), P, 5)
+    mask, _, _ = oracle.meanpool_mask_ref(_bits_of(q), cache, pt, L, Hq, Hkv, D, P, T, [0])
+    nT = L // T
+    for h in range(Hq):
+        for i in range(nT):
+            want = np.zeros(nT, dtype=np.uint8)
+            want[:oracle.keep_count(i, 3, 10) - 1] = 1
+            want[i] = 1
+            assert np.array_equal(mask[h, i], want)
+    k = rng.standard_normal((L, Hkv, D))
+    cache, pt = _paged(_bits_of(k), P, 6)
+    mask, _, _ = oracle.meanpool_mask_ref(_bits_of(q), cache, pt, L, Hq, Hkv, D, P, T, [0])
+    for h in range(Hq):
+        assert not np.triu(mask[h], 1).any()
+        for i in range(nT):
+            assert int(mask[h, i].sum()) == oracle.keep_count(i, 3, 10)
