@@ -14,6 +14,8 @@
  *   select_pages       query-aware page scores and top-k selection.
  *   sparse_decode      GQA decode attention over the kept pages (dense heads)
  *                      or the sink and local tokens (streaming heads).
+ *   estimate_block_mask  the dense heads' prefill block mask from mean-pooled
+ *                      query/key tile scores.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -189,6 +191,41 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
                   const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
                   int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * estimate_block_mask -- the dense heads' prefill block mask from mean-pooled
+ * tile scores (the step before sparse_prefill for dense heads).
+ *
+ * The mask rule of the Llama-3-8B prefill workload: a query-tile-level estimate of
+ * the block sparsity that the blog's "LServe -- Prefill Phase" section applies (a
+ * KV tile is computed or skipped whole per query tile). For every DENSE query head
+ * h (KV head g = h / (Hq/Hkv)) and query tile i (nT = ceil(L / T) tiles, the last
+ * one possibly partial):
+ *     qbar_i = mean over the rows of tile i of q[.][h][:]
+ *     kbar_j = mean over the rows of tile j of the sequence's keys of KV head g
+ *     score[i][j] = qbar_i . kbar_j                       (j < i)
+ *     n_i = ceil(keep_num * (i + 1) / keep_den)           tiles kept, diagonal included
+ *     block_mask[h][i][j] = 1 for j = i and for the n_i - 1 tiles j < i of largest
+ *                           score (equal scores: the lower j first), else 0
+ *                           (entries above the diagonal are 0)
+ * Means and scores are evaluated in fp32 (sums in a fixed order), so tiles whose
+ * score is within rounding of the row's threshold may differ from an exact
+ * evaluation; everything else is exact. Rows of streaming heads are not written.
+ *
+ *   q           bf16 [L][Hq][D]
+ *   k_cache     bf16 [NP][Hkv][P][D]
+ *   page_table  int32 [ceil(L / P)]
+ *   block_mask  uint8 [Hq][nT][nT]   (dense heads' rows fully written)
+ *   workspace   >= ubs_mask_workspace_size(...) bytes, any contents (the tile means)
+ * Supported: D in {64, 128}; T in {64, 128}; P a power of two in [16, 4096];
+ * nT <= 4096; Hq <= 256; 0 < keep_num <= keep_den <= 1024; L >= 0 (L = 0 is a
+ * no-op).
+ */
+size_t ubs_mask_workspace_size(int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t T);
+int estimate_block_mask(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const int32_t* page_table,
+                        int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t T,
+                        const uint8_t* head_kind /* host */, int32_t keep_num, int32_t keep_den,
+                        uint8_t* block_mask, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

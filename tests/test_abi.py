@@ -153,3 +153,45 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError, match="GPU tensor"):
         ubs.sparse_decode(q, kc, kc, torch.zeros((4, 2), dtype=torch.int32), torch.zeros(4, dtype=torch.int32),
                           [0] * 4 + [1] * 4, None, None, 128, 512, 0.1)
+
+
+def _mask(**kw):
+    lib = ubs.load()
+    a = dict(q=A, k=A, pt=A, L=1024, Hq=32, Hkv=8, D=128, P=64, T=128, kind=KIND, num=3, den=10, mask=A,
+             ws=A, wsb=None, stream=NULL)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.ubs_mask_workspace_size(a["L"], a["Hq"], a["Hkv"], a["D"], a["T"])
+    return lib.estimate_block_mask(a["q"], a["k"], a["pt"], a["L"], a["Hq"], a["Hkv"], a["D"], a["P"], a["T"],
+                                   a["kind"], a["num"], a["den"], a["mask"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(D=96), -2, "D=96"),
+    (dict(T=32), -2, "T=32"),
+    (dict(P=48), -2, "P=48"),
+    (dict(Hq=12), -1, "multiple"),
+    (dict(num=0), -1, "keep_num"),
+    (dict(num=11), -1, "keep_num"),
+    (dict(kind=None), -1, "head_kind"),
+    (dict(mask=None), -1, "non-NULL"),
+    (dict(q=A + 2), -1, "aligned"),
+    (dict(wsb=64), -3, "workspace"),
+    (dict(L=4096 * 128 + 1), -2, "tiles"),
+])
+def test_mask_validation(kw, code, frag):
+    assert _mask(**kw) == code
+    assert frag in _err()
+
+
+def test_mask_nothing_to_do():
+    # L = 0, and every KV head streaming: success without touching any pointer
+    assert _mask(L=0, q=None, k=None, pt=None, mask=None, ws=None, wsb=0) == 0
+    streaming = (ctypes.c_uint8 * 8)(1, 1, 1, 1, 1, 1, 1, 1)
+    assert _mask(kind=streaming, q=None, k=None, pt=None, mask=None, ws=None, wsb=0) == 0
+
+
+def test_mask_workspace_size():
+    lib = ubs.load()
+    assert lib.ubs_mask_workspace_size(65536, 32, 8, 128, 128) >= (32 + 8) * 512 * 128 * 4
+    assert lib.ubs_mask_workspace_size(65536, 32, 8, 128, 128) % 256 == 0

@@ -8,9 +8,14 @@ libubs.so, reached through its C ABI (include/ubs.h):
     select_pages       query-aware top-k page selection under a token budget
     sparse_decode      sparse paged GQA decode with split-KV and LSE combine
 
+and the step before a sparse prefill for dense heads:
+
+    estimate_block_mask  dense heads' block mask from mean-pooled tile scores
+
 Build the library with ``python -m unified_block_sparse_amd.build``.
 """
 from ._lib import (UBSError, load, sparse_prefill, build_page_bounds, select_pages,  # noqa: F401
-                   sparse_decode, LIB_PATH, EXPORTED)
+                   sparse_decode, estimate_block_mask, LIB_PATH, EXPORTED)
 
-__all__ = ["UBSError", "load", "sparse_prefill", "build_page_bounds", "select_pages", "sparse_decode"]
+__all__ = ["UBSError", "load", "sparse_prefill", "build_page_bounds", "select_pages", "sparse_decode",
+           "estimate_block_mask"]

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libubs.so")
 UBS_OK = 0
 ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
 EXPORTED = ("sparse_prefill", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
-            "sparse_decode", "ubs_decode_workspace_size", "ubs_last_error", "ubs_version")
+            "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
+            "ubs_last_error", "ubs_version")
 
 
 class UBSError(RuntimeError):
@@ -64,6 +65,10 @@ def load() -> ctypes.CDLL:
         lib.sparse_decode.restype = ctypes.c_int
         lib.sparse_decode.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _i,
                                       _f, _p, _p, _p, _sz, _p]
+        lib.ubs_mask_workspace_size.restype = _sz
+        lib.ubs_mask_workspace_size.argtypes = [_i, _i, _i, _i, _i]
+        lib.estimate_block_mask.restype = ctypes.c_int
+        lib.estimate_block_mask.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _i, _i, _p, _p, _sz, _p]
         _lib = lib
         return lib
 
@@ -264,3 +269,39 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            workspace.numel() * workspace.element_size(), st)
     _check("sparse_decode", rc)
     return (out, lse) if return_lse else out
+
+
+def estimate_block_mask(q: torch.Tensor, k_cache: torch.Tensor, page_table: torch.Tensor,
+                        head_kind: Sequence[int], T: int, keep: Tuple[int, int] = (3, 10),
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense heads' prefill block mask from mean-pooled tile scores (see include/ubs.h).
+
+    q bf16 [L, Hq, D]; k_cache bf16 [NP, Hkv, P, D]; page_table int32 [>= ceil(L/P)];
+    keep = (keep_num, keep_den): ceil(keep_num*(i+1)/keep_den) tiles kept in query-tile row
+    i, the diagonal included. Returns block_mask uint8 [Hq, nT, nT]; rows of streaming heads
+    are left as they were in `out` (zeros when out is None).
+    """
+    lib = load()
+    L, Hq, D = q.shape
+    NP, Hkv, P, D2 = k_cache.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    if D2 != D:
+        raise ValueError("q and k_cache head dims differ")
+    if len(head_kind) != Hkv:
+        raise ValueError("head_kind must have one entry per KV head")
+    if page_table.numel() < (L + P - 1) // P:
+        raise ValueError("page_table is shorter than ceil(L / P)")
+    nT = (L + T - 1) // T
+    if out is None:
+        out = torch.zeros((Hq, nT, nT), dtype=torch.uint8, device=dev)
+    _need(out, "out", torch.uint8, shape=(Hq, nT, nT), device=dev)
+    stream = _stream(dev)
+    nbytes = lib.ubs_mask_workspace_size(L, Hq, Hkv, D, T)
+    ws = _workspace("mask", dev, stream, nbytes)
+    rc = lib.estimate_block_mask(_ptr(q), _ptr(k_cache), _ptr(page_table), L, Hq, Hkv, D, P, T, _kinds(head_kind),
+                                 int(keep[0]), int(keep[1]), _ptr(out), _ptr(ws), ws.numel(), stream)
+    _check("estimate_block_mask", rc)
+    return out

@@ -294,4 +294,60 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
   return hip_status(ubs::launch_decode(a, stream), "sparse_decode launch");
 }
 
+size_t ubs_mask_workspace_size(int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t T) {
+  if (L <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || T <= 0) return 256;
+  // fp32 tile means of every query head and every KV head (an upper bound of the dense ones)
+  const size_t nT = ((size_t)L + T - 1) / T;
+  return (((size_t)Hq + Hkv) * nT * D * sizeof(float) + 255) / 256 * 256;
+}
+
+int estimate_block_mask(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const int32_t* page_table, int32_t L,
+                        int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t T, const uint8_t* head_kind,
+                        int32_t keep_num, int32_t keep_den, uint8_t* block_mask, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int rc = common_heads(Hq, Hkv, D);
+  if (rc) return rc;
+  REQUIRE(L >= 0, UBS_ERR_INVALID_ARGUMENT, "L=%d is negative", L);
+  REQUIRE(T == 64 || T == 128, UBS_ERR_UNSUPPORTED, "T=%d (supported: 64, 128)", T);
+  REQUIRE(P > 0, UBS_ERR_INVALID_ARGUMENT, "P=%d must be positive", P);
+  REQUIRE(pow2(P) && P >= 16 && P <= 4096, UBS_ERR_UNSUPPORTED, "P=%d (supported: powers of two 16..4096)", P);
+  REQUIRE(Hq <= ubs::kMaxQHeads, UBS_ERR_UNSUPPORTED, "Hq=%d above %d", Hq, ubs::kMaxQHeads);
+  REQUIRE(keep_num > 0 && keep_num <= keep_den && keep_den <= 1024, UBS_ERR_INVALID_ARGUMENT,
+          "keep_num=%d, keep_den=%d must satisfy 0 < keep_num <= keep_den <= 1024", keep_num, keep_den);
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+  if (rc) return rc;
+  if (L == 0 || dense.n == 0) return ok();
+  REQUIRE(q && k_cache && page_table && block_mask, UBS_ERR_INVALID_ARGUMENT,
+          "q, k_cache, page_table and block_mask must be non-NULL");
+  REQUIRE(aligned16(q) && aligned16(k_cache), UBS_ERR_INVALID_ARGUMENT, "q and k_cache must be 16-byte aligned");
+  const int64_t nT = (L + T - 1) / T;
+  REQUIRE(nT <= ubs::kMaxTileList, UBS_ERR_UNSUPPORTED, "L=%d spans %lld tiles of %d (at most %d)", L,
+          (long long)nT, T, ubs::kMaxTileList);
+  const size_t need = ubs_mask_workspace_size(L, Hq, Hkv, D, T);
+  REQUIRE(workspace && workspace_bytes >= need && aligned16(workspace), UBS_ERR_WORKSPACE_TOO_SMALL,
+          "workspace of %zu bytes (16-byte aligned), need %zu", workspace_bytes, need);
+  ubs::MaskArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.page_table = page_table;
+  a.L = L;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.P = P;
+  a.T = T;
+  a.log2_P = __builtin_ctz((unsigned)P);
+  a.nT = (int)nT;
+  a.G = Hq / Hkv;
+  a.keep_num = keep_num;
+  a.keep_den = keep_den;
+  a.dense_kv = dense;
+  a.block_mask = block_mask;
+  a.qmean = static_cast<float*>(workspace);
+  a.kmean = a.qmean + (size_t)dense.n * a.G * nT * D;
+  return hip_status(ubs::launch_mask(a, stream), "estimate_block_mask launch");
+}
+
 }  // extern "C"

@@ -68,6 +68,18 @@ struct PrefillArgs {
   float* lse;
 };
 
+struct MaskArgs {
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const int32_t* page_table;
+  int L, Hq, Hkv, D, P, T, log2_P, nT, G;
+  int keep_num, keep_den;
+  HeadList dense_kv;     // dense KV heads; their query heads are the dense query heads
+  uint8_t* block_mask;
+  float* qmean;          // workspace [n_dense_kv * G][nT][D]
+  float* kmean;          // workspace [n_dense_kv][nT][D]
+};
+
 // Decode split planning (shared by the workspace query and the launch).
 struct DecodePlan {
   int chunks_dense, chunks_stream;  // upper bounds of key chunks per (b, KV head)
@@ -80,5 +92,6 @@ hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
 
 }  // namespace ubs
