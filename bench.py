@@ -191,6 +191,35 @@ def cpu_baseline(c, d, kept_tiles: int, rows_per_head: int, ideal_s: float):
     }
 
 
+# ----------------------------------------------------------------------------- mask estimation
+
+def mask_estimation(c, steps: int, warmup: int):
+    """estimate_block_mask on prefill_llama8b (the dense heads' mask the prefill above uses,
+    computed on the GPU), timed alone and outside `value`. Algorithmic bytes: the dense
+    query heads' Q and the dense KV heads' K read once, the mask rows written."""
+    import torch
+    import unified_block_sparse_amd as ubs
+    dev = c.q.device
+    out = torch.empty((c.Hq, c.nT, c.nT), dtype=torch.uint8, device=dev)
+    f = lambda: ubs.estimate_block_mask(c.q, c.k_cache, c.page_table, c.head_kind, c.T, keep=(3, 10), out=out)
+    for _ in range(warmup):
+        f()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    n_dkv = sum(1 for g in range(c.Hkv) if not c.head_kind[g])
+    nq = n_dkv * c.G
+    nbytes = c.L * (nq + n_dkv) * c.D * 2 + nq * c.nT * c.nT
+    return {"workload": "prefill_llama8b dense heads (16 query heads, 512 query tiles)", "ms": round(t * 1e3, 4),
+            "bytes": nbytes, "gbps": round(nbytes / t / 1e9, 1), "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
 # ----------------------------------------------------------------------------- ragged decode
 
 def ragged_decode_step(steps: int, warmup: int):
@@ -390,6 +419,7 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
     }
+    breakdown["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
     if not args.no_ragged:
         breakdown["decode_ragged_step"] = ragged_decode_step(args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -36,17 +36,24 @@ __global__ __launch_bounds__(256) void tile_mean_kernel(const MaskArgs a) {
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int r = r0 + rr; r < r1; r += RPP) {
+  // all of a thread's rows (at most 128 / RPP) loaded before any is summed
+  constexpr int MAXR = 128 / RPP;
+  u32x4 v[MAXR];
+#pragma unroll
+  for (int x = 0; x < MAXR; ++x) {
+    const int r = r0 + rr + x * RPP;
     const uint16_t* src =
         isq ? a.q + ((int64_t)r * a.Hq + h) * D + cc * 8
             : a.k_cache + (((int64_t)a.page_table[r >> a.log2_P] * a.Hkv + g) * a.P + (r & (a.P - 1))) * D + cc * 8;
-    const u32x4 v = ld16(src);
+    v[x] = (r < r1) ? ld16(src) : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int x = 0; x < MAXR; ++x)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += bf16_lo(v[e]);
-      acc[2 * e + 1] += bf16_hi(v[e]);
+      acc[2 * e] += bf16_lo(v[x][e]);
+      acc[2 * e + 1] += bf16_hi(v[x][e]);
     }
-  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) part[rr][cc * 8 + e] = acc[e];
   __syncthreads();
