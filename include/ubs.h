@@ -97,6 +97,31 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
                    float sm_scale, float* out, float* lse, hipStream_t stream);
 
 /*
+ * sparse_prefill_chunk -- sparse_prefill for the query rows [q_start, L) of a sequence
+ * whose first q_start tokens already sit in the cache (chunked prefill: the LServe
+ * paper's serving setting, a long prompt prefilled in pieces over one paged cache).
+ *
+ * Rows r in [q_start, L) attend exactly as in sparse_prefill over the whole
+ * sequence of L tokens (keys c <= r of the kept tiles of (h, r / T)); the rows
+ * before q_start are neither read nor written. q_start must be a multiple of T, so
+ * the chunk is whole query tiles i in [q_start / T, nT), nT = ceil(L / T).
+ *
+ *   q           bf16 [L - q_start][Hq][D]          (row r at r - q_start)
+ *   k_cache,    bf16 [NP][Hkv][P][D], holding all L tokens
+ *   v_cache
+ *   page_table  int32 [ceil(L / P)]
+ *   block_mask  uint8 [Hq][nT - q_start/T][nT]     (row i at i - q_start/T)
+ *   out         fp32 [L - q_start][Hq][D]          (fully written)
+ *   lse         fp32 [Hq][L - q_start] or NULL
+ * sparse_prefill is this call with q_start = 0. Supported: as sparse_prefill.
+ */
+int sparse_prefill_chunk(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                         const int32_t* page_table, int32_t L, int32_t q_start, int32_t Hq, int32_t Hkv,
+                         int32_t D, int32_t P, int32_t T, const uint8_t* head_kind /* host */,
+                         const uint8_t* block_mask, int32_t sink_tiles, int32_t local_tiles,
+                         float sm_scale, float* out, float* lse, hipStream_t stream);
+
+/*
  * build_page_bounds -- the per-page key summary used to score pages.
  *
  * Defined by the blog's "LServe -- Decode Phase" section ("a summary vector

@@ -195,3 +195,28 @@ def test_mask_workspace_size():
     lib = ubs.load()
     assert lib.ubs_mask_workspace_size(65536, 32, 8, 128, 128) >= (32 + 8) * 512 * 128 * 4
     assert lib.ubs_mask_workspace_size(65536, 32, 8, 128, 128) % 256 == 0
+
+
+def _chunk(**kw):
+    a = dict(q=A, k=A, v=A, pt=A, L=1024, q0=256, Hq=8, Hkv=8, D=128, P=64, T=128, kind=KIND, mask=A,
+             sink=1, local=4, scale=0.1, out=A, lse=NULL, stream=NULL)
+    a.update(kw)
+    return ubs.load().sparse_prefill_chunk(a["q"], a["k"], a["v"], a["pt"], a["L"], a["q0"], a["Hq"], a["Hkv"],
+                                           a["D"], a["P"], a["T"], a["kind"], a["mask"], a["sink"], a["local"],
+                                           a["scale"], a["out"], a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(q0=100), -1, "q_start=100"),
+    (dict(q0=1152), -1, "q_start=1152"),
+    (dict(q0=-128), -1, "q_start=-128"),
+    (dict(T=32), -2, "T=32"),
+    (dict(mask=None), -1, "block_mask"),
+])
+def test_prefill_chunk_validation(kw, code, frag):
+    assert _chunk(**kw) == code
+    assert frag in _err()
+
+
+def test_prefill_chunk_empty_chunk_ok():
+    assert _chunk(q0=1024, q=None, k=None, v=None, pt=None, mask=None, out=None) == 0

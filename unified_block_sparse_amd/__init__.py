@@ -4,6 +4,7 @@ The four operations of the hot path run as hand-written HIP kernels in
 libubs.so, reached through its C ABI (include/ubs.h):
 
     sparse_prefill     block-sparse + streaming (Lambda) causal prefill attention
+                       (sparse_prefill_chunk: a chunk of query tiles over a longer cache)
     build_page_bounds  per-page, per-channel key min/max
     select_pages       query-aware top-k page selection under a token budget
     sparse_decode      sparse paged GQA decode with split-KV and LSE combine
@@ -14,8 +15,8 @@ and the step before a sparse prefill for dense heads:
 
 Build the library with ``python -m unified_block_sparse_amd.build``.
 """
-from ._lib import (UBSError, load, sparse_prefill, build_page_bounds, select_pages,  # noqa: F401
-                   sparse_decode, estimate_block_mask, LIB_PATH, EXPORTED)
+from ._lib import (UBSError, load, sparse_prefill, sparse_prefill_chunk, build_page_bounds,  # noqa: F401
+                   select_pages, sparse_decode, estimate_block_mask, LIB_PATH, EXPORTED)
 
-__all__ = ["UBSError", "load", "sparse_prefill", "build_page_bounds", "select_pages", "sparse_decode",
-           "estimate_block_mask"]
+__all__ = ["UBSError", "load", "sparse_prefill", "sparse_prefill_chunk", "build_page_bounds", "select_pages",
+           "sparse_decode", "estimate_block_mask"]

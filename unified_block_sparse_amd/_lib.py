@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libubs.so")
 
 UBS_OK = 0
 ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
-EXPORTED = ("sparse_prefill", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
+EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
             "ubs_last_error", "ubs_version")
 
@@ -54,6 +54,9 @@ def load() -> ctypes.CDLL:
         lib.ubs_version.argtypes = []
         lib.sparse_prefill.restype = ctypes.c_int
         lib.sparse_prefill.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _i, _i, _f, _p, _p, _p]
+        lib.sparse_prefill_chunk.restype = ctypes.c_int
+        lib.sparse_prefill_chunk.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _i, _f, _p, _p,
+                                             _p]
         lib.build_page_bounds.restype = ctypes.c_int
         lib.build_page_bounds.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p]
         lib.ubs_select_workspace_size.restype = _sz
@@ -305,3 +308,46 @@ def estimate_block_mask(q: torch.Tensor, k_cache: torch.Tensor, page_table: torc
                                  int(keep[0]), int(keep[1]), _ptr(out), _ptr(ws), ws.numel(), stream)
     _check("estimate_block_mask", rc)
     return out
+
+
+def sparse_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         page_table: torch.Tensor, L: int, q_start: int, head_kind: Sequence[int],
+                         block_mask: Optional[torch.Tensor], sink_tiles: int, local_tiles: int, T: int,
+                         sm_scale: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         return_lse: bool = False):
+    """Chunked prefill: query rows [q_start, L) over a cache holding all L tokens (see include/ubs.h).
+
+    q bf16 [L - q_start, Hq, D]; block_mask uint8 [Hq, nT - q_start/T, nT] (None when every KV
+    head streams). Returns out fp32 [L - q_start, Hq, D] (and lse fp32 [Hq, L - q_start]).
+    """
+    lib = load()
+    Lq, Hq, D = q.shape
+    NP, Hkv, P, D2 = k_cache.shape
+    dev = q.device
+    if Lq != L - q_start:
+        raise ValueError("q must hold rows q_start .. L-1")
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(v_cache, "v_cache", torch.bfloat16, shape=k_cache.shape, device=dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    if D2 != D:
+        raise ValueError("q and k_cache head dims differ")
+    if len(head_kind) != Hkv:
+        raise ValueError("head_kind must have one entry per KV head")
+    nT = (L + T - 1) // T
+    if page_table.numel() < (L + P - 1) // P:
+        raise ValueError("page_table is shorter than ceil(L / P)")
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, shape=(Hq, nT - q_start // T, nT), device=dev)
+    if out is None:
+        out = torch.empty((Lq, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, shape=(Lq, Hq, D), device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Lq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(Hq, Lq), device=dev)
+    rc = lib.sparse_prefill_chunk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), L, q_start, Hq, Hkv, D,
+                                  P, T, _kinds(head_kind), _ptr(block_mask), sink_tiles, local_tiles,
+                                  float(sm_scale), _ptr(out), _ptr(lse), _stream(dev))
+    _check("sparse_prefill_chunk", rc)
+    return (out, lse) if return_lse else out

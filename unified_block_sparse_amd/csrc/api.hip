@@ -87,14 +87,17 @@ const char* ubs_last_error(void) { return g_last_error.c_str(); }
 
 int ubs_version(void) { return 100; }
 
-int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
-                   const int32_t* page_table, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
-                   int32_t T, const uint8_t* head_kind, const uint8_t* block_mask, int32_t sink_tiles,
-                   int32_t local_tiles, float sm_scale, float* out, float* lse, hipStream_t stream) {
+int sparse_prefill_chunk(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                         const int32_t* page_table, int32_t L, int32_t q_start, int32_t Hq, int32_t Hkv,
+                         int32_t D, int32_t P, int32_t T, const uint8_t* head_kind, const uint8_t* block_mask,
+                         int32_t sink_tiles, int32_t local_tiles, float sm_scale, float* out, float* lse,
+                         hipStream_t stream) {
   int rc = common_heads(Hq, Hkv, D);
   if (rc) return rc;
   REQUIRE(L >= 0, UBS_ERR_INVALID_ARGUMENT, "L=%d is negative", L);
   REQUIRE(T == 64 || T == 128, UBS_ERR_UNSUPPORTED, "T=%d (supported: 64, 128)", T);
+  REQUIRE(q_start >= 0 && q_start <= L && q_start % T == 0, UBS_ERR_INVALID_ARGUMENT,
+          "q_start=%d must be a multiple of T=%d in [0, L=%d]", q_start, T, L);
   REQUIRE(P > 0, UBS_ERR_INVALID_ARGUMENT, "P=%d must be positive", P);
   REQUIRE(pow2(P) && P >= 16 && P <= 4096, UBS_ERR_UNSUPPORTED, "P=%d (supported: powers of two 16..4096)", P);
   REQUIRE(Hq <= ubs::kMaxQHeads, UBS_ERR_UNSUPPORTED, "Hq=%d above %d", Hq, ubs::kMaxQHeads);
@@ -105,7 +108,7 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   uint64_t smask;
   rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
   if (rc) return rc;
-  if (L == 0) return ok();
+  if (L == q_start) return ok();
   REQUIRE(q && k_cache && v_cache && page_table && out, UBS_ERR_INVALID_ARGUMENT,
           "q, k_cache, v_cache, page_table and out must be non-NULL");
   REQUIRE(dense.n == 0 || block_mask, UBS_ERR_INVALID_ARGUMENT, "block_mask is NULL but a KV head is dense");
@@ -114,8 +117,8 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   const int64_t nT = (L + T - 1) / T;
   REQUIRE(nT <= ubs::kMaxTileList, UBS_ERR_UNSUPPORTED, "L=%d spans %lld tiles of %d (at most %d)", L,
           (long long)nT, T, ubs::kMaxTileList);
-  REQUIRE(nT * Hq < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large",
-          (long long)(nT * Hq));
+  REQUIRE((nT - q_start / T) * Hq < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large",
+          (long long)((nT - q_start / T) * Hq));
   ubs::PrefillArgs a{};
   a.q = q;
   a.k_cache = k_cache;
@@ -128,6 +131,7 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   a.D = D;
   a.P = P;
   a.T = T;
+  a.q_tile0 = q_start / T;
   a.log2_P = __builtin_ctz((unsigned)P);
   a.sink_tiles = sink_tiles;
   a.local_tiles = local_tiles;
@@ -137,6 +141,14 @@ int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf1
   a.dense_kv_mask = ~smask & (Hkv == 64 ? ~0ull : ((1ull << Hkv) - 1));
   a.n_dense_kv = dense.n;
   return hip_status(ubs::launch_prefill(a, stream), "sparse_prefill launch");
+}
+
+int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                   const int32_t* page_table, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                   int32_t T, const uint8_t* head_kind, const uint8_t* block_mask, int32_t sink_tiles,
+                   int32_t local_tiles, float sm_scale, float* out, float* lse, hipStream_t stream) {
+  return sparse_prefill_chunk(q, k_cache, v_cache, page_table, L, 0, Hq, Hkv, D, P, T, head_kind, block_mask,
+                              sink_tiles, local_tiles, sm_scale, out, lse, stream);
 }
 
 int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, const int32_t* seq_lens,

@@ -60,6 +60,7 @@ struct PrefillArgs {
   const int32_t* page_table;
   const uint8_t* block_mask;
   int L, Hq, Hkv, D, P, T, sink_tiles, local_tiles;
+  int q_tile0;             // first query tile of the call (a chunk: tiles q_tile0 .. nT-1)
   int log2_P;
   float sm_scale;
   uint64_t dense_kv_mask;  // bit g set: KV head g is dense

@@ -122,6 +122,11 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   const int L = a.L;
   const int G = a.Hq / a.Hkv;
   const int nT = (L + T - 1) / T;
+  // query tiles of this call: q_tile0 .. nT-1 (a chunk of the sequence; q, out, lse and
+  // the mask rows hold those tiles only)
+  const int qt0 = a.q_tile0;
+  const int nQ = nT - qt0;
+  const int q0 = qt0 * T;
 
   // ---- work item: XCD-aware renumbering of the block index (blocks go to XCDs
   // round-robin), then dense heads first, query tiles from the last to the first,
@@ -149,13 +154,13 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   const int nd = a.n_dense_kv * G;
   bool streaming;
   int h, i;
-  if (w < nd * nT) {
+  if (w < nd * nQ) {
     streaming = false;
     i = nT - 1 - w / nd;
     const int x = w % nd;
     h = nth_bit(dmask, x / G) * G + x % G;
   } else {
-    const int w2 = w - nd * nT;
+    const int w2 = w - nd * nQ;
     const int ns = a.Hq - nd;
     streaming = true;
     i = nT - 1 - w2 / ns;
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   // ---- kept KV tiles, ascending, as a list in LDS
   int n_tiles;
   if (!streaming) {
-    const uint8_t* mrow = a.block_mask + ((int64_t)h * nT + i) * nT;
+    const uint8_t* mrow = a.block_mask + ((int64_t)h * nQ + (i - qt0)) * nT;
     uint8_t flag[MB];
     int cnt = 0;
 #pragma unroll
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   const int qrow = i * T + qi;
   bf16x8 qb[QK];
   {
-    const uint16_t* qp = a.q + ((int64_t)qrow * a.Hq + h) * D + q2 * (D / 2);
+    const uint16_t* qp = a.q + ((int64_t)(qrow - q0) * a.Hq + h) * D + q2 * (D / 2);
 #pragma unroll
     for (int kk = 0; kk < QK; ++kk) qb[kk] = as_bf16x8(qrow < L ? ld16(qp + kk * 8) : u32x4{0, 0, 0, 0});
   }
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   const float l_row = l_run + shfl_xor(l_run, 32);
   const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
   if (qrow < L) {
-    float* op = a.out + ((int64_t)qrow * a.Hq + h) * D + 4 * q2;
+    float* op = a.out + ((int64_t)(qrow - q0) * a.Hq + h) * D + 4 * q2;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -556,13 +561,13 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
         *reinterpret_cast<f32x4*>(op + cb * 32 + 8 * jj) = v;
       }
     if (q2 == 0 && a.lse)
-      a.lse[(int64_t)h * L + qrow] = l_row > 0.f ? (m_run * c2 + __log2f(l_row)) * kLn2 : kNegInf;
+      a.lse[(int64_t)h * (L - q0) + (qrow - q0)] = l_row > 0.f ? (m_run * c2 + __log2f(l_row)) * kLn2 : kNegInf;
   }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const int nT = (a.L + a.T - 1) / a.T;
-  const int64_t blocks = (int64_t)nT * a.Hq;
+  const int64_t blocks = (int64_t)(nT - a.q_tile0) * a.Hq;
   if (blocks == 0) return hipSuccess;
 #define UBS_PREFILL(TT, DD)                                                                    \
   if (a.T == TT && a.D == DD) {                                                                \
