@@ -16,6 +16,8 @@
  *                      or the sink and local tokens (streaming heads).
  *   estimate_block_mask  the dense heads' prefill block mask from mean-pooled
  *                      query/key tile scores.
+ *   append_kv          new tokens into the paged cache, with the page summaries
+ *                      they change.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -216,6 +218,32 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
                   const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
                   int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * append_kv -- write newly decoded or prefilled tokens into the paged KV cache and
+ * refresh the page summaries they change (the steps beside decode in the serving
+ * loop of the LServe paper; page layout of the blog's "LServe -- Decode Phase").
+ *
+ * For every sequence b and x < n_new, token t = seq_lens[b] + x gets
+ *     k_cache[page_table[b][t / P]][g][t % P][:] = k_new[b][x][g][:]   (every KV head g)
+ * and likewise v_cache. When bounds is not NULL, every DENSE KV head's sub-page (Lp
+ * tokens) that received a new token is recomputed over all its valid tokens of the
+ * sequence of length seq_lens[b] + n_new, exactly as build_page_bounds would;
+ * other sub-pages are left untouched. seq_lens is the length BEFORE the append and
+ * is not modified; the caller advances it.
+ *
+ *   k_new, v_new  bf16 [B][n_new][Hkv][D]
+ *   page_table    int32 [B][max_pages], pages for all seq_lens[b] + n_new tokens
+ *   seq_lens      int32 [B], seq_lens[b] + n_new <= max_pages * P
+ *   k_cache,      bf16 [NP][Hkv][P][D]
+ *   v_cache
+ *   bounds        bf16 [NP][Hkv][P/Lp][2][D] or NULL
+ * Supported: D in {64, 128}; P in {16, 32, 64, 128}; Lp divides P.
+ */
+int append_kv(const ubs_bf16_t* k_new, const ubs_bf16_t* v_new, const int32_t* page_table,
+              const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t n_new, int32_t Hkv, int32_t D,
+              int32_t P, int32_t Lp, const uint8_t* head_kind /* host */, ubs_bf16_t* k_cache,
+              ubs_bf16_t* v_cache, ubs_bf16_t* bounds, hipStream_t stream);
 
 /*
  * estimate_block_mask -- the dense heads' prefill block mask from mean-pooled

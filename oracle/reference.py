@@ -209,6 +209,25 @@ def meanpool_mask_ref(q_bits, k_cache_bits, page_table, L: int, Hq: int, Hkv: in
     return mask, score, mag
 
 
+# ----------------------------------------------------------------------------- KV append
+
+def append_ref(k_cache_bits, v_cache_bits, page_table, seq_lens, k_new_bits, v_new_bits, P: int):
+    """The paged cache after appending n_new tokens to every sequence (the layout of the
+    blog's decode section, as in tokens_of_sequence): token t = seq_lens[b] + x of sequence
+    b goes to row t % P of physical page page_table[b][t // P], for every KV head.
+    k_new/v_new are [B, n_new, Hkv, D] bits. Returns new (k_cache, v_cache) arrays."""
+    k = np.array(k_cache_bits, copy=True)
+    v = np.array(v_cache_bits, copy=True)
+    kn, vn = np.asarray(k_new_bits), np.asarray(v_new_bits)
+    pt = np.asarray(page_table)
+    for b, L in enumerate(seq_lens):
+        for x in range(kn.shape[1]):
+            t = int(L) + x
+            k[pt[b, t // P], :, t % P, :] = kn[b, x]
+            v[pt[b, t // P], :, t % P, :] = vn[b, x]
+    return k, v
+
+
 # ----------------------------------------------------------------------------- page bounds
 
 def bounds_ref(k_cache_bits, page_table, seq_lens, P: int, Lp: int, head_kind,

@@ -220,3 +220,29 @@ def test_prefill_chunk_validation(kw, code, frag):
 
 def test_prefill_chunk_empty_chunk_ok():
     assert _chunk(q0=1024, q=None, k=None, v=None, pt=None, mask=None, out=None) == 0
+
+
+def _append(**kw):
+    a = dict(kn=A, vn=A, pt=A, sl=A, B=4, maxp=64, n=1, Hkv=8, D=128, P=64, Lp=16, kind=KIND, k=A, v=A, bnd=A,
+             stream=NULL)
+    a.update(kw)
+    return ubs.load().append_kv(a["kn"], a["vn"], a["pt"], a["sl"], a["B"], a["maxp"], a["n"], a["Hkv"], a["D"],
+                                a["P"], a["Lp"], a["kind"], a["k"], a["v"], a["bnd"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(D=96), -2, "D=96"),
+    (dict(P=48), -2, "P=48"),
+    (dict(Lp=24), -2, "Lp=24"),
+    (dict(n=-1), -1, "n_new=-1"),
+    (dict(kind=None), -1, "head_kind"),
+    (dict(k=None), -1, "non-NULL"),
+    (dict(bnd=A + 2), -1, "aligned"),
+])
+def test_append_validation(kw, code, frag):
+    assert _append(**kw) == code
+    assert frag in _err()
+
+
+def test_append_nothing_to_do():
+    assert _append(n=0, kn=None, vn=None, pt=None, sl=None, k=None, v=None, bnd=None) == 0

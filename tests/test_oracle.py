@@ -473,3 +473,38 @@ def test_meanpool_mask_ties_go_to_lower_tiles_and_counts():
         assert not np.triu(mask[h], 1).any()
         for i in range(nT):
             assert int(mask[h, i].sum()) == oracle.keep_count(i, 3, 10)
+
+
+# ----------------------------------------------------------------------------- KV append pin
+
+def test_append_then_gather_round_trip():
+    """Appending then gathering a sequence token by token returns the old tokens followed by
+    the new ones; rows of other sequences and unused rows are untouched."""
+    rng = np.random.default_rng(3)
+    P, Hkv, D, B, n_new = 16, 2, 8, 3, 21
+    lens = [5, 16, 40]
+    n_pages = [(L + n_new + P - 1) // P for L in lens]
+    NP = sum(n_pages) + 2
+    perm = rng.permutation(NP)
+    pt = np.zeros((B, max(n_pages)), dtype=np.int32)
+    off = 0
+    for b, n in enumerate(n_pages):
+        pt[b, :n] = perm[off:off + n]
+        off += n
+    k = rng.integers(0, 1 << 16, size=(NP, Hkv, P, D), dtype=np.uint16)
+    v = rng.integers(0, 1 << 16, size=(NP, Hkv, P, D), dtype=np.uint16)
+    kn = rng.integers(0, 1 << 16, size=(B, n_new, Hkv, D), dtype=np.uint16)
+    vn = rng.integers(0, 1 << 16, size=(B, n_new, Hkv, D), dtype=np.uint16)
+    k2, v2 = oracle.append_ref(k, v, pt, lens, kn, vn, P)
+    touched = np.zeros((NP, P), dtype=bool)
+    for b, L in enumerate(lens):
+        old = oracle.tokens_of_sequence(k, pt[b], L, P)
+        new = oracle.tokens_of_sequence(k2, pt[b], L + n_new, P)
+        assert np.array_equal(new[:L], old)
+        assert np.array_equal(new[L:], kn[b])
+        assert np.array_equal(oracle.tokens_of_sequence(v2, pt[b], L + n_new, P)[L:], vn[b])
+        for t in range(L, L + n_new):
+            touched[pt[b, t // P], t % P] = True
+    kt, k2t = k.transpose(0, 2, 1, 3), k2.transpose(0, 2, 1, 3)       # [NP, P, Hkv, D]
+    vt, v2t = v.transpose(0, 2, 1, 3), v2.transpose(0, 2, 1, 3)
+    assert np.array_equal(k2t[~touched], kt[~touched]) and np.array_equal(v2t[~touched], vt[~touched])

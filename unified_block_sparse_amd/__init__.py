@@ -9,14 +9,15 @@ libubs.so, reached through its C ABI (include/ubs.h):
     select_pages       query-aware top-k page selection under a token budget
     sparse_decode      sparse paged GQA decode with split-KV and LSE combine
 
-and the step before a sparse prefill for dense heads:
+and the steps around them in serving:
 
     estimate_block_mask  dense heads' block mask from mean-pooled tile scores
+    append_kv            new tokens into the paged cache, page bounds refreshed
 
 Build the library with ``python -m unified_block_sparse_amd.build``.
 """
 from ._lib import (UBSError, load, sparse_prefill, sparse_prefill_chunk, build_page_bounds,  # noqa: F401
-                   select_pages, sparse_decode, estimate_block_mask, LIB_PATH, EXPORTED)
+                   select_pages, sparse_decode, estimate_block_mask, append_kv, LIB_PATH, EXPORTED)
 
 __all__ = ["UBSError", "load", "sparse_prefill", "sparse_prefill_chunk", "build_page_bounds", "select_pages",
-           "sparse_decode", "estimate_block_mask"]
+           "sparse_decode", "estimate_block_mask", "append_kv"]

@@ -21,6 +21,7 @@ UBS_OK = 0
 ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
 EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
+            "append_kv",
             "ubs_last_error", "ubs_version")
 
 
@@ -68,6 +69,8 @@ def load() -> ctypes.CDLL:
         lib.sparse_decode.restype = ctypes.c_int
         lib.sparse_decode.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _i,
                                       _f, _p, _p, _p, _sz, _p]
+        lib.append_kv.restype = ctypes.c_int
+        lib.append_kv.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]
         lib.ubs_mask_workspace_size.restype = _sz
         lib.ubs_mask_workspace_size.argtypes = [_i, _i, _i, _i, _i]
         lib.estimate_block_mask.restype = ctypes.c_int
@@ -351,3 +354,39 @@ def sparse_prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                   float(sm_scale), _ptr(out), _ptr(lse), _stream(dev))
     _check("sparse_prefill_chunk", rc)
     return (out, lse) if return_lse else out
+
+
+def append_kv(k_new: torch.Tensor, v_new: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+              head_kind: Sequence[int], k_cache: torch.Tensor, v_cache: torch.Tensor,
+              bounds: Optional[torch.Tensor] = None, Lp: Optional[int] = None) -> None:
+    """Write n_new tokens per sequence into the paged cache after position seq_lens[b], and
+    refresh the dense heads' page bounds they change (see include/ubs.h). seq_lens is the
+    length before the append; it is not modified.
+
+    k_new, v_new bf16 [B, n_new, Hkv, D]; page_table int32 [B, max_pages]; seq_lens int32 [B];
+    k_cache, v_cache bf16 [NP, Hkv, P, D]; bounds bf16 [NP, Hkv, P/Lp, 2, D] or None.
+    """
+    lib = load()
+    B, n_new, Hkv, D = k_new.shape
+    NP, Hkv2, P, D2 = k_cache.shape
+    dev = k_new.device
+    _need(k_new, "k_new", torch.bfloat16, device=dev)
+    _need(v_new, "v_new", torch.bfloat16, shape=k_new.shape, device=dev)
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(v_cache, "v_cache", torch.bfloat16, shape=k_cache.shape, device=dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    if (Hkv2, D2) != (Hkv, D):
+        raise ValueError("k_new and k_cache shapes differ")
+    if len(head_kind) != Hkv:
+        raise ValueError("head_kind must have one entry per KV head")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages]")
+    if bounds is not None:
+        if Lp is None:
+            Lp = P // bounds.shape[2]
+        _need(bounds, "bounds", torch.bfloat16, shape=(NP, Hkv, P // Lp, 2, D), device=dev)
+    rc = lib.append_kv(_ptr(k_new), _ptr(v_new), _ptr(page_table), _ptr(seq_lens), B, page_table.shape[1], n_new,
+                       Hkv, D, P, int(Lp if Lp is not None else P), _kinds(head_kind), _ptr(k_cache), _ptr(v_cache),
+                       _ptr(bounds), _stream(dev))
+    _check("append_kv", rc)

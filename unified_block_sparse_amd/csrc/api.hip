@@ -168,7 +168,7 @@ int build_page_bounds(const ubs_bf16_t* k_cache, const int32_t* page_table, cons
           "k_cache, page_table, seq_lens and bounds must be non-NULL");
   REQUIRE(aligned16(k_cache) && aligned16(bounds), UBS_ERR_INVALID_ARGUMENT,
           "k_cache and bounds must be 16-byte aligned");
-  ubs::BoundsArgs a{k_cache, page_table, seq_lens, B, max_pages, Hkv, D, P, Lp, dense, bounds};
+  ubs::BoundsArgs a{k_cache, page_table, seq_lens, B, max_pages, Hkv, D, P, Lp, dense, bounds, 0, max_pages};
   return hip_status(ubs::launch_bounds(a, stream), "build_page_bounds launch");
 }
 
@@ -360,6 +360,37 @@ int estimate_block_mask(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const in
   a.qmean = static_cast<float*>(workspace);
   a.kmean = a.qmean + (size_t)dense.n * a.G * nT * D;
   return hip_status(ubs::launch_mask(a, stream), "estimate_block_mask launch");
+}
+
+int append_kv(const ubs_bf16_t* k_new, const ubs_bf16_t* v_new, const int32_t* page_table,
+              const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t n_new, int32_t Hkv, int32_t D,
+              int32_t P, int32_t Lp, const uint8_t* head_kind, ubs_bf16_t* k_cache, ubs_bf16_t* v_cache,
+              ubs_bf16_t* bounds, hipStream_t stream) {
+  REQUIRE(B >= 0 && max_pages >= 0 && n_new >= 0, UBS_ERR_INVALID_ARGUMENT,
+          "B=%d, max_pages=%d, n_new=%d must be >= 0", B, max_pages, n_new);
+  REQUIRE(Hkv >= 1, UBS_ERR_INVALID_ARGUMENT, "Hkv=%d must be positive", Hkv);
+  REQUIRE(D == 64 || D == 128, UBS_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  int rc = paged_P(P);
+  if (rc) return rc;
+  REQUIRE(Lp > 0 && P % Lp == 0, UBS_ERR_UNSUPPORTED, "Lp=%d must divide P=%d", Lp, P);
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+  if (rc) return rc;
+  if (B == 0 || n_new == 0) return ok();
+  REQUIRE(k_new && v_new && page_table && seq_lens && k_cache && v_cache, UBS_ERR_INVALID_ARGUMENT,
+          "k_new, v_new, page_table, seq_lens, k_cache and v_cache must be non-NULL");
+  REQUIRE(aligned16(k_new) && aligned16(v_new) && aligned16(k_cache) && aligned16(v_cache) &&
+              (!bounds || aligned16(bounds)),
+          UBS_ERR_INVALID_ARGUMENT, "k_new, v_new, k_cache, v_cache and bounds must be 16-byte aligned");
+  REQUIRE((int64_t)B * n_new * Hkv * (D / 8) < (1ll << 40), UBS_ERR_UNSUPPORTED, "append too large");
+  ubs::AppendArgs a{k_new, v_new, page_table, seq_lens, B, max_pages, n_new, Hkv, D, P, k_cache, v_cache};
+  hipError_t e = ubs::launch_append(a, stream);
+  if (e != hipSuccess || !bounds || dense.n == 0) return hip_status(e, "append_kv launch");
+  const int span = (n_new + P - 1) / P + 1;
+  ubs::BoundsArgs b{k_cache, page_table, seq_lens, B, max_pages, Hkv, D, P, Lp, dense, bounds, n_new,
+                    span < max_pages ? span : max_pages};
+  return hip_status(ubs::launch_bounds(b, stream), "append_kv bounds launch");
 }
 
 }  // extern "C"

@@ -7,7 +7,9 @@
 
 namespace ubs {
 
-// One wave per (sequence b, page index j, dense KV head). Lane layout: CH = D/8
+// One wave per (sequence b, page index j, dense KV head); after an append of n_new
+// tokens, one wave per (b, page holding new tokens, dense KV head), recomputing only the
+// sub-pages that received new tokens (over all their valid tokens, old and new). Lane layout: CH = D/8
 // lanes cover one key row (8 channels = 16 bytes each), RG = 64/CH row groups
 // take rows rg, rg + RG, ... The whole page is loaded up front (rows past the
 // sequence end are inside the page, so the loads stay in bounds) and only valid
@@ -17,7 +19,8 @@ __global__ __launch_bounds__(256) void bounds_kernel(const uint16_t* __restrict_
                                                      const int32_t* __restrict__ page_table,
                                                      const int32_t* __restrict__ seq_lens,
                                                      int max_pages, int Hkv, int Lp, HeadList dense,
-                                                     int64_t n_items, uint16_t* __restrict__ bounds) {
+                                                     int n_new, int page_span, int64_t n_items,
+                                                     uint16_t* __restrict__ bounds) {
   constexpr int CH = D / 8;
   constexpr int RG = 64 / CH;
   constexpr int NR = P / RG;  // rows per lane
@@ -27,9 +30,12 @@ __global__ __launch_bounds__(256) void bounds_kernel(const uint16_t* __restrict_
   const int nd = dense.n;
   const int di = (int)(item % nd);
   const int64_t bj = item / nd;
-  const int j = (int)(bj % max_pages);
-  const int b = (int)(bj / max_pages);
-  const int L = seq_lens[b];
+  const int b = (int)(bj / page_span);
+  // an update after an append covers the pages from the one holding the first new token
+  const int from = n_new > 0 ? seq_lens[b] : 0;
+  const int j = (int)(bj % page_span) + from / P;
+  const int L = seq_lens[b] + n_new;
+  if (j >= max_pages) return;
   const int valid = min(P, L - j * P);
   if (valid <= 0) return;
   const int g = dense.h[di];
@@ -47,6 +53,7 @@ __global__ __launch_bounds__(256) void bounds_kernel(const uint16_t* __restrict_
   for (int u = 0; u < U; ++u) {
     const int lo = u * Lp;
     if (lo >= valid) break;
+    if (j * P + lo + Lp <= from) continue;   // no new token in this sub-page (updates only)
     const int hi = min(lo + Lp, valid);
     float mn[8], mx[8];
 #pragma unroll
@@ -90,11 +97,12 @@ __global__ __launch_bounds__(256) void bounds_kernel(const uint16_t* __restrict_
 
 template <int D, int P>
 static hipError_t launch_bounds_t(const BoundsArgs& a, hipStream_t s) {
-  const int64_t n_items = (int64_t)a.B * a.max_pages * a.dense.n;
+  const int64_t n_items = (int64_t)a.B * a.page_span * a.dense.n;
   if (n_items == 0) return hipSuccess;
   const int64_t blocks = (n_items + 3) / 4;
   hipLaunchKernelGGL((bounds_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s, a.k_cache,
-                     a.page_table, a.seq_lens, a.max_pages, a.Hkv, a.Lp, a.dense, n_items, a.bounds);
+                     a.page_table, a.seq_lens, a.max_pages, a.Hkv, a.Lp, a.dense, a.n_new, a.page_span,
+                     n_items, a.bounds);
   return hipGetLastError();
 }
 

@@ -20,6 +20,21 @@ struct BoundsArgs {
   int B, max_pages, Hkv, D, P, Lp;
   HeadList dense;
   uint16_t* bounds;
+  // n_new > 0: an update after appending n_new tokens to each sequence; the sequence
+  // is seq_lens[b] + n_new tokens long and only the sub-pages holding tokens at or
+  // past seq_lens[b] are recomputed (page_span pages per sequence from page
+  // seq_lens[b] / P). n_new = 0: every sub-page (page_span = max_pages).
+  int n_new, page_span;
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;   // [B][n_new][Hkv][D]
+  const uint16_t* v_new;
+  const int32_t* page_table;
+  const int32_t* seq_lens; // before the append
+  int B, max_pages, n_new, Hkv, D, P;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
 };
 
 struct SelectArgs {
@@ -94,5 +109,6 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
 }  // namespace ubs
