@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times) and exit: "
                          "the known-size kernel that scales the HBM byte counters")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time the vendor library's dense bf16 GEMM (torch.matmul, n = 8192 and "
+                         "16384) and exit: the matrix-core rate this GPU sustains in practice")
     return ap.parse_args()
 
 
@@ -77,6 +80,29 @@ def copy_calibration(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize(dev)
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def gemm_ceiling():
+    """Sustained bf16 matrix-core rate of the vendor GEMM (hipBLASLt through torch.matmul):
+    a practical ceiling to read the prefill kernel's TFLOP/s against, next to the
+    published dense peak."""
+    import torch
+    dev = torch.device("cuda:0")
+    for n, reps in ((8192, 20), (16384, 4)):
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(3):
+            a @ b
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            a @ b
+        e1.record()
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1) / reps
+        print(json.dumps({"gemm_bf16_n": n, "ms": round(ms, 4), "tflops": round(2 * n ** 3 / ms / 1e9, 1),
+                          "frac_of_peak": round(2 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}), flush=True)
 
 
 # ----------------------------------------------------------------------------- work accounting
@@ -305,6 +331,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling()
         return
     import torch
     import unified_block_sparse_amd as ubs

@@ -218,6 +218,32 @@ def test_prefill_empty_tile_row():
     assert_attention_close(out.cpu().numpy(), ref, "prefill out")
 
 
+@pytest.mark.parametrize("D,T", [(128, 128), (64, 128), (128, 64)])
+def test_prefill_growing_scores_rescale(D, T):
+    """Keys scaled up along the sequence, so every row's running max keeps growing by more
+    than the kernel's lazy-rescale margin (2^8 in weight) and the stored O is rescaled
+    several times per row."""
+    from workloads import gen
+    L, Hq, Hkv, P = 1000, 4, 2, 64
+    c = cases.make_prefill("g", L, Hq, Hkv, D, T, P, [0, 1], 1, 2, "all", 44, DEV, keep_tokens=True)
+    gain = (1.0 + torch.arange(L, device=DEV, dtype=torch.float32) / 16.0)[:, None, None]
+    k_tok = (c.k_tok.float() * gain).to(torch.bfloat16)
+    gen.scatter_pages(k_tok, c.page_table, c.k_cache, P, 44, 7)
+    # the inputs do what the test is for: the last row's max over all keys exceeds its max
+    # over the first 32 keys by more than 8 in the log2 domain
+    qf = c.q[L - 1].float().cpu().double().numpy()
+    kf = k_tok.float().cpu().double().numpy()
+    s = np.einsum("hd,thd->ht", qf[::Hq // Hkv][:Hkv], kf) * c.sm_scale / np.log(2.0)
+    assert np.all(s.max(axis=1) - s[:, :32].max(axis=1) > 8.0)
+    out, lse = ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, [0, 1], c.block_mask, 1, 2, T,
+                                  c.sm_scale, return_lse=True)
+    _sync()
+    ref, ref_lse = oracle.prefill_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.cpu().numpy(),
+                                      L, Hq, Hkv, D, P, T, [0, 1], c.block_mask.cpu().numpy(), 1, 2, c.sm_scale)
+    assert_attention_close(out.cpu().numpy(), ref, "prefill out")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, "prefill lse")
+
+
 # ----------------------------------------------------------------------------- invariances
 
 def _repermute(cache, page_table, seed):
