@@ -359,22 +359,15 @@ def decode_keys_ref(L: int, P: int, streaming: bool, selected: Sequence[int], si
     return np.concatenate(toks).astype(np.int64) if toks else np.zeros(0, dtype=np.int64)
 
 
-def decode_ref(q_bits, k_cache_bits, v_cache_bits, page_table, seq_lens, Hq: int, Hkv: int,
-               P: int, head_kind, selected: Dict[Tuple[int, int], Sequence[int]],
-               sink_tokens: int, local_tokens: int, sm_scale: float,
-               batches: Optional[Sequence[int]] = None):
-    """Sparse decode attention, fp64: out[b, h] = softmax-weighted sum of v over the key
-    set of (b, KV head h // G) from decode_keys_ref; lse = ln sum exp(scores); an empty
-    key set gives out = 0 and lse = -inf. selected maps (b, g) of dense heads to page
-    indices. Returns (out [nb, Hq, D], lse [nb, Hq]) for the batches given."""
+def _decode_over(Q: np.ndarray, rows, D: int, page_table, seq_lens, Hq: int, Hkv: int, P: int,
+                 head_kind, selected, sink_tokens: int, local_tokens: int, sm_scale: float,
+                 batches: Optional[Sequence[int]]):
+    """Decode attention with the key and value rows of a key set supplied by
+    rows(b, g, page_row, L, keys) -> (K [n, D], V [n, D]) in fp64."""
     G = Hq // Hkv
-    Kc = np.asarray(k_cache_bits)                            # bits; decoded per key set
-    Vc = np.asarray(v_cache_bits)
-    Q = bf16_to_f64(q_bits)
     pt = np.asarray(page_table)
     lens = [int(x) for x in seq_lens]
     bl = list(range(len(lens))) if batches is None else [int(b) for b in batches]
-    D = Kc.shape[-1]
     out = np.zeros((len(bl), Hq, D))
     lse = np.full((len(bl), Hq), -math.inf)
     for bi, b in enumerate(bl):
@@ -383,10 +376,118 @@ def decode_ref(q_bits, k_cache_bits, v_cache_bits, page_table, seq_lens, Hq: int
             streaming = bool(head_kind[g])
             keys = decode_keys_ref(L, P, streaming, [] if streaming else selected[(b, g)],
                                    sink_tokens, local_tokens)
-            Kt = bf16_to_f64(tokens_of_sequence(Kc, pt[b], L, P, keys)[:, g, :])
-            Vt = bf16_to_f64(tokens_of_sequence(Vc, pt[b], L, P, keys)[:, g, :])
+            Kt, Vt = rows(b, g, pt[b], L, keys)
             for h in range(g * G, (g + 1) * G):
                 o, z = _softmax_attend(sm_scale * (Kt @ Q[b, h]), Vt)
                 out[bi, h] = o
                 lse[bi, h] = z
     return out, lse
+
+
+def decode_ref(q_bits, k_cache_bits, v_cache_bits, page_table, seq_lens, Hq: int, Hkv: int,
+               P: int, head_kind, selected: Dict[Tuple[int, int], Sequence[int]],
+               sink_tokens: int, local_tokens: int, sm_scale: float,
+               batches: Optional[Sequence[int]] = None):
+    """Sparse decode attention, fp64: out[b, h] = softmax-weighted sum of v over the key
+    set of (b, KV head h // G) from decode_keys_ref; lse = ln sum exp(scores); an empty
+    key set gives out = 0 and lse = -inf. selected maps (b, g) of dense heads to page
+    indices. Returns (out [nb, Hq, D], lse [nb, Hq]) for the batches given."""
+    Kc = np.asarray(k_cache_bits)                            # bits; decoded per key set
+    Vc = np.asarray(v_cache_bits)
+
+    def rows(b, g, page_row, L, keys):
+        return (bf16_to_f64(tokens_of_sequence(Kc, page_row, L, P, keys)[:, g, :]),
+                bf16_to_f64(tokens_of_sequence(Vc, page_row, L, P, keys)[:, g, :]))
+
+    return _decode_over(bf16_to_f64(q_bits), rows, Kc.shape[-1], page_table, seq_lens, Hq, Hkv, P,
+                        head_kind, selected, sink_tokens, local_tokens, sm_scale, batches)
+
+
+# ----------------------------------------------------------------------------- INT4 KV pages
+#
+# Blog "LServe -- Decode Phase" and the Figure 2 caption: INT4 KV quantization stacks
+# with page sparsity, cutting the bytes of every page that is read. The pages give no
+# format; the reading taken here: every (token, KV head) row of D channels is quantized
+# on its own, asymmetrically, to 4-bit codes n in [0, 15] with x ~ n * scale + zero;
+# scale and zero are stored as fp16, and two codes share a byte (channel 2i in the low
+# nibble, 2i+1 in the high one). The code is an integer chosen by floating point, so it
+# is taken in fp32, as the GPU takes it:
+#   lo, hi = min_c x_c, max_c x_c;  scale16 = fp16((hi - lo) / 15);  zero16 = fp16(lo)
+#   n_c = clamp(rint((x_c - zero) / scale), 0, 15), all in fp32 with the fp16 values
+#   widened; a row with scale16 == 0 has every code 0 (and dequantizes to zero16).
+
+def quantize_int4_ref(x_bits) -> Tuple[np.ndarray, np.ndarray]:
+    """Codes [..., D] (uint8 in [0, 15]) and fp16 bit patterns [..., 2] = (scale, zero)
+    of bf16 rows x_bits [..., D], by the steps above (fp32 arithmetic, round half to even)."""
+    x = (np.ascontiguousarray(x_bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    lo = x.min(axis=-1)
+    hi = x.max(axis=-1)
+    scale16 = ((hi - lo) / np.float32(15.0)).astype(np.float16)
+    zero16 = lo.astype(np.float16)
+    sc = scale16.astype(np.float32)[..., None]
+    ze = zero16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.rint((x - ze) / sc)
+    codes = np.where(sc == 0, np.float32(0), np.clip(t, 0, 15)).astype(np.uint8)
+    params = np.stack([scale16.view(np.uint16), zero16.view(np.uint16)], axis=-1)
+    return codes, params
+
+
+def pack_int4(codes) -> np.ndarray:
+    """Two codes per byte: channel 2i in the low nibble, 2i + 1 in the high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def dequant_int4_ref(packed, params) -> np.ndarray:
+    """x_c = n_c * scale + zero in fp64 from packed codes [..., D/2] and fp16 params [..., 2]."""
+    pr = np.ascontiguousarray(params, dtype=np.uint16).view(np.float16).astype(np.float64)
+    return unpack_int4(packed).astype(np.float64) * pr[..., 0:1] + pr[..., 1:2]
+
+
+def quantize_cache_int4_ref(cache_bits, page_table, seq_lens, P: int):
+    """INT4 pages of the valid tokens of every sequence: (packed [NP, Hkv, P, D/2] uint8,
+    params [NP, Hkv, P, 2] uint16) and a mask [NP, P] of the rows that were written
+    (rows of other pages and past a sequence's length stay zero)."""
+    C = np.asarray(cache_bits, dtype=np.uint16)
+    NP, Hkv, _, D = C.shape
+    packed = np.zeros((NP, Hkv, P, D // 2), dtype=np.uint8)
+    params = np.zeros((NP, Hkv, P, 2), dtype=np.uint16)
+    written = np.zeros((NP, P), dtype=bool)
+    pt = np.asarray(page_table)
+    for b, L in enumerate(int(x) for x in seq_lens):
+        for j in range((L + P - 1) // P):
+            pg = int(pt[b, j])
+            n = min(P, L - j * P)
+            codes, pr = quantize_int4_ref(C[pg, :, :n, :])
+            packed[pg, :, :n] = pack_int4(codes)
+            params[pg, :, :n] = pr
+            written[pg, :n] = True
+    return packed, params, written
+
+
+def decode_int4_ref(q_bits, k_packed, v_packed, k_params, v_params, page_table, seq_lens, Hq: int,
+                    Hkv: int, P: int, head_kind, selected: Dict[Tuple[int, int], Sequence[int]],
+                    sink_tokens: int, local_tokens: int, sm_scale: float,
+                    batches: Optional[Sequence[int]] = None):
+    """decode_ref over INT4 pages: the same key sets, with K and V rows the fp64
+    dequantization of their codes."""
+    Kq, Vq = np.asarray(k_packed), np.asarray(v_packed)
+    Kp, Vp = np.asarray(k_params), np.asarray(v_params)
+
+    def rows(b, g, page_row, L, keys):
+        return (dequant_int4_ref(tokens_of_sequence(Kq, page_row, L, P, keys)[:, g, :],
+                                 tokens_of_sequence(Kp, page_row, L, P, keys)[:, g, :]),
+                dequant_int4_ref(tokens_of_sequence(Vq, page_row, L, P, keys)[:, g, :],
+                                 tokens_of_sequence(Vp, page_row, L, P, keys)[:, g, :]))
+
+    return _decode_over(bf16_to_f64(q_bits), rows, 2 * Kq.shape[-1], page_table, seq_lens, Hq, Hkv, P,
+                        head_kind, selected, sink_tokens, local_tokens, sm_scale, batches)

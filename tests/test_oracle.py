@@ -508,3 +508,111 @@ def test_append_then_gather_round_trip():
     kt, k2t = k.transpose(0, 2, 1, 3), k2.transpose(0, 2, 1, 3)       # [NP, P, Hkv, D]
     vt, v2t = v.transpose(0, 2, 1, 3), v2.transpose(0, 2, 1, 3)
     assert np.array_equal(k2t[~touched], kt[~touched]) and np.array_equal(v2t[~touched], vt[~touched])
+
+
+# ----------------------------------------------------------------------------- INT4 KV pages
+
+def _f32_to_bf16_bits(x) -> np.ndarray:
+    """bf16 bits of values that bf16 holds exactly (the test builds only such values)."""
+    b = np.asarray(x, dtype=np.float32).view(np.uint32)
+    assert np.all(b & 0xFFFF == 0), "value not exact in bf16"
+    return (b >> 16).astype(np.uint16)
+
+
+def test_int4_hand_example_codes_bytes_and_params():
+    """Row 0..15: lo 0, hi 15, scale (15 - 0)/15 = 1 -> fp16 0x3C00, zero fp16(0) = 0x0000;
+    codes equal the values; bytes pair channel 2i (low nibble) with 2i+1 (high nibble):
+    (0,1) -> 0x10, (2,3) -> 0x32, ..., (14,15) -> 0xFE."""
+    x = _f32_to_bf16_bits(np.arange(16, dtype=np.float32))
+    codes, params = oracle.quantize_int4_ref(x)
+    assert codes.tolist() == list(range(16))
+    assert params.tolist() == [0x3C00, 0x0000]
+    packed = oracle.pack_int4(codes)
+    assert packed.tolist() == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    assert np.array_equal(oracle.unpack_int4(packed), codes)
+    assert np.array_equal(oracle.dequant_int4_ref(packed, params), np.arange(16, dtype=np.float64))
+
+
+def test_int4_negative_range_exact_round_trip():
+    """x = -3 + 0.5k, k = 0..15 in a shuffled order: scale 7.5/15 = 0.5 and zero -3 are exact
+    in fp16, every value sits on a code, so the round trip is exact and code = k."""
+    rng = np.random.default_rng(5)
+    k = rng.permutation(16)
+    xs = (-3.0 + 0.5 * k).astype(np.float32)
+    codes, params = oracle.quantize_int4_ref(_f32_to_bf16_bits(xs))
+    assert codes.tolist() == k.tolist()
+    assert params.view(np.float16).astype(np.float64).tolist() == [0.5, -3.0]
+    assert np.array_equal(oracle.dequant_int4_ref(oracle.pack_int4(codes), params), xs.astype(np.float64))
+
+
+def test_int4_constant_row_has_zero_scale():
+    x = _f32_to_bf16_bits(np.full(8, -1.25, dtype=np.float32))
+    codes, params = oracle.quantize_int4_ref(x)
+    assert codes.tolist() == [0] * 8
+    assert params.view(np.float16).astype(np.float64).tolist() == [0.0, -1.25]
+    assert np.array_equal(oracle.dequant_int4_ref(oracle.pack_int4(codes), params), np.full(8, -1.25))
+
+
+def test_int4_codes_are_nearest_and_error_bounded():
+    """Brute force over the 16 codes: each chosen code is the nearest grid point
+    n*scale + zero to x (within fp32 rounding of the division), and |x - xhat| <= scale/2
+    up to the fp16 rounding of the parameters."""
+    rng = np.random.default_rng(6)
+    xb = (rng.standard_normal((300, 64)).astype(np.float32) * rng.uniform(0.01, 20, (300, 1)).astype(np.float32))
+    xb = ((xb.view(np.uint32) + 0x8000) >> 16).astype(np.uint16)          # round to bf16
+    x = oracle.bf16_to_f64(xb)
+    codes, params = oracle.quantize_int4_ref(xb)
+    pr = params.view(np.float16).astype(np.float64)
+    s, z = pr[:, 0:1], pr[:, 1:2]
+    grid = np.arange(16)[None, None, :] * s[:, :, None] + z[:, :, None]   # [rows, 1, 16]
+    dist = np.abs(x[:, :, None] - grid)
+    chosen = np.take_along_axis(dist, codes[:, :, None].astype(np.int64), axis=2)[:, :, 0]
+    assert np.all(chosen <= dist.min(axis=2) + 1e-6 * s)
+    xhat = oracle.dequant_int4_ref(oracle.pack_int4(codes), params)
+    assert np.all(np.abs(x - xhat) <= 0.51 * s + 1e-12)
+    assert np.all((codes >= 0) & (codes <= 15))
+
+
+def test_int4_cache_writes_valid_rows_only():
+    rng = np.random.default_rng(7)
+    P, Hkv, D = 16, 2, 8
+    lens = [5, 40]
+    pt = np.array([[3, 0, 0], [1, 4, 2]], dtype=np.int32)
+    cache = ((rng.standard_normal((5, Hkv, P, D)).astype(np.float32).view(np.uint32) + 0x8000) >> 16)
+    cache = cache.astype(np.uint16)
+    packed, params, written = oracle.quantize_cache_int4_ref(cache, pt, lens, P)
+    want = np.zeros((5, P), dtype=bool)
+    want[3, :5] = True
+    want[1, :] = True
+    want[4, :] = True
+    want[2, :8] = True
+    assert np.array_equal(written, want)
+    assert not packed.transpose(0, 2, 1, 3)[~want].any() and not params.transpose(0, 2, 1, 3)[~want].any()
+    c, p = oracle.quantize_int4_ref(cache[2, 1, 3])
+    assert np.array_equal(packed[2, 1, 3], oracle.pack_int4(c)) and np.array_equal(params[2, 1, 3], p)
+
+
+def test_int4_decode_equals_bf16_decode_on_exactly_representable_rows():
+    """Rows built on an exact INT4 grid (integers 0..15 times a power of two plus an offset
+    that bf16 and fp16 hold exactly, both ends present): dequantization reproduces them, so
+    decode over the INT4 pages equals decode over the bf16 pages."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, D, P = 2, 4, 2, 16, 16
+    lens = [40, 23]
+    NP = 6
+    pt = np.array([[5, 0, 3], [2, 4, 0]], dtype=np.int32)
+    codes = rng.integers(0, 16, size=(NP, Hkv, P, 2, D))
+    codes[..., 0] = 0
+    codes[..., 1] = 15
+    step = 2.0 ** rng.integers(-3, 2, size=(NP, Hkv, P, 2, 1))
+    off = rng.integers(-8, 8, size=(NP, Hkv, P, 2, 1)) * 0.25
+    vals = (codes * step + off).astype(np.float32)
+    kb, vb = _f32_to_bf16_bits(vals[:, :, :, 0]), _f32_to_bf16_bits(vals[:, :, :, 1])
+    q = ((rng.standard_normal((B, Hq, D)).astype(np.float32).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)
+    kq, kp, _ = oracle.quantize_cache_int4_ref(kb, pt, lens, P)
+    vq, vp, _ = oracle.quantize_cache_int4_ref(vb, pt, lens, P)
+    sel = {(0, 0): [0, 2], (1, 0): [1]}
+    args = (pt, lens, Hq, Hkv, P, [0, 1], sel, 3, 7, 0.3)
+    o1, l1 = oracle.decode_ref(q, kb, vb, *args)
+    o2, l2 = oracle.decode_int4_ref(q, kq, vq, kp, vp, *args)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12) and np.allclose(l1, l2, rtol=0, atol=1e-12)
