@@ -18,6 +18,8 @@
  *                      query/key tile scores.
  *   append_kv          new tokens into the paged cache, with the page summaries
  *                      they change.
+ *   quantize_kv_int4, sparse_decode_int4
+ *                      INT4 pages of the cache and decode attention over them.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -218,6 +220,45 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
                   const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
                   int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * INT4 KV pages -- quantize_kv_int4 and sparse_decode_int4.
+ *
+ * The blog's "LServe -- Decode Phase" section and its Figure 2 caption: INT4 KV
+ * quantization stacks with page sparsity, cutting the bytes of every page decode
+ * reads. The pages give no format; this library's format quantizes every
+ * (token, KV head) row of D channels on its own, asymmetrically:
+ *   scale = fp16((max_c x_c - min_c x_c) / 15), zero = fp16(min_c x_c)
+ *   n_c   = clamp(rint((x_c - zero) / scale), 0, 15)  in fp32 (n = 0 if scale == 0)
+ *   x_c  ~ n_c * scale + zero
+ * Layout (same page indexing as the bf16 cache):
+ *   codes  uint8  [NP][Hkv][P][D/2]: channel 2i in the low nibble of byte i,
+ *                                     channel 2i+1 in its high nibble
+ *   params uint16 [NP][Hkv][P][2]:   fp16 bits of (scale, zero)
+ * 68 bytes per row at D = 128 against 256 for bf16.
+ *
+ * quantize_kv_int4: the codes and params of every valid token (t < seq_lens[b])
+ * of every sequence, every KV head, K and V; rows of other pages or past a
+ * sequence's length are left as they were. Inputs are bf16 caches
+ * [NP][Hkv][P][D] (16-byte aligned); codes and params 4-byte aligned. Values
+ * must be finite and their range / 15 must fit fp16.
+ *
+ * sparse_decode_int4: sparse_decode with K and V read from INT4 pages instead of
+ * the bf16 caches; the key sets, arguments, outputs, workspace and supported
+ * shapes are those of sparse_decode. The result is attention over the
+ * dequantized rows (fp32 arithmetic). Codes 16-byte aligned, params 4-byte.
+ */
+int quantize_kv_int4(const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache, const int32_t* page_table,
+                     const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hkv, int32_t D, int32_t P,
+                     uint8_t* k_codes, uint8_t* v_codes, uint16_t* k_params, uint16_t* v_params,
+                     hipStream_t stream);
+int sparse_decode_int4(const ubs_bf16_t* q, const uint8_t* k_codes, const uint8_t* v_codes,
+                       const uint16_t* k_params, const uint16_t* v_params, const int32_t* page_table,
+                       const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv,
+                       int32_t D, int32_t P, const uint8_t* head_kind /* host */, const int32_t* selected,
+                       const int32_t* num_selected, int32_t max_selected, int32_t sink_tokens,
+                       int32_t local_tokens, float sm_scale, float* out, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 /*
  * append_kv -- write newly decoded or prefilled tokens into the paged KV cache and

@@ -246,3 +246,50 @@ def test_append_validation(kw, code, frag):
 
 def test_append_nothing_to_do():
     assert _append(n=0, kn=None, vn=None, pt=None, sl=None, k=None, v=None, bnd=None) == 0
+
+
+def _quant(**kw):
+    a = dict(k=A, v=A, pt=A, sl=A, B=4, maxp=64, Hkv=8, D=128, P=64, kc=A, vc=A, kp=A, vp=A, stream=NULL)
+    a.update(kw)
+    return ubs.load().quantize_kv_int4(a["k"], a["v"], a["pt"], a["sl"], a["B"], a["maxp"], a["Hkv"], a["D"],
+                                       a["P"], a["kc"], a["vc"], a["kp"], a["vp"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(D=96), -2, "D=96"),
+    (dict(P=40), -2, "P=40"),
+    (dict(Hkv=0), -1, "Hkv=0"),
+    (dict(B=-1), -1, "B=-1"),
+    (dict(kc=None), -1, "non-NULL"),
+    (dict(k=A + 8), -1, "aligned"),
+    (dict(kp=A + 2), -1, "aligned"),
+])
+def test_quantize_int4_validation(kw, code, frag):
+    assert _quant(**kw) == code
+    assert frag in _err()
+
+
+def test_quantize_int4_nothing_to_do():
+    assert _quant(B=0, k=None, v=None, pt=None, sl=None, kc=None, vc=None, kp=None, vp=None) == 0
+
+
+def _decode4(**kw):
+    lib = ubs.load()
+    a = dict(q=A, kc=A, vc=A, kp=A, vp=A, pt=A, sl=A, B=4, maxp=512, Hq=32, Hkv=8, D=128, P=64, kind=KIND, sel=A,
+             nsel=A, ms=64, sink=128, local=512, scale=0.088, out=A, lse=NULL, ws=A, wsb=None, stream=NULL)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.ubs_decode_workspace_size(a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["ms"],
+                                                    a["sink"], a["local"])
+    return lib.sparse_decode_int4(a["q"], a["kc"], a["vc"], a["kp"], a["vp"], a["pt"], a["sl"], a["B"], a["maxp"],
+                                  a["Hq"], a["Hkv"], a["D"], a["P"], a["kind"], a["sel"], a["nsel"], a["ms"],
+                                  a["sink"], a["local"], a["scale"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                  a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(P=40), -2), (dict(Hq=24), -2), (dict(D=80), -2), (dict(sink=-1), -1), (dict(wsb=100), -3),
+    (dict(nsel=None), -1), (dict(out=None), -1), (dict(kp=None), -1), (dict(kc=A + 4), -1), (dict(vp=A + 2), -1),
+])
+def test_decode_int4_validation(kw, code):
+    assert _decode4(**kw) == code

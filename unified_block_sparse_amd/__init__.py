@@ -13,11 +13,14 @@ and the steps around them in serving:
 
     estimate_block_mask  dense heads' block mask from mean-pooled tile scores
     append_kv            new tokens into the paged cache, page bounds refreshed
+    quantize_kv_int4     INT4 pages of the cache (per-row 4-bit codes, fp16 scale/zero)
+    sparse_decode_int4   sparse_decode over the INT4 pages
 
 Build the library with ``python -m unified_block_sparse_amd.build``.
 """
 from ._lib import (UBSError, load, sparse_prefill, sparse_prefill_chunk, build_page_bounds,  # noqa: F401
-                   select_pages, sparse_decode, estimate_block_mask, append_kv, LIB_PATH, EXPORTED)
+                   select_pages, sparse_decode, estimate_block_mask, append_kv, quantize_kv_int4,
+                   sparse_decode_int4, LIB_PATH, EXPORTED)
 
 __all__ = ["UBSError", "load", "sparse_prefill", "sparse_prefill_chunk", "build_page_bounds", "select_pages",
-           "sparse_decode", "estimate_block_mask", "append_kv"]
+           "sparse_decode", "estimate_block_mask", "append_kv", "quantize_kv_int4", "sparse_decode_int4"]

@@ -21,7 +21,7 @@ UBS_OK = 0
 ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
 EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
-            "append_kv",
+            "append_kv", "quantize_kv_int4", "sparse_decode_int4",
             "ubs_last_error", "ubs_version")
 
 
@@ -69,6 +69,11 @@ def load() -> ctypes.CDLL:
         lib.sparse_decode.restype = ctypes.c_int
         lib.sparse_decode.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _i,
                                       _f, _p, _p, _p, _sz, _p]
+        lib.sparse_decode_int4.restype = ctypes.c_int
+        lib.sparse_decode_int4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i,
+                                           _i, _f, _p, _p, _p, _sz, _p]
+        lib.quantize_kv_int4.restype = ctypes.c_int
+        lib.quantize_kv_int4.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]
         lib.append_kv.restype = ctypes.c_int
         lib.append_kv.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]
         lib.ubs_mask_workspace_size.restype = _sz
@@ -274,6 +279,90 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            sink_tokens, local_tokens, float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), st)
     _check("sparse_decode", rc)
+    return (out, lse) if return_lse else out
+
+
+def quantize_kv_int4(k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                     seq_lens: torch.Tensor, out: Optional[Tuple[torch.Tensor, ...]] = None):
+    """INT4 pages of the valid tokens of every sequence (see include/ubs.h).
+
+    k_cache, v_cache bf16 [NP, Hkv, P, D]; page_table int32 [B, max_pages]; seq_lens int32 [B].
+    Returns (k_codes, v_codes) uint8 [NP, Hkv, P, D/2] and (k_params, v_params) int16 [NP, Hkv, P, 2]
+    holding fp16 (scale, zero) bits, as the tuple (k_codes, v_codes, k_params, v_params). Rows
+    that are not valid tokens keep what `out` held (zeros when out is None).
+    """
+    lib = load()
+    NP, Hkv, P, D = k_cache.shape
+    B, max_pages = page_table.shape
+    dev = k_cache.device
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(v_cache, "v_cache", torch.bfloat16, shape=k_cache.shape, device=dev)
+    _need(page_table, "page_table", torch.int32, shape=(B, max_pages), device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    if out is None:
+        out = (torch.zeros((NP, Hkv, P, D // 2), dtype=torch.uint8, device=dev),
+               torch.zeros((NP, Hkv, P, D // 2), dtype=torch.uint8, device=dev),
+               torch.zeros((NP, Hkv, P, 2), dtype=torch.int16, device=dev),
+               torch.zeros((NP, Hkv, P, 2), dtype=torch.int16, device=dev))
+    kc, vc, kp, vp = out
+    for t, name, dt, shp in ((kc, "k_codes", torch.uint8, (NP, Hkv, P, D // 2)),
+                             (vc, "v_codes", torch.uint8, (NP, Hkv, P, D // 2)),
+                             (kp, "k_params", torch.int16, (NP, Hkv, P, 2)),
+                             (vp, "v_params", torch.int16, (NP, Hkv, P, 2))):
+        _need(t, name, dt, shape=shp, device=dev)
+    rc = lib.quantize_kv_int4(_ptr(k_cache), _ptr(v_cache), _ptr(page_table), _ptr(seq_lens), B, max_pages, Hkv,
+                              D, P, _ptr(kc), _ptr(vc), _ptr(kp), _ptr(vp), _stream(dev))
+    _check("quantize_kv_int4", rc)
+    return kc, vc, kp, vp
+
+
+def sparse_decode_int4(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Tensor, k_params: torch.Tensor,
+                       v_params: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                       head_kind: Sequence[int], selected: Optional[torch.Tensor],
+                       num_selected: Optional[torch.Tensor], sink_tokens: int, local_tokens: int, sm_scale: float,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """sparse_decode over INT4 pages (codes uint8 [NP, Hkv, P, D/2], params int16 [NP, Hkv, P, 2])."""
+    lib = load()
+    B, Hq, D = q.shape
+    NP, Hkv, P, D2 = k_codes.shape
+    _, max_pages = page_table.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(k_codes, "k_codes", torch.uint8, device=dev)
+    _need(v_codes, "v_codes", torch.uint8, shape=k_codes.shape, device=dev)
+    _need(k_params, "k_params", torch.int16, shape=(NP, Hkv, P, 2), device=dev)
+    _need(v_params, "v_params", torch.int16, shape=(NP, Hkv, P, 2), device=dev)
+    _need(page_table, "page_table", torch.int32, shape=(B, max_pages), device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    if 2 * D2 != D:
+        raise ValueError("q's head dim must be twice the codes' last dim")
+    if selected is not None:
+        _need(selected, "selected", torch.int32, device=dev)
+        if selected.dim() != 3 or selected.shape[:2] != (B, Hkv):
+            raise ValueError("selected must be [B, Hkv, max_selected]")
+        max_selected = selected.shape[2]
+    else:
+        max_selected = 0
+    if num_selected is not None:
+        _need(num_selected, "num_selected", torch.int32, shape=(B, Hkv), device=dev)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, shape=(B, Hq, D), device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq), device=dev)
+    st = _stream(dev)
+    need = lib.ubs_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens)
+    if workspace is None:
+        workspace = _workspace("decode", dev, st, need)
+    rc = lib.sparse_decode_int4(_ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_params), _ptr(v_params),
+                                _ptr(page_table), _ptr(seq_lens), B, max_pages, Hq, Hkv, D, P, _kinds(head_kind),
+                                _ptr(selected), _ptr(num_selected), max_selected, sink_tokens, local_tokens,
+                                float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), st)
+    _check("sparse_decode_int4", rc)
     return (out, lse) if return_lse else out
 
 

@@ -242,12 +242,14 @@ size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
   return ((size_t)B * Hq * ms * (D + 2) * sizeof(float) + 255) / 256 * 256;
 }
 
-int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
-                  const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq,
-                  int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind, const int32_t* selected,
-                  const int32_t* num_selected, int32_t max_selected, int32_t sink_tokens, int32_t local_tokens,
-                  float sm_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream) {
+// Shared body of sparse_decode (bf16 pages: k, v are the caches) and sparse_decode_int4
+// (k, v are the code arrays, kp, vp the row params).
+static int decode_impl(const char* name, bool int4, const ubs_bf16_t* q, const void* k, const void* v,
+                       const uint16_t* kp, const uint16_t* vp, const int32_t* page_table, const int32_t* seq_lens,
+                       int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                       const uint8_t* head_kind, const int32_t* selected, const int32_t* num_selected,
+                       int32_t max_selected, int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out,
+                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = common_heads(Hq, Hkv, D);
   if (rc) return rc;
   REQUIRE(B >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT, "B=%d, max_pages=%d must be >= 0", B, max_pages);
@@ -263,13 +265,20 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
   rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
   if (rc) return rc;
   if (B == 0) return ok();
-  REQUIRE(q && k_cache && v_cache && page_table && seq_lens && out, UBS_ERR_INVALID_ARGUMENT,
-          "q, k_cache, v_cache, page_table, seq_lens and out must be non-NULL");
+  if (int4) {
+    REQUIRE(q && k && v && kp && vp && page_table && seq_lens && out, UBS_ERR_INVALID_ARGUMENT,
+            "q, k_codes, v_codes, k_params, v_params, page_table, seq_lens and out must be non-NULL");
+    REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && ((uintptr_t)kp % 4 == 0) && ((uintptr_t)vp % 4 == 0),
+            UBS_ERR_INVALID_ARGUMENT, "q and the codes must be 16-byte aligned, the params 4-byte aligned");
+  } else {
+    REQUIRE(q && k && v && page_table && seq_lens && out, UBS_ERR_INVALID_ARGUMENT,
+            "q, k_cache, v_cache, page_table, seq_lens and out must be non-NULL");
+    REQUIRE(aligned16(q) && aligned16(k) && aligned16(v), UBS_ERR_INVALID_ARGUMENT,
+            "q, k_cache and v_cache must be 16-byte aligned");
+  }
   REQUIRE(dense.n == 0 || max_selected == 0 || (selected && num_selected), UBS_ERR_INVALID_ARGUMENT,
           "selected / num_selected are NULL but a KV head is dense");
   REQUIRE(dense.n == 0 || num_selected, UBS_ERR_INVALID_ARGUMENT, "num_selected is NULL but a KV head is dense");
-  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache), UBS_ERR_INVALID_ARGUMENT,
-          "q, k_cache and v_cache must be 16-byte aligned");
   const size_t need = ubs_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens);
   REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
           "workspace of %zu bytes, need %zu", workspace_bytes, need);
@@ -278,8 +287,16 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
   REQUIRE(blocks < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large", (long long)blocks);
   ubs::DecodeArgs a{};
   a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
+  if (int4) {
+    a.int4 = 1;
+    a.k_codes = static_cast<const uint8_t*>(k);
+    a.v_codes = static_cast<const uint8_t*>(v);
+    a.k_params = kp;
+    a.v_params = vp;
+  } else {
+    a.k_cache = static_cast<const uint16_t*>(k);
+    a.v_cache = static_cast<const uint16_t*>(v);
+  }
   a.page_table = page_table;
   a.seq_lens = seq_lens;
   a.selected = selected;
@@ -303,7 +320,50 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
   a.lse = lse;
   a.partials = static_cast<float*>(workspace);
   a.max_splits = pl.max_splits;
-  return hip_status(ubs::launch_decode(a, stream), "sparse_decode launch");
+  std::string what = std::string(name) + " launch";
+  return hip_status(ubs::launch_decode(a, stream), what.c_str());
+}
+
+int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                  const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq,
+                  int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind, const int32_t* selected,
+                  const int32_t* num_selected, int32_t max_selected, int32_t sink_tokens, int32_t local_tokens,
+                  float sm_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  return decode_impl("sparse_decode", false, q, k_cache, v_cache, nullptr, nullptr, page_table, seq_lens, B,
+                     max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, max_selected, sink_tokens,
+                     local_tokens, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int sparse_decode_int4(const ubs_bf16_t* q, const uint8_t* k_codes, const uint8_t* v_codes, const uint16_t* k_params,
+                       const uint16_t* v_params, const int32_t* page_table, const int32_t* seq_lens, int32_t B,
+                       int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind,
+                       const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
+                       int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl("sparse_decode_int4", true, q, k_codes, v_codes, k_params, v_params, page_table, seq_lens, B,
+                     max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, max_selected, sink_tokens,
+                     local_tokens, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int quantize_kv_int4(const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache, const int32_t* page_table,
+                     const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hkv, int32_t D, int32_t P,
+                     uint8_t* k_codes, uint8_t* v_codes, uint16_t* k_params, uint16_t* v_params,
+                     hipStream_t stream) {
+  REQUIRE(Hkv > 0 && Hkv <= 64, UBS_ERR_INVALID_ARGUMENT, "Hkv=%d must be in 1..64", Hkv);
+  REQUIRE(D == 64 || D == 128, UBS_ERR_UNSUPPORTED, "D=%d (supported: 64, 128)", D);
+  REQUIRE(B >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT, "B=%d, max_pages=%d must be >= 0", B, max_pages);
+  REQUIRE(P > 0 && P % 16 == 0 && P <= 256, UBS_ERR_UNSUPPORTED, "P=%d must be a multiple of 16 up to 256", P);
+  if (B == 0 || max_pages == 0) return ok();
+  REQUIRE((int64_t)B * max_pages < (1ll << 31), UBS_ERR_UNSUPPORTED, "B * max_pages is too large");
+  REQUIRE(k_cache && v_cache && page_table && seq_lens && k_codes && v_codes && k_params && v_params,
+          UBS_ERR_INVALID_ARGUMENT, "every pointer must be non-NULL");
+  REQUIRE(aligned16(k_cache) && aligned16(v_cache) && ((uintptr_t)k_codes % 4 == 0) &&
+              ((uintptr_t)v_codes % 4 == 0) && ((uintptr_t)k_params % 4 == 0) && ((uintptr_t)v_params % 4 == 0),
+          UBS_ERR_INVALID_ARGUMENT, "the caches must be 16-byte aligned, codes and params 4-byte aligned");
+  ubs::QuantArgs a{k_cache, v_cache, page_table, seq_lens, B, max_pages, Hkv, D, P,
+                   k_codes, v_codes, k_params, v_params};
+  return hip_status(ubs::launch_quant_int4(a, stream), "quantize_kv_int4 launch");
 }
 
 size_t ubs_mask_workspace_size(int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t T) {

@@ -15,6 +15,10 @@
 //   online softmax in the log2 domain (fp32);
 //   O += P V     : fp32 FMAs, each lane owning 8 channels of one key row, V read with
 //                  16-byte loads that cover whole rows, P broadcast through LDS.
+// INT4 pages (same kernel, Q4 = true): K rows come as 4-bit codes n with a per-row fp16
+// (scale s, zero z), x = n s + z. The codes enter the MFMA as bf16 128 + n (exact: the
+// code is OR-ed into the mantissa of 128), so S = s (Q.(128 + n)) + (z - 128 s) sum(Q);
+// V codes are weighted by p s and the sum of p z is added to every channel at the end.
 // Partial (max, sum, output) triples of the 4 waves are merged through LDS; the
 // work-group writes one partial per split (or the output when the key set has one
 // split), and a second launch merges the splits of each (b, g) with a log-sum-exp
@@ -27,6 +31,34 @@
 namespace ubs {
 
 constexpr int kMaxSplits = 128;
+constexpr int kChunkTokens = 32;   // tokens per chunk
+
+// K and V of one chunk in registers, per lane: bf16 rows, or INT4 codes and row params
+template <int D, bool Q4>
+struct ChunkRegs {
+  u32x4 k[kChunkTokens / 16][D / 32];
+  u32x4 v[D / 16];
+};
+template <int D>
+struct ChunkRegs<D, true> {
+  uint32_t k[kChunkTokens / 16][D / 32];   // 8 codes per word
+  uint32_t kp[kChunkTokens / 16];          // fp16 (scale, zero) of the lane's key row
+  uint32_t v[D / 16];                      // the lane's 8 channels of a V row
+  uint32_t vp[D / 16];
+};
+
+__device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// 8 INT4 codes (channel 2j in the low nibble of byte j, 2j+1 in its high nibble) as the
+// bf16 values 128 + n, in channel order
+__device__ __forceinline__ bf16x8 codes_bf16(uint32_t w) {
+  const uint32_t t = w & 0x0F0F0F0Fu, u = (w >> 4) & 0x0F0F0F0Fu;
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = 0x43004300u | ((t >> (8 * j)) & 0xFu) | (((u >> (8 * j)) & 0xFu) << 16);
+  return as_bf16x8(r);
+}
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -82,12 +114,12 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
   return ch;
 }
 
-template <int D, int G>
+template <int D, int G, bool Q4>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   constexpr int KK = D / 32;   // QK MFMA steps (16x16x32)
   constexpr int CH = D / 8;    // lanes per V row (16-byte pieces)
   constexpr int TG = 64 / CH;  // token groups in P.V
-  constexpr int CT = 32;       // tokens per chunk
+  constexpr int CT = kChunkTokens;
   constexpr int NB = CT / 16;  // 16-key MFMA blocks per chunk
   constexpr int VR = CT / TG;  // V rows per lane and chunk
   __shared__ float p_lds[4][CT][G];
@@ -129,15 +161,32 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 
   // ---- Q as the MFMA A operand: row m = query head (zero rows past G); k-slot group
   // qg = l/16 holds channels kk*32 + qg*8 + [0, 8) for step kk (so that one K load
-  // instruction reads 64 contiguous bytes of each of its 16 rows).
+  // instruction reads 64 contiguous bytes of each of its 16 rows); with INT4 pages,
+  // channels qg*D/4 + kk*8 + [0, 8) (one load brings a lane's codes for every step).
   const int m = lane & 15;
   const int qg = lane >> 4;
   bf16x8 qa[KK];
   {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + m) * D + qg * 8;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + m) * D;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qa[kk] = as_bf16x8((m < G) ? ld16(qrow + kk * 32) : u32x4{0, 0, 0, 0});
+      qa[kk] = as_bf16x8((m < G) ? ld16(qrow + (Q4 ? qg * (D / 4) + kk * 8 : kk * 32 + qg * 8))
+                                 : u32x4{0, 0, 0, 0});
+  }
+  // INT4: sum of the channels of query heads 4*qg + i (the rows of this lane's scores)
+  float qsum[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (Q4) {
+    float sq = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4 w = __builtin_bit_cast(u32x4, qa[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sq += bf16_lo(w[e]) + bf16_hi(w[e]);
+    }
+    sq += shfl_xor(sq, 16);
+    sq += shfl_xor(sq, 32);   // all channels of head m
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qsum[i] = __shfl(sq, 4 * qg + i, 64);
   }
 
   float m_run[4];   // running max of heads 4*qg + i (lane-replicated within a 16-lane group)
@@ -145,9 +194,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   for (int i = 0; i < 4; ++i) m_run[i] = kNegInf;
   float o[G][8];
   float lsum[G];
+  float zacc[G];   // INT4: sum over the lane's V rows of p * zero
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     lsum[h] = 0.f;
+    zacc[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
@@ -167,26 +218,61 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
     return __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, page >= 0 ? P * D * 2 : 0, 0x00020000);
   };
-  auto load = [&](int t, int nt, u32x4 (&kr)[NB][KK], u32x4 (&vr)[VR]) __attribute__((always_inline)) {
+  // (INT4: the same over a slab of row_bytes-byte rows of codes or of params)
+  auto slab_rsrc4 = [&](const void* base, int page, int row_bytes) __attribute__((always_inline)) {
+    const uint64_t addr =
+        (uint64_t)((const uint8_t*)base + ((int64_t)max(page, 0) * a.Hkv + g) * (int64_t)P * row_bytes);
+    const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, page >= 0 ? P * row_bytes : 0, 0x00020000);
+  };
+  auto load = [&](int t, int nt, ChunkRegs<D, Q4>& R) __attribute__((always_inline)) {
     const int page = t < nt ? __builtin_amdgcn_readlane(d_page, min(t, 63)) : -1;
     const int r0 = __builtin_amdgcn_readlane(d_r0, min(t, 63));
-    const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache, page);
-    const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache, page);
+    if constexpr (Q4) {
+      const __amdgpu_buffer_rsrc_t rk = slab_rsrc4(a.k_codes, page, D / 2);
+      const __amdgpu_buffer_rsrc_t rkp = slab_rsrc4(a.k_params, page, 4);
+      const __amdgpu_buffer_rsrc_t rv = slab_rsrc4(a.v_codes, page, D / 2);
+      const __amdgpu_buffer_rsrc_t rvp = slab_rsrc4(a.v_params, page, 4);
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      const int row = min(r0 + blk * 16 + m, P - 1);
-      const int off = (row * D + qg * 8) * 2;
+      for (int blk = 0; blk < NB; ++blk) {
+        const int row = min(r0 + blk * 16 + m, P - 1);
+        if constexpr (D == 128) {
+          const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rk, row * 64 + qg * 16, 0, 0);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kr[blk][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 64, 0, 0);
-    }
+          for (int kk = 0; kk < KK; ++kk) R.k[blk][kk] = w[kk];
+        } else {
+          const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rk, row * (D / 2) + qg * (D / 8), 0, 0);
 #pragma unroll
-    for (int x = 0; x < VR; ++x) {
-      const int row = min(r0 + tg + TG * x, P - 1);
-      vr[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * D + cc * 8) * 2, 0, 0);
+          for (int kk = 0; kk < KK; ++kk) R.k[blk][kk] = w[kk];
+        }
+        R.kp[blk] = __builtin_amdgcn_raw_buffer_load_b32(rkp, row * 4, 0, 0);
+      }
+#pragma unroll
+      for (int x = 0; x < VR; ++x) {
+        const int row = min(r0 + tg + TG * x, P - 1);
+        R.v[x] = __builtin_amdgcn_raw_buffer_load_b32(rv, row * (D / 2) + cc * 4, 0, 0);
+        R.vp[x] = __builtin_amdgcn_raw_buffer_load_b32(rvp, row * 4, 0, 0);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache, page);
+      const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache, page);
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk) {
+        const int row = min(r0 + blk * 16 + m, P - 1);
+        const int off = (row * D + qg * 8) * 2;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) R.k[blk][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 64, 0, 0);
+      }
+#pragma unroll
+      for (int x = 0; x < VR; ++x) {
+        const int row = min(r0 + tg + TG * x, P - 1);
+        R.v[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * D + cc * 8) * 2, 0, 0);
+      }
     }
   };
   // ---- online softmax and P.V over one chunk already in registers
-  auto compute = [&](int t, int nt, const u32x4 (&kr)[NB][KK], const u32x4 (&vr)[VR]) __attribute__((always_inline)) {
+  auto compute = [&](int t, int nt, const ChunkRegs<D, Q4>& R) __attribute__((always_inline)) {
     const int page = t < nt ? __builtin_amdgcn_readlane(d_page, min(t, 63)) : -1;
     if (page < 0) return;
     const int r0 = __builtin_amdgcn_readlane(d_r0, t);
@@ -196,13 +282,22 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(kr[blk][kk]), acc, 0, 0, 0);
       const int row = r0 + blk * 16 + m;
       const bool ok = row >= lo && row < hi;
+      if constexpr (Q4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], codes_bf16(R.k[blk][kk]), acc, 0, 0, 0);
+        const float sk = half_lo(R.kp[blk]), zk = half_hi(R.kp[blk]) - 128.f * sk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[blk][i] = ok ? fmaf(sk, acc[i], zk * qsum[i]) * scale_log2 : kNegInf;
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(R.k[blk][kk]), acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
+      }
     }
     // chunk max per head (heads 4*qg + i), then running max and weights
     float alpha_i[4];
@@ -231,6 +326,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       lsum[h] *= alpha[h];
+      if constexpr (Q4) zacc[h] *= alpha[h];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
     }
@@ -241,18 +337,35 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       const int rr = tg + TG * x;
       const int row = r0 + rr;
       const bool ok = row >= lo && row < hi;
-      float vf[8];
+      if constexpr (Q4) {
+        // (rows outside [lo, hi) have weight zero; their params are not trusted)
+        const float sv = ok ? half_lo(R.vp[x]) : 0.f, zv = ok ? half_hi(R.vp[x]) : 0.f;
+        float vf[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vf[2 * e] = ok ? bf16_lo(vr[x][e]) : 0.f;
-        vf[2 * e + 1] = ok ? bf16_hi(vr[x][e]) : 0.f;
-      }
+        for (int e = 0; e < 8; ++e) vf[e] = (float)((R.v[x] >> (4 * e)) & 0xFu);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = p_lds[wave][rr][h];
-        lsum[h] += p;
+        for (int h = 0; h < G; ++h) {
+          const float p = p_lds[wave][rr][h];
+          lsum[h] += p;
+          zacc[h] = fmaf(p, zv, zacc[h]);
+          const float ps = p * sv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(ps, vf[e], o[h][e]);
+        }
+      } else {
+        float vf[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vf[2 * e] = ok ? bf16_lo(R.v[x][e]) : 0.f;
+          vf[2 * e + 1] = ok ? bf16_hi(R.v[x][e]) : 0.f;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float p = p_lds[wave][rr][h];
+          lsum[h] += p;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+        }
       }
     }
     wave_sync_lds();
@@ -262,7 +375,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   // page table) costs one round trip per 64 chunks, before any of their K/V loads. Then
   // the loads of chunk t+1 are in flight while chunk t is computed (register double
   // buffer; unrolled by two so each buffer is a fixed register set).
-  u32x4 ka[NB][KK], va[VR], kb[NB][KK], vb[VR];
+  ChunkRegs<D, Q4> ra, rb;
   for (int t0 = 0; t0 < cpw; t0 += 64) {
     const int nt = min(64, cpw - t0);
     d_page = -1;
@@ -281,17 +394,24 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
     // (chunks past nt are empty: their loads read nothing and their compute is skipped;
     // the scheduling barriers keep each chunk's loads after the previous compute, so
     // at most two chunks' registers are live)
-    load(0, nt, ka, va);
+    load(0, nt, ra);
     for (int t = 0; t < nt; t += 2) {
-      load(t + 1, nt, kb, vb);
+      load(t + 1, nt, rb);
       __builtin_amdgcn_sched_barrier(0);
-      compute(t, nt, ka, va);
+      compute(t, nt, ra);
       __builtin_amdgcn_sched_barrier(0);
-      load(t + 2, nt, ka, va);
+      load(t + 2, nt, ra);
       __builtin_amdgcn_sched_barrier(0);
-      compute(t + 1, nt, kb, vb);
+      compute(t + 1, nt, rb);
       __builtin_amdgcn_sched_barrier(0);
     }
+  }
+  // (INT4: the zero terms join the output before the token groups are summed)
+  if constexpr (Q4) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[h][e] += zacc[h];
   }
 
   // ---- reduce the token groups of the wave
@@ -431,7 +551,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int64_t merge_blocks = (int64_t)a.B * merge_per_b;
 #define UBS_DECODE(DD, GG)                                                                            \
   if (a.D == DD && G == GG) {                                                                         \
-    hipLaunchKernelGGL((decode_kernel<DD, GG>), dim3((unsigned)blocks), dim3(256), 0, s, a);          \
+    if (a.int4)                                                                                       \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);  \
+    else                                                                                              \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, false>), dim3((unsigned)blocks), dim3(256), 0, s, a); \
     hipError_t e = hipGetLastError();                                                                 \
     if (e != hipSuccess || merge_blocks == 0) return e;                                               \
     hipLaunchKernelGGL((decode_merge_kernel<DD, GG>), dim3((unsigned)merge_blocks), dim3(256), 0, s, a); \

@@ -66,6 +66,24 @@ struct DecodeArgs {
   float* lse;
   float* partials;     // workspace [B][Hq][max_splits][D + 2]
   int max_splits;
+  // INT4 pages (int4 != 0): codes [NP][Hkv][P][D/2], fp16 (scale, zero) [NP][Hkv][P][2]
+  int int4;
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint16_t* k_params;
+  const uint16_t* v_params;
+};
+
+struct QuantArgs {
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  int B, max_pages, Hkv, D, P;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint16_t* k_params;
+  uint16_t* v_params;
 };
 
 struct PrefillArgs {
@@ -110,5 +128,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_quant_int4(const QuantArgs& a, hipStream_t s);
 
 }  // namespace ubs
