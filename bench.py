@@ -246,6 +246,85 @@ def mask_estimation(c, steps: int, warmup: int):
             "bytes": nbytes, "gbps": round(nbytes / t / 1e9, 1), "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
+# ----------------------------------------------------------------------------- graph-replayed decode
+
+def decode_graph_step(R: int = 24, replays: int = 10):
+    """Selection + decode of decode_llama8b, cycled over R independent cache instances
+    (seeds 1002 + r) captured once as one HIP graph: R x ~43 MB > 1 GiB of working set, so
+    each step reads HBM rather than the Infinity Cache, and graph replay takes the host
+    launch path out of the step. Time per step = replay time / R. Every replay's outputs
+    are checked bitwise against an eager run of the same calls before capture.
+    """
+    import torch
+    import unified_block_sparse_amd as ubs
+    from workloads import cases
+    dev = torch.device("cuda:0")
+    lib = ubs.load()
+    inst = []
+    for r in range(R):
+        d = cases.decode_llama8b(dev, seed=1002 + r)
+        bnd = torch.zeros((d.num_physical_pages, d.Hkv, d.P // d.Lp, 2, d.D), dtype=torch.bfloat16, device=dev)
+        ubs.build_page_bounds(d.k_cache, d.page_table, d.seq_lens_t, d.head_kind, d.Lp, bounds=bnd)
+        sel = torch.empty((d.B, d.Hkv, d.k_pages), dtype=torch.int32, device=dev)
+        num = torch.empty((d.B, d.Hkv), dtype=torch.int32, device=dev)
+        out = torch.empty((d.B, d.Hq, d.D), dtype=torch.float32, device=dev)
+        inst.append((d, bnd, sel, num, out))
+    d0 = inst[0][0]
+    ws_sel = torch.zeros(max(256, lib.ubs_select_workspace_size(d0.B, d0.page_table.shape[1], d0.Hkv)),
+                         dtype=torch.uint8, device=dev)
+    ws_dec = torch.zeros(max(256, lib.ubs_decode_workspace_size(d0.B, d0.Hq, d0.Hkv, d0.D, d0.P, d0.k_pages,
+                                                                d0.sink_tokens, d0.local_tokens)),
+                         dtype=torch.uint8, device=dev)
+
+    def run_all():
+        for d, bnd, sel, num, out in inst:
+            ubs.select_pages(d.q, bnd, d.page_table, d.seq_lens_t, d.head_kind, d.P, d.token_budget,
+                             selected=sel, num_selected=num, workspace=ws_sel)
+            ubs.sparse_decode(d.q, d.k_cache, d.v_cache, d.page_table, d.seq_lens_t, d.head_kind, sel, num,
+                              d.sink_tokens, d.local_tokens, d.sm_scale, out=out, workspace=ws_dec)
+
+    run_all()
+    torch.cuda.synchronize(dev)
+    ref = [(sel.clone(), num.clone(), out.clone()) for _, _, sel, num, out in inst]
+    nbytes = 0
+    for (d, _, _, _, _), (sel_r, num_r, _) in zip(inst, ref):
+        sel_h, num_h = sel_r.cpu().tolist(), num_r.cpu().tolist()
+        sel_pages = [[sel_h[b][g][:num_h[b][g]] for g in range(d.Hkv)] for b in range(d.B)]
+        _, b_select, b_decode = decode_bytes(d, sel_pages)
+        nbytes += b_select + b_decode
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        run_all()                     # warm the side stream before capture
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_all()
+    torch.cuda.synchronize(dev)
+    for _, _, sel, num, out in inst:  # replays must rewrite every output
+        sel.fill_(-7)
+        num.fill_(-7)
+        out.fill_(float("nan"))
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    for (_, _, sel, num, out), (sel_r, num_r, out_r) in zip(inst, ref):
+        if not (torch.equal(sel, sel_r) and torch.equal(num, num_r) and torch.equal(out, out_r)):
+            raise RuntimeError("graph replay differs from the eager run")
+    t = e0.elapsed_time(e1) * 1e-3 / replays / R
+    nb = nbytes / R
+    return {"workload": f"decode_llama8b x {R} cache instances, one HIP graph", "ms": round(t * 1e3, 4),
+            "bytes": int(nb), "gbps": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / PEAK_HBM_GBPS, 4)}
+
+
 # ----------------------------------------------------------------------------- ragged decode
 
 def ragged_decode_step(steps: int, warmup: int):
@@ -316,9 +395,62 @@ def ragged_decode_step(steps: int, warmup: int):
            "selection_reused_4_steps": {"ms_per_step": round(t_r * 1e3, 4), "bytes_per_step": int(b_r),
                                         "gbps": round(b_r / t_r / 1e9, 1),
                                         "frac": round(b_r / t_r / 1e9 / PEAK_HBM_GBPS, 4)}}
+    res["int4"] = ragged_int4(r, sel, num, sel_pages, b_select, t_sel, steps, warmup)
     del r, bnd
     torch.cuda.empty_cache()
     return res
+
+
+def ragged_int4(r, sel, num, sel_pages, b_select, t_sel, steps: int, warmup: int):
+    """INT4 pages of decode_ragged: quantize_kv_int4 over every valid token (read K and V
+    bf16 rows, write codes and params), then sparse_decode_int4 on the same selection
+    (K and V codes plus row params of every attended token, q, out). The step with INT4
+    pages is select_pages (timed above) + sparse_decode_int4."""
+    import torch
+    import unified_block_sparse_amd as ubs
+    dev = r.q.device
+    kc, vc, kp, vp = ubs.quantize_kv_int4(r.k_cache, r.v_cache, r.page_table, r.seq_lens_t)
+    out = torch.empty((r.B, r.Hq, r.D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(f, n):
+        for _ in range(warmup):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize(dev)
+        e0.record(stream)
+        for _ in range(n):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) * 1e-3 / n
+
+    t_q = timed(lambda: ubs.quantize_kv_int4(r.k_cache, r.v_cache, r.page_table, r.seq_lens_t,
+                                             out=(kc, vc, kp, vp)), max(1, steps // 4))
+    t_d = timed(lambda: ubs.sparse_decode_int4(r.q, kc, vc, kp, vp, r.page_table, r.seq_lens_t, r.head_kind, sel,
+                                               num, r.sink_tokens, r.local_tokens, r.sm_scale, out=out), steps)
+    row4 = r.D // 2 + 4
+    tokens = sum(r.seq_lens) * r.Hkv
+    b_q = tokens * 2 * (r.D * 2 + row4)
+    attended = 0
+    for b, L in enumerate(r.seq_lens):
+        for g in range(r.Hkv):
+            if r.head_kind[g]:
+                A = min(r.sink_tokens, L)
+                attended += A + L - max(A, L - r.local_tokens)
+            else:
+                attended += sum(min(r.P, L - j * r.P) for j in sel_pages[b][g])
+    q_bytes = r.B * r.Hq * r.D * 2
+    b_d = attended * 2 * row4 + q_bytes + r.B * r.Hq * r.D * 4
+    t_step = t_sel + t_d
+    del kc, vc, kp, vp
+    return {"quantize_kv_int4": {"ms": round(t_q * 1e3, 4), "bytes": b_q, "gbps": round(b_q / t_q / 1e9, 1),
+                                 "frac": round(b_q / t_q / 1e9 / PEAK_HBM_GBPS, 4)},
+            "sparse_decode_int4": {"ms": round(t_d * 1e3, 4), "bytes": b_d, "gbps": round(b_d / t_d / 1e9, 1),
+                                   "frac": round(b_d / t_d / 1e9 / PEAK_HBM_GBPS, 4)},
+            "step_select_plus_int4_decode": {"ms": round(t_step * 1e3, 4), "bytes": b_select + b_d,
+                                             "gbps": round((b_select + b_d) / t_step / 1e9, 1),
+                                             "frac": round((b_select + b_d) / t_step / 1e9 / PEAK_HBM_GBPS, 4)}}
 
 
 # ----------------------------------------------------------------------------- main
@@ -449,6 +581,7 @@ def main():
         "breakdown": breakdown,
     }
     breakdown["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
+    breakdown["decode_step_graph"] = decode_graph_step()
     if not args.no_ragged:
         breakdown["decode_ragged_step"] = ragged_decode_step(args.steps, args.warmup)
     if not args.no_cpu_baseline:
