@@ -9,7 +9,9 @@
  *
  *   sparse_prefill     block-sparse causal attention over a paged GQA KV cache;
  *                      each KV tile is computed whole or skipped whole, and
- *                      streaming heads keep only sink tiles plus a local window.
+ *                      streaming heads keep only sink tiles plus a local window
+ *                      (sparse_prefill_chunk: a chunk of query tiles;
+ *                      sparse_prefill_varlen: several sequences per call).
  *   build_page_bounds  per-page, per-channel key min/max (the page summary).
  *   select_pages       query-aware page scores and top-k selection.
  *   sparse_decode      GQA decode attention over the kept pages (dense heads)
@@ -124,6 +126,38 @@ int sparse_prefill_chunk(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const u
                          int32_t D, int32_t P, int32_t T, const uint8_t* head_kind /* host */,
                          const uint8_t* block_mask, int32_t sink_tiles, int32_t local_tiles,
                          float sm_scale, float* out, float* lse, hipStream_t stream);
+
+/*
+ * sparse_prefill_varlen -- sparse_prefill of B sequences in one call (batched
+ * prefill, the serving setting of the LServe paper; the variable-length layout
+ * of packed query rows).
+ *
+ * Sequence b has L_b = cu_seqlens[b+1] - cu_seqlens[b] tokens, all in the paged
+ * cache through page-table row b, and is computed exactly as sparse_prefill of that
+ * sequence alone; its query rows are rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of the
+ * packed q, out and lse.
+ *
+ *   q            bf16 [total_q][Hq][D]                 (packed rows)
+ *   k_cache,     bf16 [NP][Hkv][P][D]
+ *   v_cache
+ *   page_table   int32 [B][max_pages]                  (row b: sequence b)
+ *   cu_seqlens   int32 [B + 1], DEVICE memory: 0 = cu_seqlens[0] <= ... <=
+ *                cu_seqlens[B] = total_q; every L_b <= max_seqlen (host int)
+ *   block_mask   uint8 [B][Hq][nT_max][nT_max], nT_max = ceil(max_seqlen / T):
+ *                mask row i of head h of sequence b at [b][h][i][0 .. nT_b)
+ *   out          fp32 [total_q][Hq][D]                 (fully written)
+ *   lse          fp32 [Hq][total_q] or NULL
+ * The grid covers B * Hq * nT_max work-groups; those past a sequence's own tiles
+ * return at once. A sequence longer than max_seqlen is a caller error (its last
+ * rows are not computed). Supported: as sparse_prefill, with nT_max <= 4096 and
+ * max_pages * P >= max_seqlen.
+ */
+int sparse_prefill_varlen(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                          const int32_t* page_table, int32_t max_pages, const int32_t* cu_seqlens, int32_t B,
+                          int32_t max_seqlen, int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                          int32_t T, const uint8_t* head_kind /* host */, const uint8_t* block_mask,
+                          int32_t sink_tiles, int32_t local_tiles, float sm_scale, float* out, float* lse,
+                          hipStream_t stream);
 
 /*
  * build_page_bounds -- the per-page key summary used to score pages.

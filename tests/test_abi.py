@@ -293,3 +293,32 @@ def _decode4(**kw):
 ])
 def test_decode_int4_validation(kw, code):
     assert _decode4(**kw) == code
+
+
+def _varlen(**kw):
+    a = dict(q=A, k=A, v=A, pt=A, maxp=16, cu=A, B=3, maxs=1000, tot=2000, Hq=8, Hkv=8, D=128, P=64, T=128,
+             kind=KIND, mask=A, sink=1, local=4, scale=0.1, out=A, lse=NULL, stream=NULL)
+    a.update(kw)
+    return ubs.load().sparse_prefill_varlen(a["q"], a["k"], a["v"], a["pt"], a["maxp"], a["cu"], a["B"], a["maxs"],
+                                            a["tot"], a["Hq"], a["Hkv"], a["D"], a["P"], a["T"], a["kind"],
+                                            a["mask"], a["sink"], a["local"], a["scale"], a["out"], a["lse"],
+                                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,frag", [
+    (dict(T=32), -2, "T=32"),
+    (dict(D=96), -2, "D=96"),
+    (dict(maxp=10), -1, "cannot hold"),
+    (dict(cu=None), -1, "non-NULL"),
+    (dict(mask=None), -1, "block_mask"),
+    (dict(B=-1), -1, "B=-1"),
+    (dict(out=A + 4), -1, "aligned"),
+])
+def test_prefill_varlen_validation(kw, code, frag):
+    assert _varlen(**kw) == code
+    assert frag in _err()
+
+
+def test_prefill_varlen_nothing_to_do():
+    assert _varlen(B=0, q=None, k=None, v=None, pt=None, cu=None, mask=None, out=None) == 0
+    assert _varlen(tot=0, q=None, k=None, v=None, pt=None, cu=None, mask=None, out=None) == 0

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libubs.so")
 
 UBS_OK = 0
 ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
-EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
+EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "sparse_prefill_varlen", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
             "append_kv", "quantize_kv_int4", "sparse_decode_int4",
             "ubs_last_error", "ubs_version")
@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
         lib.sparse_prefill_chunk.restype = ctypes.c_int
         lib.sparse_prefill_chunk.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _i, _f, _p, _p,
                                              _p]
+        lib.sparse_prefill_varlen.restype = ctypes.c_int
+        lib.sparse_prefill_varlen.argtypes = [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _i, _i,
+                                              _f, _p, _p, _p]
         lib.build_page_bounds.restype = ctypes.c_int
         lib.build_page_bounds.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p]
         lib.ubs_select_workspace_size.restype = _sz
@@ -175,6 +178,50 @@ def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
                             _kinds(head_kind), _ptr(block_mask), sink_tiles, local_tiles, float(sm_scale),
                             _ptr(out), _ptr(lse), _stream(dev))
     _check("sparse_prefill", rc)
+    return (out, lse) if return_lse else out
+
+
+def sparse_prefill_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          page_table: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                          head_kind: Sequence[int], block_mask: Optional[torch.Tensor], sink_tiles: int,
+                          local_tiles: int, T: int, sm_scale: float, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, return_lse: bool = False):
+    """Block-sparse / streaming prefill of B sequences in one call (see include/ubs.h).
+
+    q bf16 [total_q, Hq, D] (packed rows); page_table int32 [B, max_pages]; cu_seqlens int32
+    [B + 1] on the GPU; max_seqlen >= every length; block_mask uint8 [B, Hq, nT_max, nT_max]
+    with nT_max = ceil(max_seqlen / T). Returns out fp32 [total_q, Hq, D] (and lse fp32
+    [Hq, total_q] with return_lse).
+    """
+    lib = load()
+    total_q, Hq, D = q.shape
+    NP, Hkv, P, D2 = k_cache.shape
+    B, max_pages = page_table.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(v_cache, "v_cache", torch.bfloat16, shape=k_cache.shape, device=dev)
+    _need(page_table, "page_table", torch.int32, device=dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, shape=(B + 1,), device=dev)
+    if D2 != D:
+        raise ValueError("q and k_cache head dims differ")
+    if len(head_kind) != Hkv:
+        raise ValueError("head_kind must have one entry per KV head")
+    nTm = (max_seqlen + T - 1) // T
+    if block_mask is not None:
+        _need(block_mask, "block_mask", torch.uint8, shape=(B, Hq, nTm, nTm), device=dev)
+    if out is None:
+        out = torch.empty((total_q, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, shape=(total_q, Hq, D), device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(Hq, total_q), device=dev)
+    rc = lib.sparse_prefill_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), max_pages,
+                                   _ptr(cu_seqlens), B, int(max_seqlen), total_q, Hq, Hkv, D, P, T,
+                                   _kinds(head_kind), _ptr(block_mask), sink_tiles, local_tiles, float(sm_scale),
+                                   _ptr(out), _ptr(lse), _stream(dev))
+    _check("sparse_prefill_varlen", rc)
     return (out, lse) if return_lse else out
 
 

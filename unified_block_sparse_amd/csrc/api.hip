@@ -143,6 +143,68 @@ int sparse_prefill_chunk(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const u
   return hip_status(ubs::launch_prefill(a, stream), "sparse_prefill launch");
 }
 
+int sparse_prefill_varlen(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                          const int32_t* page_table, int32_t max_pages, const int32_t* cu_seqlens, int32_t B,
+                          int32_t max_seqlen, int32_t total_q, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                          int32_t T, const uint8_t* head_kind, const uint8_t* block_mask, int32_t sink_tiles,
+                          int32_t local_tiles, float sm_scale, float* out, float* lse, hipStream_t stream) {
+  int rc = common_heads(Hq, Hkv, D);
+  if (rc) return rc;
+  REQUIRE(B >= 0 && max_seqlen >= 0 && total_q >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT,
+          "B=%d, max_seqlen=%d, total_q=%d, max_pages=%d must be >= 0", B, max_seqlen, total_q, max_pages);
+  REQUIRE(T == 64 || T == 128, UBS_ERR_UNSUPPORTED, "T=%d (supported: 64, 128)", T);
+  REQUIRE(P > 0, UBS_ERR_INVALID_ARGUMENT, "P=%d must be positive", P);
+  REQUIRE(pow2(P) && P >= 16 && P <= 4096, UBS_ERR_UNSUPPORTED, "P=%d (supported: powers of two 16..4096)", P);
+  REQUIRE(Hq <= ubs::kMaxQHeads, UBS_ERR_UNSUPPORTED, "Hq=%d above %d", Hq, ubs::kMaxQHeads);
+  REQUIRE(sink_tiles >= 0 && local_tiles >= 0, UBS_ERR_INVALID_ARGUMENT,
+          "sink_tiles=%d, local_tiles=%d must be >= 0", sink_tiles, local_tiles);
+  REQUIRE(sm_scale == sm_scale, UBS_ERR_INVALID_ARGUMENT, "sm_scale is NaN");
+  REQUIRE((int64_t)max_pages * P >= max_seqlen, UBS_ERR_INVALID_ARGUMENT,
+          "max_pages=%d pages of %d tokens cannot hold max_seqlen=%d", max_pages, P, max_seqlen);
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+  if (rc) return rc;
+  if (B == 0 || max_seqlen == 0 || total_q == 0) return ok();
+  REQUIRE(q && k_cache && v_cache && page_table && cu_seqlens && out, UBS_ERR_INVALID_ARGUMENT,
+          "q, k_cache, v_cache, page_table, cu_seqlens and out must be non-NULL");
+  REQUIRE(dense.n == 0 || block_mask, UBS_ERR_INVALID_ARGUMENT, "block_mask is NULL but a KV head is dense");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out), UBS_ERR_INVALID_ARGUMENT,
+          "q, k_cache, v_cache and out must be 16-byte aligned");
+  const int64_t nTm = (max_seqlen + T - 1) / T;
+  REQUIRE(nTm <= ubs::kMaxTileList, UBS_ERR_UNSUPPORTED, "max_seqlen=%d spans %lld tiles of %d (at most %d)",
+          max_seqlen, (long long)nTm, T, ubs::kMaxTileList);
+  REQUIRE((int64_t)B * Hq * nTm < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large",
+          (long long)((int64_t)B * Hq * nTm));
+  ubs::PrefillArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_table = page_table;
+  a.block_mask = block_mask;
+  a.L = 0;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.D = D;
+  a.P = P;
+  a.T = T;
+  a.q_tile0 = 0;
+  a.cu_seqlens = cu_seqlens;
+  a.n_seq = B;
+  a.pt_stride = max_pages;
+  a.nT_max = (int)nTm;
+  a.total_q = total_q;
+  a.log2_P = __builtin_ctz((unsigned)P);
+  a.sink_tiles = sink_tiles;
+  a.local_tiles = local_tiles;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.lse = lse;
+  a.dense_kv_mask = ~smask & (Hkv == 64 ? ~0ull : ((1ull << Hkv) - 1));
+  a.n_dense_kv = dense.n;
+  return hip_status(ubs::launch_prefill(a, stream), "sparse_prefill_varlen launch");
+}
+
 int sparse_prefill(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
                    const int32_t* page_table, int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                    int32_t T, const uint8_t* head_kind, const uint8_t* block_mask, int32_t sink_tiles,

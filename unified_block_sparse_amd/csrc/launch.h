@@ -94,6 +94,11 @@ struct PrefillArgs {
   const uint8_t* block_mask;
   int L, Hq, Hkv, D, P, T, sink_tiles, local_tiles;
   int q_tile0;             // first query tile of the call (a chunk: tiles q_tile0 .. nT-1)
+  // several sequences (cu_seqlens != nullptr): sequence b is rows cu_seqlens[b] ..
+  // cu_seqlens[b+1]-1 of q / out / lse, page-table row b (pt_stride entries), mask
+  // block b of [Hq][nT_max][nT_max]; L and q_tile0 are unused
+  const int32_t* cu_seqlens;
+  int n_seq, pt_stride, nT_max, total_q;
   int log2_P;
   float sm_scale;
   uint64_t dense_kv_mask;  // bit g set: KV head g is dense

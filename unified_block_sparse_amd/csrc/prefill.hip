@@ -119,14 +119,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (and known to be)
-  const int L = a.L;
   const int G = a.Hq / a.Hkv;
-  const int nT = (L + T - 1) / T;
-  // query tiles of this call: q_tile0 .. nT-1 (a chunk of the sequence; q, out, lse and
-  // the mask rows hold those tiles only)
-  const int qt0 = a.q_tile0;
-  const int nQ = nT - qt0;
-  const int q0 = qt0 * T;
 
   // ---- work item: XCD-aware renumbering of the block index (blocks go to XCDs
   // round-robin), then dense heads first, query tiles from the last to the first,
@@ -143,6 +136,38 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
       w = b;
     }
   }
+  // ---- the sequence. One call, one sequence: q, out, lse and the mask rows hold query
+  // tiles q_tile0 .. nT-1 of it (a chunk). Several sequences: the items of sequence b
+  // are w in [b, b+1) * Hq * nT_max, its rows start at row cu_seqlens[b] of q, out and
+  // lse, and items past its own tiles have nothing to do.
+  int L, qt0, q_off, lse_stride, m_rows, m_stride;
+  const int32_t* __restrict__ ptab_v;
+  const uint8_t* mask_base;
+  if (a.cu_seqlens) {
+    const int per = a.Hq * a.nT_max;
+    const int bs = w / per;
+    w -= bs * per;
+    q_off = a.cu_seqlens[bs];
+    L = a.cu_seqlens[bs + 1] - q_off;
+    if (w >= a.Hq * ((L + T - 1) / T)) return;   // (whole work-group, before any barrier)
+    qt0 = 0;
+    lse_stride = a.total_q;
+    m_rows = m_stride = a.nT_max;
+    ptab_v = a.page_table + (int64_t)bs * a.pt_stride;
+    mask_base = a.block_mask + (int64_t)bs * a.Hq * a.nT_max * a.nT_max;
+  } else {
+    L = a.L;
+    qt0 = a.q_tile0;
+    q_off = -qt0 * T;
+    lse_stride = L - qt0 * T;
+    m_rows = (L + T - 1) / T - qt0;
+    m_stride = (L + T - 1) / T;
+    ptab_v = a.page_table;
+    mask_base = a.block_mask;
+  }
+  const int nT = (L + T - 1) / T;
+  const int nQ = nT - qt0;
+
   // query heads in order: the G heads of each dense KV head (ascending), then those of
   // each streaming KV head; the k-th KV head of a kind is the k-th set bit of its mask
   const uint64_t dmask = a.dense_kv_mask;
@@ -175,7 +200,6 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   // physical chunk s%CPR, i.e. logical chunk (s%CPR) ^ swizzle(row).
   const int lp = a.log2_P;
   const int pmask = (1 << lp) - 1;
-  const int32_t* __restrict__ ptab_v = a.page_table;
   // first row (sequence position) of 16-row block b of step half hf of tile j
   auto row0 = [&](int j, int hf, int b) __attribute__((always_inline)) { return j * T + hf * SK + wave * RW + b * 16; };
   // Each 16-row block goes through its own buffer resource (wave-uniform base: the
@@ -224,7 +248,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   // ---- kept KV tiles, ascending, as a list in LDS
   int n_tiles;
   if (!streaming) {
-    const uint8_t* mrow = a.block_mask + ((int64_t)h * nQ + (i - qt0)) * nT;
+    const uint8_t* mrow = mask_base + ((int64_t)h * m_rows + (i - qt0)) * m_stride;
     uint8_t flag[MB];
     int cnt = 0;
 #pragma unroll
@@ -270,7 +294,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   const int qrow = i * T + qi;
   bf16x8 qb[QK];
   {
-    const uint16_t* qp = a.q + ((int64_t)(qrow - q0) * a.Hq + h) * D + q2 * (D / 2);
+    const uint16_t* qp = a.q + ((int64_t)(qrow + q_off) * a.Hq + h) * D + q2 * (D / 2);
 #pragma unroll
     for (int kk = 0; kk < QK; ++kk) qb[kk] = as_bf16x8(qrow < L ? ld16(qp + kk * 8) : u32x4{0, 0, 0, 0});
   }
@@ -550,7 +574,7 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
   const float l_row = l_run + shfl_xor(l_run, 32);
   const float inv = l_row > 0.f ? 1.0f / l_row : 0.f;
   if (qrow < L) {
-    float* op = a.out + ((int64_t)(qrow - q0) * a.Hq + h) * D + 4 * q2;
+    float* op = a.out + ((int64_t)(qrow + q_off) * a.Hq + h) * D + 4 * q2;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
@@ -561,13 +585,13 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
         *reinterpret_cast<f32x4*>(op + cb * 32 + 8 * jj) = v;
       }
     if (q2 == 0 && a.lse)
-      a.lse[(int64_t)h * (L - q0) + (qrow - q0)] = l_row > 0.f ? (m_run * c2 + __log2f(l_row)) * kLn2 : kNegInf;
+      a.lse[(int64_t)h * lse_stride + (qrow + q_off)] = l_row > 0.f ? (m_run * c2 + __log2f(l_row)) * kLn2 : kNegInf;
   }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const int nT = (a.L + a.T - 1) / a.T;
-  const int64_t blocks = (int64_t)(nT - a.q_tile0) * a.Hq;
+  const int64_t blocks = a.cu_seqlens ? (int64_t)a.n_seq * a.Hq * a.nT_max : (int64_t)(nT - a.q_tile0) * a.Hq;
   if (blocks == 0) return hipSuccess;
 #define UBS_PREFILL(TT, DD)                                                                    \
   if (a.T == TT && a.D == DD) {                                                                \
