@@ -246,6 +246,61 @@ def mask_estimation(c, steps: int, warmup: int):
             "bytes": nbytes, "gbps": round(nbytes / t / 1e9, 1), "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4)}
 
 
+# ----------------------------------------------------------------------------- batched prefill
+
+def varlen_prefill(steps: int, warmup: int):
+    """sparse_prefill_varlen on 8 sequences of 4K-16K tokens (seeded lengths) with the
+    Llama-3-8B layer's heads and mask rule (planted keys, mean-pooled top-30% rows for the
+    dense heads, sink 1 + local 8 tiles for the streaming ones), packed into one call over
+    one paged cache. Work = kept tiles x 4 T^2 D, as for the single-sequence prefill."""
+    import numpy as np
+    import torch
+    import unified_block_sparse_amd as ubs
+    from workloads import cases
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(1006)
+    lens = [int(x) * 128 for x in rng.integers(32, 129, size=8)]
+    hk = [0, 0, 0, 0, 1, 1, 1, 1]
+    seqs = [cases.make_prefill(f"vb{b}", L, 32, 8, 128, 128, 64, hk, 1, 8, "meanpool", 1100 + b, dev, planted=True)
+            for b, L in enumerate(lens)]
+    kept = sum(kept_tile_count(c) for c in seqs)
+    flops = sum(prefill_flops(c, kept_tile_count(c)) for c in seqs)
+    offs, n = [], 0
+    for c in seqs:
+        offs.append(n)
+        n += c.k_cache.shape[0]
+    k_all = torch.cat([c.k_cache for c in seqs])
+    v_all = torch.cat([c.v_cache for c in seqs])
+    max_pages = max((L + 63) // 64 for L in lens)
+    pt = torch.zeros((len(seqs), max_pages), dtype=torch.int32, device=dev)
+    for b, c in enumerate(seqs):
+        pt[b, :c.page_table.numel()] = c.page_table + offs[b]
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=dev)
+    q = torch.cat([c.q for c in seqs])
+    nTm = max(lens) // 128
+    mask = torch.zeros((len(seqs), 32, nTm, nTm), dtype=torch.uint8, device=dev)
+    for b, c in enumerate(seqs):
+        mask[b, :, :c.nT, :c.nT] = c.block_mask
+    out = torch.empty((sum(lens), 32, 128), dtype=torch.float32, device=dev)
+    del seqs
+    f = lambda: ubs.sparse_prefill_varlen(q, k_all, v_all, pt, cu, max(lens), hk, mask, 1, 8, 128,
+                                          1.0 / math.sqrt(128), out=out)
+    for _ in range(warmup):
+        f()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    e0.record(stream)
+    for _ in range(steps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    t = e0.elapsed_time(e1) * 1e-3 / steps
+    return {"workload": f"8 sequences, lengths {lens}, Hq=32, Hkv=8, D=128, T=128, half KV heads streaming",
+            "ms": round(t * 1e3, 4), "kept_tiles": kept, "tflop": round(flops / 1e12, 4),
+            "tflops": round(flops / t / 1e12, 2), "frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 # ----------------------------------------------------------------------------- graph-replayed decode
 
 def decode_graph_step(R: int = 24, replays: int = 10):
@@ -582,6 +637,7 @@ def main():
     }
     breakdown["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
     breakdown["decode_step_graph"] = decode_graph_step()
+    breakdown["sparse_prefill_varlen"] = varlen_prefill(max(2, args.steps // 4), 2)
     if not args.no_ragged:
         breakdown["decode_ragged_step"] = ragged_decode_step(args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -136,20 +136,46 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
       w = b;
     }
   }
-  // ---- the sequence. One call, one sequence: q, out, lse and the mask rows hold query
-  // tiles q_tile0 .. nT-1 of it (a chunk). Several sequences: the items of sequence b
-  // are w in [b, b+1) * Hq * nT_max, its rows start at row cu_seqlens[b] of q, out and
-  // lse, and items past its own tiles have nothing to do.
+  // ---- the work item (sequence, query head h, query tile i). Query heads in order: the
+  // G heads of each dense KV head (ascending), then those of each streaming KV head; the
+  // k-th KV head of a kind is the k-th set bit of its mask. One sequence per call: q,
+  // out, lse and the mask rows hold query tiles q_tile0 .. nT-1 of it (a chunk); items go
+  // dense heads first, query tiles from the last to the first. Several sequences: the
+  // same order over the whole batch (dense heads, then tile index from the largest,
+  // then sequence, then head), so that every sequence's long rows start early; items
+  // past a sequence's own tiles have nothing to do. Sequence b's rows start at row
+  // cu_seqlens[b] of q, out and lse.
+  const uint64_t dmask = a.dense_kv_mask;
+  const uint64_t smask = ~dmask & (a.Hkv == 64 ? ~0ull : ((1ull << a.Hkv) - 1));
+  auto nth_bit = [](uint64_t m, int k) __attribute__((always_inline)) {
+    for (; k > 0; --k) m &= m - 1;
+    return __builtin_ctzll(m);
+  };
+  const int nd = a.n_dense_kv * G;
+  const int ns = a.Hq - nd;
   int L, qt0, q_off, lse_stride, m_rows, m_stride;
   const int32_t* __restrict__ ptab_v;
   const uint8_t* mask_base;
+  bool streaming;
+  int h, i, x;
   if (a.cu_seqlens) {
-    const int per = a.Hq * a.nT_max;
-    const int bs = w / per;
-    w -= bs * per;
+    const int nb = a.n_seq;
+    int bs;
+    if (w < nd * a.nT_max * nb) {
+      streaming = false;
+      i = a.nT_max - 1 - w / (nd * nb);
+      bs = (w % (nd * nb)) / nd;
+      x = w % nd;
+    } else {
+      const int w2 = w - nd * a.nT_max * nb;
+      streaming = true;
+      i = a.nT_max - 1 - w2 / (ns * nb);
+      bs = (w2 % (ns * nb)) / ns;
+      x = w2 % ns;
+    }
     q_off = a.cu_seqlens[bs];
     L = a.cu_seqlens[bs + 1] - q_off;
-    if (w >= a.Hq * ((L + T - 1) / T)) return;   // (whole work-group, before any barrier)
+    if (i * T >= L) return;   // (whole work-group, before any barrier)
     qt0 = 0;
     lse_stride = a.total_q;
     m_rows = m_stride = a.nT_max;
@@ -159,39 +185,26 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
     L = a.L;
     qt0 = a.q_tile0;
     q_off = -qt0 * T;
+    const int nT1 = (L + T - 1) / T;
     lse_stride = L - qt0 * T;
-    m_rows = (L + T - 1) / T - qt0;
-    m_stride = (L + T - 1) / T;
+    m_rows = nT1 - qt0;
+    m_stride = nT1;
     ptab_v = a.page_table;
     mask_base = a.block_mask;
+    const int nQ1 = nT1 - qt0;
+    if (w < nd * nQ1) {
+      streaming = false;
+      i = nT1 - 1 - w / nd;
+      x = w % nd;
+    } else {
+      const int w2 = w - nd * nQ1;
+      streaming = true;
+      i = nT1 - 1 - w2 / ns;
+      x = w2 % ns;
+    }
   }
+  h = nth_bit(streaming ? smask : dmask, x / G) * G + x % G;
   const int nT = (L + T - 1) / T;
-  const int nQ = nT - qt0;
-
-  // query heads in order: the G heads of each dense KV head (ascending), then those of
-  // each streaming KV head; the k-th KV head of a kind is the k-th set bit of its mask
-  const uint64_t dmask = a.dense_kv_mask;
-  const uint64_t smask = ~dmask & (a.Hkv == 64 ? ~0ull : ((1ull << a.Hkv) - 1));
-  auto nth_bit = [](uint64_t m, int k) __attribute__((always_inline)) {
-    for (; k > 0; --k) m &= m - 1;
-    return __builtin_ctzll(m);
-  };
-  const int nd = a.n_dense_kv * G;
-  bool streaming;
-  int h, i;
-  if (w < nd * nQ) {
-    streaming = false;
-    i = nT - 1 - w / nd;
-    const int x = w % nd;
-    h = nth_bit(dmask, x / G) * G + x % G;
-  } else {
-    const int w2 = w - nd * nQ;
-    const int ns = a.Hq - nd;
-    streaming = true;
-    i = nT - 1 - w2 / ns;
-    const int x = w2 % ns;
-    h = nth_bit(smask, x / G) * G + x % G;
-  }
   const int g = h / G;
 
   // ---- direct-to-LDS loader. Wave w loads rows w*RW .. w*RW + RW - 1 of every step's
