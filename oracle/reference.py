@@ -409,12 +409,17 @@ def decode_ref(q_bits, k_cache_bits, v_cache_bits, page_table, seq_lens, Hq: int
 # with page sparsity, cutting the bytes of every page that is read. The pages give no
 # format; the reading taken here: every (token, KV head) row of D channels is quantized
 # on its own, asymmetrically, to 4-bit codes n in [0, 15] with x ~ n * scale + zero;
-# scale and zero are stored as fp16, and two codes share a byte (channel 2i in the low
-# nibble, 2i+1 in the high one). The code is an integer chosen by floating point, so it
-# is taken in fp32, as the GPU takes it:
+# scale and zero are stored as fp16. The code is an integer chosen by floating point, so
+# it is taken in fp32, as the GPU takes it:
 #   lo, hi = min_c x_c, max_c x_c;  scale16 = fp16((hi - lo) / 15);  zero16 = fp16(lo)
 #   n_c = clamp(rint((x_c - zero) / scale), 0, 15), all in fp32 with the fp16 values
 #   widened; a row with scale16 == 0 has every code 0 (and dequantizes to zero16).
+# Storage of the codes, in 32-bit little-endian words of 8 codes: code k of a group of 8
+# goes to nibble k/2 of the word's low half (k even) or of its high half (k odd), so the
+# word's bytes are (n0 | n2 << 4, n4 | n6 << 4, n1 | n3 << 4, n5 | n7 << 4). K pages hold
+# each token's row as D/8 such words, channels in order ([NP][Hkv][P][D/2] bytes). V pages
+# are channel-major: for each channel, the P tokens of the page as P/8 words
+# ([NP][Hkv][D][P/2] bytes). Params: [NP][Hkv][P][2] fp16 (scale, zero) for K and for V.
 
 def quantize_int4_ref(x_bits) -> Tuple[np.ndarray, np.ndarray]:
     """Codes [..., D] (uint8 in [0, 15]) and fp16 bit patterns [..., 2] = (scale, zero)
@@ -434,17 +439,21 @@ def quantize_int4_ref(x_bits) -> Tuple[np.ndarray, np.ndarray]:
 
 
 def pack_int4(codes) -> np.ndarray:
-    """Two codes per byte: channel 2i in the low nibble, 2i + 1 in the high nibble."""
+    """Codes [..., 8m] -> bytes [..., 4m]: each group of 8 codes n0..n7 as the bytes
+    (n0 | n2 << 4, n4 | n6 << 4, n1 | n3 << 4, n5 | n7 << 4)."""
     c = np.asarray(codes, dtype=np.uint8)
-    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    g = c.reshape(c.shape[:-1] + (c.shape[-1] // 8, 8))
+    out = np.stack([g[..., 0] | (g[..., 2] << 4), g[..., 4] | (g[..., 6] << 4),
+                    g[..., 1] | (g[..., 3] << 4), g[..., 5] | (g[..., 7] << 4)], axis=-1)
+    return out.reshape(c.shape[:-1] + (c.shape[-1] // 2,)).astype(np.uint8)
 
 
 def unpack_int4(packed) -> np.ndarray:
     p = np.asarray(packed, dtype=np.uint8)
-    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
-    out[..., 0::2] = p & 0xF
-    out[..., 1::2] = p >> 4
-    return out
+    w = p.reshape(p.shape[:-1] + (p.shape[-1] // 4, 4))
+    g = np.stack([w[..., 0] & 0xF, w[..., 2] & 0xF, w[..., 0] >> 4, w[..., 2] >> 4,
+                  w[..., 1] & 0xF, w[..., 3] & 0xF, w[..., 1] >> 4, w[..., 3] >> 4], axis=-1)
+    return g.reshape(p.shape[:-1] + (2 * p.shape[-1],)).astype(np.uint8)
 
 
 def dequant_int4_ref(packed, params) -> np.ndarray:
@@ -453,41 +462,54 @@ def dequant_int4_ref(packed, params) -> np.ndarray:
     return unpack_int4(packed).astype(np.float64) * pr[..., 0:1] + pr[..., 1:2]
 
 
-def quantize_cache_int4_ref(cache_bits, page_table, seq_lens, P: int):
-    """INT4 pages of the valid tokens of every sequence: (packed [NP, Hkv, P, D/2] uint8,
-    params [NP, Hkv, P, 2] uint16) and a mask [NP, P] of the rows that were written
-    (rows of other pages and past a sequence's length stay zero)."""
-    C = np.asarray(cache_bits, dtype=np.uint16)
-    NP, Hkv, _, D = C.shape
-    packed = np.zeros((NP, Hkv, P, D // 2), dtype=np.uint8)
-    params = np.zeros((NP, Hkv, P, 2), dtype=np.uint16)
+def quantize_cache_int4_ref(k_bits, v_bits, page_table, seq_lens, P: int):
+    """INT4 pages of the valid tokens of every sequence, in the storage above:
+    (k_codes [NP, Hkv, P, D/2], v_codes [NP, Hkv, D, P/2], k_params, v_params
+    [NP, Hkv, P, 2]) and a mask [NP, P] of the token rows that were written. K codes and
+    both params are written for valid tokens only; a V word is written when one of its 8
+    tokens is valid, with code 0 for the others. Everything else stays zero."""
+    K = np.asarray(k_bits, dtype=np.uint16)
+    V = np.asarray(v_bits, dtype=np.uint16)
+    NP, Hkv, _, D = K.shape
+    kq = np.zeros((NP, Hkv, P, D // 2), dtype=np.uint8)
+    vq = np.zeros((NP, Hkv, D, P // 2), dtype=np.uint8)
+    kp = np.zeros((NP, Hkv, P, 2), dtype=np.uint16)
+    vp = np.zeros((NP, Hkv, P, 2), dtype=np.uint16)
     written = np.zeros((NP, P), dtype=bool)
     pt = np.asarray(page_table)
     for b, L in enumerate(int(x) for x in seq_lens):
         for j in range((L + P - 1) // P):
             pg = int(pt[b, j])
             n = min(P, L - j * P)
-            codes, pr = quantize_int4_ref(C[pg, :, :n, :])
-            packed[pg, :, :n] = pack_int4(codes)
-            params[pg, :, :n] = pr
+            c, pr = quantize_int4_ref(K[pg, :, :n, :])
+            kq[pg, :, :n] = pack_int4(c)
+            kp[pg, :, :n] = pr
+            c, pr = quantize_int4_ref(V[pg, :, :n, :])
+            vp[pg, :, :n] = pr
+            ct = np.zeros((Hkv, D, P), dtype=np.uint8)
+            ct[:, :, :n] = c.transpose(0, 2, 1)
+            nw = (n + 7) // 8                                  # words touched per channel
+            vq[pg, :, :, :4 * nw] = pack_int4(ct)[:, :, :4 * nw]
             written[pg, :n] = True
-    return packed, params, written
+    return kq, vq, kp, vp, written
 
 
-def decode_int4_ref(q_bits, k_packed, v_packed, k_params, v_params, page_table, seq_lens, Hq: int,
+def decode_int4_ref(q_bits, k_codes, v_codes, k_params, v_params, page_table, seq_lens, Hq: int,
                     Hkv: int, P: int, head_kind, selected: Dict[Tuple[int, int], Sequence[int]],
                     sink_tokens: int, local_tokens: int, sm_scale: float,
                     batches: Optional[Sequence[int]] = None):
-    """decode_ref over INT4 pages: the same key sets, with K and V rows the fp64
-    dequantization of their codes."""
-    Kq, Vq = np.asarray(k_packed), np.asarray(v_packed)
+    """decode_ref over INT4 pages (storage above): the same key sets, with K and V rows the
+    fp64 dequantization of their codes."""
+    Kq, Vq = np.asarray(k_codes), np.asarray(v_codes)
     Kp, Vp = np.asarray(k_params), np.asarray(v_params)
+    Vrows = unpack_int4(Vq).transpose(0, 1, 3, 2)               # [NP, Hkv, P, D] codes
 
     def rows(b, g, page_row, L, keys):
+        vc = tokens_of_sequence(Vrows, page_row, L, P, keys)[:, g, :].astype(np.float64)
+        vpr = tokens_of_sequence(Vp, page_row, L, P, keys)[:, g, :].view(np.float16).astype(np.float64)
         return (dequant_int4_ref(tokens_of_sequence(Kq, page_row, L, P, keys)[:, g, :],
                                  tokens_of_sequence(Kp, page_row, L, P, keys)[:, g, :]),
-                dequant_int4_ref(tokens_of_sequence(Vq, page_row, L, P, keys)[:, g, :],
-                                 tokens_of_sequence(Vp, page_row, L, P, keys)[:, g, :]))
+                vc * vpr[:, 0:1] + vpr[:, 1:2])
 
     return _decode_over(bf16_to_f64(q_bits), rows, 2 * Kq.shape[-1], page_table, seq_lens, Hq, Hkv, P,
                         head_kind, selected, sink_tokens, local_tokens, sm_scale, batches)

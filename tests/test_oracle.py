@@ -521,14 +521,15 @@ def _f32_to_bf16_bits(x) -> np.ndarray:
 
 def test_int4_hand_example_codes_bytes_and_params():
     """Row 0..15: lo 0, hi 15, scale (15 - 0)/15 = 1 -> fp16 0x3C00, zero fp16(0) = 0x0000;
-    codes equal the values; bytes pair channel 2i (low nibble) with 2i+1 (high nibble):
-    (0,1) -> 0x10, (2,3) -> 0x32, ..., (14,15) -> 0xFE."""
+    codes equal the values; each group of 8 codes n0..n7 is stored as the bytes
+    (n0 | n2 << 4, n4 | n6 << 4, n1 | n3 << 4, n5 | n7 << 4): 0x20 0x64 0x31 0x75 for 0..7,
+    0xA8 0xEC 0xB9 0xFD for 8..15."""
     x = _f32_to_bf16_bits(np.arange(16, dtype=np.float32))
     codes, params = oracle.quantize_int4_ref(x)
     assert codes.tolist() == list(range(16))
     assert params.tolist() == [0x3C00, 0x0000]
     packed = oracle.pack_int4(codes)
-    assert packed.tolist() == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    assert packed.tolist() == [0x20, 0x64, 0x31, 0x75, 0xA8, 0xEC, 0xB9, 0xFD]
     assert np.array_equal(oracle.unpack_int4(packed), codes)
     assert np.array_equal(oracle.dequant_int4_ref(packed, params), np.arange(16, dtype=np.float64))
 
@@ -574,22 +575,34 @@ def test_int4_codes_are_nearest_and_error_bounded():
 
 
 def test_int4_cache_writes_valid_rows_only():
+    """K codes and both params exactly for the valid rows; V words (8 tokens of a channel)
+    exactly for the token groups holding a valid token, code 0 for the invalid tokens."""
     rng = np.random.default_rng(7)
     P, Hkv, D = 16, 2, 8
     lens = [5, 40]
     pt = np.array([[3, 0, 0], [1, 4, 2]], dtype=np.int32)
-    cache = ((rng.standard_normal((5, Hkv, P, D)).astype(np.float32).view(np.uint32) + 0x8000) >> 16)
-    cache = cache.astype(np.uint16)
-    packed, params, written = oracle.quantize_cache_int4_ref(cache, pt, lens, P)
+    mk = lambda: ((rng.standard_normal((5, Hkv, P, D)).astype(np.float32).view(np.uint32) + 0x8000) >> 16
+                  ).astype(np.uint16)
+    kb, vb = mk(), mk()
+    kq, vq, kp, vp, written = oracle.quantize_cache_int4_ref(kb, vb, pt, lens, P)
     want = np.zeros((5, P), dtype=bool)
     want[3, :5] = True
     want[1, :] = True
     want[4, :] = True
     want[2, :8] = True
     assert np.array_equal(written, want)
-    assert not packed.transpose(0, 2, 1, 3)[~want].any() and not params.transpose(0, 2, 1, 3)[~want].any()
-    c, p = oracle.quantize_int4_ref(cache[2, 1, 3])
-    assert np.array_equal(packed[2, 1, 3], oracle.pack_int4(c)) and np.array_equal(params[2, 1, 3], p)
+    for a in (kq, kp, vp):
+        assert not a.transpose(0, 2, 1, 3)[~want].any()
+    c, p = oracle.quantize_int4_ref(kb[2, 1, 3])
+    assert np.array_equal(kq[2, 1, 3], oracle.pack_int4(c)) and np.array_equal(kp[2, 1, 3], p)
+    # V of page 3 (5 valid tokens): channel-major, tokens 5..7 of the first word coded 0,
+    # the second word (tokens 8..15) untouched
+    c, p = oracle.quantize_int4_ref(vb[3, 0, :5])                       # [5 tokens, D]
+    ct = np.zeros((D, 8), dtype=np.uint8)
+    ct[:, :5] = c.T
+    assert np.array_equal(vq[3, 0, :, :4], oracle.pack_int4(ct)) and not vq[3, 0, :, 4:].any()
+    assert np.array_equal(vp[3, 0, :5], p)
+    assert np.array_equal(oracle.unpack_int4(vq[3, 0])[:, :5], c.T)
 
 
 def test_int4_decode_equals_bf16_decode_on_exactly_representable_rows():
@@ -609,8 +622,7 @@ def test_int4_decode_equals_bf16_decode_on_exactly_representable_rows():
     vals = (codes * step + off).astype(np.float32)
     kb, vb = _f32_to_bf16_bits(vals[:, :, :, 0]), _f32_to_bf16_bits(vals[:, :, :, 1])
     q = ((rng.standard_normal((B, Hq, D)).astype(np.float32).view(np.uint32) + 0x8000) >> 16).astype(np.uint16)
-    kq, kp, _ = oracle.quantize_cache_int4_ref(kb, pt, lens, P)
-    vq, vp, _ = oracle.quantize_cache_int4_ref(vb, pt, lens, P)
+    kq, vq, kp, vp, _ = oracle.quantize_cache_int4_ref(kb, vb, pt, lens, P)
     sel = {(0, 0): [0, 2], (1, 0): [1]}
     args = (pt, lens, Hq, Hkv, P, [0, 1], sel, 3, 7, 0.3)
     o1, l1 = oracle.decode_ref(q, kb, vb, *args)
