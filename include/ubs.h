@@ -265,15 +265,19 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
  *   scale = fp16((max_c x_c - min_c x_c) / 15), zero = fp16(min_c x_c)
  *   n_c   = clamp(rint((x_c - zero) / scale), 0, 15)  in fp32 (n = 0 if scale == 0)
  *   x_c  ~ n_c * scale + zero
- * Layout (same page indexing as the bf16 cache):
- *   codes  uint8  [NP][Hkv][P][D/2]: channel 2i in the low nibble of byte i,
- *                                     channel 2i+1 in its high nibble
- *   params uint16 [NP][Hkv][P][2]:   fp16 bits of (scale, zero)
+ * Storage (same page indexing as the bf16 cache). Codes sit 8 to a 32-bit
+ * little-endian word: code k of the 8 in nibble k/2 of the low half (k even) or of
+ * the high half (k odd), i.e. bytes (n0|n2<<4, n4|n6<<4, n1|n3<<4, n5|n7<<4).
+ *   k_codes uint8  [NP][Hkv][P][D/2]: each token's row, words of 8 channels
+ *   v_codes uint8  [NP][Hkv][D][P/2]: channel-major, for each channel the
+ *                                      page's tokens in words of 8 tokens
+ *   params  uint16 [NP][Hkv][P][2]:   fp16 bits of (scale, zero), K and V each
  * 68 bytes per row at D = 128 against 256 for bf16.
  *
  * quantize_kv_int4: the codes and params of every valid token (t < seq_lens[b])
- * of every sequence, every KV head, K and V; rows of other pages or past a
- * sequence's length are left as they were. Inputs are bf16 caches
+ * of every sequence, every KV head, K and V; K rows and params of other tokens are
+ * left as they were, and so are V words holding no valid token (the other tokens
+ * of a V word that is written get code 0). Inputs are bf16 caches
  * [NP][Hkv][P][D] (16-byte aligned); codes and params 4-byte aligned. Values
  * must be finite and their range / 15 must fit fp16.
  *

@@ -42,20 +42,27 @@ QUANT_CASES = [
 def test_quantize_int4_bit_exact(lens, Hkv, D, P):
     c = cases.make_decode("q4", lens, 2 * Hkv, Hkv, D, P, P, [0] * Hkv, P, 1, 1, 51, DEV, planted=True,
                           extra_pages=3)
-    sentinel = (torch.full(c.k_cache.shape[:3] + (D // 2,), 0xA5, dtype=torch.uint8, device=DEV),
-                torch.full(c.k_cache.shape[:3] + (D // 2,), 0x5A, dtype=torch.uint8, device=DEV),
+    NP = c.k_cache.shape[0]
+    sentinel = (torch.full((NP, Hkv, P, D // 2), 0xA5, dtype=torch.uint8, device=DEV),
+                torch.full((NP, Hkv, D, P // 2), 0x5A, dtype=torch.uint8, device=DEV),
                 torch.full(c.k_cache.shape[:3] + (2,), 0x1234, dtype=torch.int16, device=DEV),
                 torch.full(c.k_cache.shape[:3] + (2,), 0x4321, dtype=torch.int16, device=DEV))
     kc, vc, kp, vp = ubs.quantize_kv_int4(c.k_cache, c.v_cache, c.page_table, c.seq_lens_t, out=sentinel)
     _sync()
     pt = c.page_table.cpu().numpy()
-    for got_c, got_p, cache, fill_c, fill_p in ((kc, kp, c.k_cache, 0xA5, 0x1234), (vc, vp, c.v_cache, 0x5A, 0x4321)):
-        ref_c, ref_p, written = oracle.quantize_cache_int4_ref(bits(cache), pt, c.seq_lens, P)
-        gc = _u8(got_c).transpose(0, 2, 1, 3)           # [NP, P, Hkv, D/2]
-        gp = _u16(got_p).transpose(0, 2, 1, 3)
-        assert np.array_equal(gc[written], ref_c.transpose(0, 2, 1, 3)[written]), "codes differ"
-        assert np.array_equal(gp[written], ref_p.transpose(0, 2, 1, 3)[written]), "params differ"
-        assert np.all(gc[~written] == fill_c) and np.all(gp[~written] == fill_p), "rows outside the sequences touched"
+    rkq, rvq, rkp, rvp, written = oracle.quantize_cache_int4_ref(bits(c.k_cache), bits(c.v_cache), pt, c.seq_lens, P)
+    tr = lambda x: x.transpose(0, 2, 1, 3)               # [NP, P, Hkv, ...]
+    for got, ref, fill, what in ((_u8(kc), rkq, 0xA5, "k codes"), (_u16(kp), rkp, 0x1234, "k params"),
+                                 (_u16(vp), rvp, 0x4321, "v params")):
+        assert np.array_equal(tr(got)[written], tr(ref)[written]), f"{what} differ"
+        assert np.all(tr(got)[~written] == fill), f"{what}: rows outside the sequences touched"
+    # V words: written where a word holds a valid token, untouched elsewhere
+    gv = _u8(vc).reshape(NP, Hkv, D, P // 8, 4)
+    wv = written.reshape(NP, P // 8, 8).any(axis=2)      # [NP, words]
+    rv = rvq.reshape(NP, Hkv, D, P // 8, 4)
+    sel = np.broadcast_to(wv[:, None, None, :], gv.shape[:4])
+    assert np.array_equal(gv[sel], rv[sel]), "v codes differ"
+    assert np.all(gv[~sel] == 0x5A), "v words outside the sequences touched"
 
 
 DECODE4_CASES = [
@@ -82,8 +89,7 @@ def _sel_tensors(sel_o, B, Hkv, k):
 def test_decode_int4_matches_oracle(lens, Hq, Hkv, D, P, Lp, hk, budget, sink, local):
     c = cases.make_decode("d4", lens, Hq, Hkv, D, P, Lp, hk, budget, sink, local, 52, DEV, planted=True)
     pt = c.page_table.cpu().numpy()
-    kq, kp, _ = oracle.quantize_cache_int4_ref(bits(c.k_cache), pt, lens, P)
-    vq, vp, _ = oracle.quantize_cache_int4_ref(bits(c.v_cache), pt, lens, P)
+    kq, vq, kp, vp, _ = oracle.quantize_cache_int4_ref(bits(c.k_cache), bits(c.v_cache), pt, lens, P)
     sel_o, _ = oracle.select_ref(bits(c.q), bits(c.k_cache), pt, lens, Hq, Hkv, P, Lp, budget, hk)
     sel_t, num_t = _sel_tensors(sel_o, c.B, Hkv, budget // P)
     dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).view(dt).to(DEV)
@@ -126,12 +132,14 @@ def test_int4_ragged_sampled_sequences():
     kc, vc, kp, vp = ubs.quantize_kv_int4(c.k_cache, c.v_cache, c.page_table, c.seq_lens_t)
     _sync()
     qb, kb, vb, pt, lens = decode_subset(c, batches)
-    kq, kpr, _ = oracle.quantize_cache_int4_ref(kb, pt, lens, c.P)
-    vq, vpr, _ = oracle.quantize_cache_int4_ref(vb, pt, lens, c.P)
+    kq, vq, kpr, vpr, written = oracle.quantize_cache_int4_ref(kb, vb, pt, lens, c.P)
     pages = torch.tensor([int(c.page_table[b, j]) for b in batches for j in range((c.seq_lens[b] + c.P - 1) // c.P)],
                          device=DEV)
     assert np.array_equal(_u8(kc[pages]), kq) and np.array_equal(_u16(kp[pages]), kpr.view(np.uint16))
-    assert np.array_equal(_u8(vc[pages]), vq) and np.array_equal(_u16(vp[pages]), vpr.view(np.uint16))
+    wv = np.broadcast_to(written.reshape(-1, c.P // 8, 8).any(axis=2)[:, None, None, :],
+                         (len(pages), c.Hkv, c.D, c.P // 8))
+    gv = _u8(vc[pages]).reshape(len(pages), c.Hkv, c.D, c.P // 8, 4)
+    assert np.array_equal(gv[wv], vq.reshape(gv.shape)[wv]) and np.array_equal(_u16(vp[pages]), vpr.view(np.uint16))
     sel_o, _ = oracle.select_ref(qb, kb, pt, lens, c.Hq, c.Hkv, c.P, c.Lp, c.token_budget, c.head_kind)
     sel_t = torch.full((c.B, c.Hkv, c.k_pages), -1, dtype=torch.int32, device=DEV)
     num_t = torch.zeros((c.B, c.Hkv), dtype=torch.int32, device=DEV)

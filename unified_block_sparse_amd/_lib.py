@@ -334,9 +334,10 @@ def quantize_kv_int4(k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: t
     """INT4 pages of the valid tokens of every sequence (see include/ubs.h).
 
     k_cache, v_cache bf16 [NP, Hkv, P, D]; page_table int32 [B, max_pages]; seq_lens int32 [B].
-    Returns (k_codes, v_codes) uint8 [NP, Hkv, P, D/2] and (k_params, v_params) int16 [NP, Hkv, P, 2]
-    holding fp16 (scale, zero) bits, as the tuple (k_codes, v_codes, k_params, v_params). Rows
-    that are not valid tokens keep what `out` held (zeros when out is None).
+    Returns the tuple (k_codes uint8 [NP, Hkv, P, D/2], v_codes uint8 [NP, Hkv, D, P/2] (channel-
+    major), k_params, v_params int16 [NP, Hkv, P, 2] holding fp16 (scale, zero) bits). What is
+    not written (rows that are not valid tokens; V words with no valid token) keeps what `out`
+    held (zeros when out is None).
     """
     lib = load()
     NP, Hkv, P, D = k_cache.shape
@@ -348,12 +349,12 @@ def quantize_kv_int4(k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: t
     _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
     if out is None:
         out = (torch.zeros((NP, Hkv, P, D // 2), dtype=torch.uint8, device=dev),
-               torch.zeros((NP, Hkv, P, D // 2), dtype=torch.uint8, device=dev),
+               torch.zeros((NP, Hkv, D, P // 2), dtype=torch.uint8, device=dev),
                torch.zeros((NP, Hkv, P, 2), dtype=torch.int16, device=dev),
                torch.zeros((NP, Hkv, P, 2), dtype=torch.int16, device=dev))
     kc, vc, kp, vp = out
     for t, name, dt, shp in ((kc, "k_codes", torch.uint8, (NP, Hkv, P, D // 2)),
-                             (vc, "v_codes", torch.uint8, (NP, Hkv, P, D // 2)),
+                             (vc, "v_codes", torch.uint8, (NP, Hkv, D, P // 2)),
                              (kp, "k_params", torch.int16, (NP, Hkv, P, 2)),
                              (vp, "v_params", torch.int16, (NP, Hkv, P, 2))):
         _need(t, name, dt, shape=shp, device=dev)
@@ -369,7 +370,8 @@ def sparse_decode_int4(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Te
                        num_selected: Optional[torch.Tensor], sink_tokens: int, local_tokens: int, sm_scale: float,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                        return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
-    """sparse_decode over INT4 pages (codes uint8 [NP, Hkv, P, D/2], params int16 [NP, Hkv, P, 2])."""
+    """sparse_decode over INT4 pages (k_codes uint8 [NP, Hkv, P, D/2], v_codes uint8 [NP, Hkv, D, P/2],
+    params int16 [NP, Hkv, P, 2]; see include/ubs.h)."""
     lib = load()
     B, Hq, D = q.shape
     NP, Hkv, P, D2 = k_codes.shape
@@ -377,7 +379,7 @@ def sparse_decode_int4(q: torch.Tensor, k_codes: torch.Tensor, v_codes: torch.Te
     dev = q.device
     _need(q, "q", torch.bfloat16, device=dev)
     _need(k_codes, "k_codes", torch.uint8, device=dev)
-    _need(v_codes, "v_codes", torch.uint8, shape=k_codes.shape, device=dev)
+    _need(v_codes, "v_codes", torch.uint8, shape=(NP, Hkv, D2 * 2, P // 2), device=dev)
     _need(k_params, "k_params", torch.int16, shape=(NP, Hkv, P, 2), device=dev)
     _need(v_params, "v_params", torch.int16, shape=(NP, Hkv, P, 2), device=dev)
     _need(page_table, "page_table", torch.int32, shape=(B, max_pages), device=dev)

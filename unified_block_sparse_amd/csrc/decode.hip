@@ -15,10 +15,14 @@
 //   online softmax in the log2 domain (fp32);
 //   O += P V     : fp32 FMAs, each lane owning 8 channels of one key row, V read with
 //                  16-byte loads that cover whole rows, P broadcast through LDS.
-// INT4 pages (same kernel, Q4 = true): K rows come as 4-bit codes n with a per-row fp16
-// (scale s, zero z), x = n s + z. The codes enter the MFMA as bf16 128 + n (exact: the
-// code is OR-ed into the mantissa of 128), so S = s (Q.(128 + n)) + (z - 128 s) sum(Q);
-// V codes are weighted by p s and the sum of p z is added to every channel at the end.
+// INT4 pages (same kernel, Q4 = true): rows come as 4-bit codes n with a per-row fp16
+// (scale s, zero z), x = n s + z. Codes enter the MFMA as the value 16 + n (exact: the
+// code fills the top mantissa bits of 16), so S = s (Q.(16 + n)) + (z - 16 s) sum(Q).
+// P.V runs on the fp16 MFMA, O^T = V^T (P s)^T: V pages are channel-major, so a lane's A
+// operand (8 tokens of one channel) is one word; the weights p s, rounded to fp16, go
+// through LDS as the B operand, and sum p z - 16 sum fp16(p s) joins every channel at the
+// end. (fp16 rather than bf16 for P.V: its 11-bit weights keep the rounding of p s well
+// inside the attention tolerance.)
 // Partial (max, sum, output) triples of the 4 waves are merged through LDS; the
 // work-group writes one partial per split (or the output when the key set has one
 // split), and a second launch merges the splits of each (b, g) with a log-sum-exp
@@ -29,6 +33,10 @@
 #include <algorithm>
 
 namespace ubs {
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 
 constexpr int kMaxSplits = 128;
 constexpr int kChunkTokens = 32;   // tokens per chunk
@@ -41,23 +49,33 @@ struct ChunkRegs {
 };
 template <int D>
 struct ChunkRegs<D, true> {
-  uint32_t k[kChunkTokens / 16][D / 32];   // 8 codes per word
-  uint32_t kp[kChunkTokens / 16];          // fp16 (scale, zero) of the lane's key row
-  uint32_t v[D / 16];                      // the lane's 8 channels of a V row
-  uint32_t vp[D / 16];
+  uint32_t k[kChunkTokens / 16][D / 32];   // K codes of the lane's key rows, 8 per word
+  uint32_t kp[kChunkTokens / 16];          // fp16 (scale, zero) of those K rows
+  uint32_t vp[kChunkTokens / 16];          // ... and of the same V rows
+  uint32_t v[D / 16];                      // V codes: channel cb*16 + m, tokens 8*qg + [0, 8)
 };
 
 __device__ __forceinline__ float half_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float half_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-// 8 INT4 codes (channel 2j in the low nibble of byte j, 2j+1 in its high nibble) as the
-// bf16 values 128 + n, in channel order
+// The 8 INT4 codes of a word (code k in nibble k/2 of the low half if k is even, of the
+// high half if odd) in code order, as the values 16 + n: exponent 4 and the code as the
+// top 4 mantissa bits (bf16 bits 0x4180 | n << 3, fp16 bits 0x4C00 | n << 6). Pair j
+// takes nibble j of both halves: one shift and one and-or.
+template <int J, int POS>
+__device__ __forceinline__ uint32_t nibble_pair(uint32_t w) {
+  constexpr int sh = 4 * J - POS;   // nibble J of each half to bit POS of that half
+  return sh >= 0 ? w >> sh : w << -sh;
+}
 __device__ __forceinline__ bf16x8 codes_bf16(uint32_t w) {
-  const uint32_t t = w & 0x0F0F0F0Fu, u = (w >> 4) & 0x0F0F0F0Fu;
-  u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = 0x43004300u | ((t >> (8 * j)) & 0xFu) | (((u >> (8 * j)) & 0xFu) << 16);
+  const u32x4 r = {(nibble_pair<0, 3>(w) & 0x00780078u) | 0x41804180u, (nibble_pair<1, 3>(w) & 0x00780078u) | 0x41804180u,
+                   (nibble_pair<2, 3>(w) & 0x00780078u) | 0x41804180u, (nibble_pair<3, 3>(w) & 0x00780078u) | 0x41804180u};
   return as_bf16x8(r);
+}
+__device__ __forceinline__ f16x8 codes_f16(uint32_t w) {
+  const u32x4 r = {(nibble_pair<0, 6>(w) & 0x03C003C0u) | 0x4C004C00u, (nibble_pair<1, 6>(w) & 0x03C003C0u) | 0x4C004C00u,
+                   (nibble_pair<2, 6>(w) & 0x03C003C0u) | 0x4C004C00u, (nibble_pair<3, 6>(w) & 0x03C003C0u) | 0x4C004C00u};
+  return __builtin_bit_cast(f16x8, r);
 }
 
 __device__ __forceinline__ void wave_sync_lds() {
@@ -122,7 +140,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   constexpr int CT = kChunkTokens;
   constexpr int NB = CT / 16;  // 16-key MFMA blocks per chunk
   constexpr int VR = CT / TG;  // V rows per lane and chunk
-  __shared__ float p_lds[4][CT][G];
+  __shared__ float p_lds[Q4 ? 1 : 4][CT][G];
+  __shared__ __attribute__((aligned(16))) float p_t[Q4 ? 4 : 1][16][CT + 4];   // INT4: fp16(p s) [head][token]
+  __shared__ float a_lds[4][16];                                                // INT4: per-head factors
   __shared__ float w_m[4][G], w_l[4][G];
   __shared__ float w_o[4][G][D];
 
@@ -194,14 +214,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
   for (int i = 0; i < 4; ++i) m_run[i] = kNegInf;
   float o[G][8];
   float lsum[G];
-  float zacc[G];   // INT4: sum over the lane's V rows of p * zero
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     lsum[h] = 0.f;
-    zacc[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
   }
+  // INT4: O^T blocks (lane: channels cb*16 + 4*qg + i of head m), and the lane's sums
+  // over its key rows of p and of p z - 16 fp16(p s) for heads 4*qg + i
+  f32x4 oT[Q4 ? D / 16 : 1];
+  float lsum4[4], zacc4[4];
+#pragma unroll
+  for (int cb = 0; cb < (Q4 ? D / 16 : 1); ++cb) oT[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lsum4[i] = zacc4[i] = 0.f;
   const int cc = lane % CH;
   const int tg = lane / CH;
   const int64_t head_stride = (int64_t)P * D;  // one (page, KV head) slab
@@ -249,11 +275,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
         R.kp[blk] = __builtin_amdgcn_raw_buffer_load_b32(rkp, row * 4, 0, 0);
       }
 #pragma unroll
-      for (int x = 0; x < VR; ++x) {
-        const int row = min(r0 + tg + TG * x, P - 1);
-        R.v[x] = __builtin_amdgcn_raw_buffer_load_b32(rv, row * (D / 2) + cc * 4, 0, 0);
-        R.vp[x] = __builtin_amdgcn_raw_buffer_load_b32(rvp, row * 4, 0, 0);
-      }
+      for (int blk = 0; blk < NB; ++blk)
+        R.vp[blk] = __builtin_amdgcn_raw_buffer_load_b32(rvp, min(r0 + blk * 16 + m, P - 1) * 4, 0, 0);
+      // (tokens past the page read the next channel's word, or zeros past the slab; their
+      // weights are zero)
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+        R.v[cb] = __builtin_amdgcn_raw_buffer_load_b32(rv, (cb * 16 + m) * (P / 2) + (r0 + 8 * qg) / 2, 0, 0);
     } else {
       const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache, page);
       const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache, page);
@@ -288,7 +316,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], codes_bf16(R.k[blk][kk]), acc, 0, 0, 0);
-        const float sk = half_lo(R.kp[blk]), zk = half_hi(R.kp[blk]) - 128.f * sk;
+        const float sk = half_lo(R.kp[blk]), zk = half_hi(R.kp[blk]) - 16.f * sk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[blk][i] = ok ? fmaf(sk, acc[i], zk * qsum[i]) * scale_log2 : kNegInf;
       } else {
@@ -312,47 +340,68 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       alpha_i[i] = rescale_factor(m_run[i], mn);
       m_run[i] = mn;
     }
+    if constexpr (Q4) {
+      // weights: p_t[head][token] = fp16(p s_v) (exact as fp32), and the lane's sums
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk)
+      for (int blk = 0; blk < NB; ++blk) {
+        const int row = r0 + blk * 16 + m;
+        const bool ok = row >= lo && row < hi;   // (params of other rows are not trusted)
+        const float sv = ok ? half_lo(R.vp[blk]) : 0.f, zv = ok ? half_hi(R.vp[blk]) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = qg * 4 + i;
-        if (h < G) p_lds[wave][blk * 16 + m][h] = softmax_weight(s[blk][i], m_run[i]);
-      }
-    wave_sync_lds();
-    float alpha[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) alpha[h] = readlane_f(alpha_i[h & 3], 16 * (h >> 2));
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      lsum[h] *= alpha[h];
-      if constexpr (Q4) zacc[h] *= alpha[h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
-    }
-    // O += P V over the chunk's rows tg, tg + TG, ... (weights of rows outside [lo, hi)
-    // are zero and their V values are replaced by zero)
-#pragma unroll
-    for (int x = 0; x < VR; ++x) {
-      const int rr = tg + TG * x;
-      const int row = r0 + rr;
-      const bool ok = row >= lo && row < hi;
-      if constexpr (Q4) {
-        // (rows outside [lo, hi) have weight zero; their params are not trusted)
-        const float sv = ok ? half_lo(R.vp[x]) : 0.f, zv = ok ? half_hi(R.vp[x]) : 0.f;
-        float vf[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vf[e] = (float)((R.v[x] >> (4 * e)) & 0xFu);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = p_lds[wave][rr][h];
-          lsum[h] += p;
-          zacc[h] = fmaf(p, zv, zacc[h]);
-          const float ps = p * sv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(ps, vf[e], o[h][e]);
+        for (int i = 0; i < 4; ++i) {
+          const float p = softmax_weight(s[blk][i], m_run[i]);
+          const float pr = (float)(_Float16)(p * sv);
+          p_t[wave][qg * 4 + i][blk * 16 + m] = pr;
+          lsum4[i] = blk == 0 ? fmaf(lsum4[i], alpha_i[i], p) : lsum4[i] + p;
+          zacc4[i] = fmaf(-16.f, pr, fmaf(p, zv, blk == 0 ? zacc4[i] * alpha_i[i] : zacc4[i]));
         }
-      } else {
+      }
+      if (m == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a_lds[wave][qg * 4 + i] = alpha_i[i];
+      }
+      wave_sync_lds();
+      // B operand: head m, tokens 8*qg + [0, 8); (heads past G give columns never read)
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(&p_t[wave][m][8 * qg]);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(&p_t[wave][m][8 * qg + 4]);
+      u32x4 pw;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0[2 * e], p0[2 * e + 1]}), f16x2));
+        pw[2 + e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p1[2 * e], p1[2 * e + 1]}), f16x2));
+      }
+      const f16x8 pb = __builtin_bit_cast(f16x8, pw);
+      const float al = a_lds[wave][m];
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb) {
+        oT[cb] *= al;
+        oT[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_f16(R.v[cb]), pb, oT[cb], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = qg * 4 + i;
+          if (h < G) p_lds[wave][blk * 16 + m][h] = softmax_weight(s[blk][i], m_run[i]);
+        }
+      wave_sync_lds();
+      float alpha[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) alpha[h] = readlane_f(alpha_i[h & 3], 16 * (h >> 2));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        lsum[h] *= alpha[h];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+      }
+      // O += P V over the chunk's rows tg, tg + TG, ... (weights of rows outside [lo, hi)
+      // are zero and their V values are replaced by zero)
+#pragma unroll
+      for (int x = 0; x < VR; ++x) {
+        const int rr = tg + TG * x;
+        const int row = r0 + rr;
+        const bool ok = row >= lo && row < hi;
         float vf[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -406,38 +455,62 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  // (INT4: the zero terms join the output before the token groups are summed)
   if constexpr (Q4) {
+    // ---- the wave's partial: sums over the 16 key lanes of each head group; O^T plus
+    // the zero term of its head
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] += zacc[h];
-  }
-
-  // ---- reduce the token groups of the wave
+      for (int o2 = 1; o2 < 16; o2 <<= 1) {
+        lsum4[i] += shfl_xor(lsum4[i], o2);
+        zacc4[i] += shfl_xor(zacc4[i], o2);
+      }
+    if (m == 0) {
 #pragma unroll
-  for (int x = CH; x < 64; x <<= 1) {
+      for (int i = 0; i < 4; ++i) {
+        const int h = qg * 4 + i;
+        if (h < G) {
+          w_m[wave][h] = m_run[i];
+          w_l[wave][h] = lsum4[i];
+        }
+        a_lds[wave][h] = zacc4[i];
+      }
+    }
+    wave_sync_lds();
+    if (m < G) {
+      const float z = a_lds[wave][m];
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w_o[wave][m][cb * 16 + 4 * qg + i] = oT[cb][i] + z;
+    }
+    __syncthreads();
+  } else {
+    // ---- reduce the token groups of the wave
+#pragma unroll
+    for (int x = CH; x < 64; x <<= 1) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        lsum[h] += shfl_xor(lsum[h], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] += shfl_xor(o[h][e], x);
+      }
+    }
+    // ---- stage the wave's partial in LDS
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      lsum[h] += shfl_xor(lsum[h], x);
+      const float mh = readlane_f(m_run[h & 3], 16 * (h >> 2));
+      if (lane == 0) {
+        w_m[wave][h] = mh;
+        w_l[wave][h] = lsum[h];
+      }
+      if (tg == 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] += shfl_xor(o[h][e], x);
+        for (int e = 0; e < 8; ++e) w_o[wave][h][cc * 8 + e] = o[h][e];
+      }
     }
+    __syncthreads();
   }
-  // ---- stage the wave's partial in LDS
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mh = readlane_f(m_run[h & 3], 16 * (h >> 2));
-    if (lane == 0) {
-      w_m[wave][h] = mh;
-      w_l[wave][h] = lsum[h];
-    }
-    if (tg == 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w_o[wave][h][cc * 8 + e] = o[h][e];
-    }
-  }
-  __syncthreads();
 
   // ---- merge the 4 waves: element (h, c) per thread
   const bool single = (n_splits == 1);
