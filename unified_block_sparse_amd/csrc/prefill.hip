@@ -174,7 +174,9 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
       x = w2 % ns;
     }
     q_off = a.cu_seqlens[bs];
-    L = a.cu_seqlens[bs + 1] - q_off;
+    // (a length past max_seqlen or past the page-table row is a caller error: clamped, so
+    // that no page-table entry outside the row is read)
+    L = min(a.cu_seqlens[bs + 1] - q_off, min(a.nT_max * T, a.pt_stride << a.log2_P));
     if (i * T >= L) return;   // (whole work-group, before any barrier)
     qt0 = 0;
     lse_stride = a.total_q;
