@@ -372,11 +372,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
       }
       const f16x8 pb = __builtin_bit_cast(f16x8, pw);
       const float al = a_lds[wave][m];
+      if (__ballot(al != 1.f)) {   // (a head's max grew: rare after the first chunks)
 #pragma unroll
-      for (int cb = 0; cb < D / 16; ++cb) {
-        oT[cb] *= al;
-        oT[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_f16(R.v[cb]), pb, oT[cb], 0, 0, 0);
+        for (int cb = 0; cb < D / 16; ++cb) oT[cb] *= al;
       }
+#pragma unroll
+      for (int cb = 0; cb < D / 16; ++cb)
+        oT[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_f16(R.v[cb]), pb, oT[cb], 0, 0, 0);
     } else {
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
