@@ -83,6 +83,14 @@ __global__ __launch_bounds__(256) void score_kernel(const uint16_t* __restrict__
 
   const int32_t* pt = page_table + (int64_t)b * max_pages;
   float* out = scores + ((int64_t)b * Hkv + g) * max_pages;
+  // the page-table entries of all the wave's groups first, so that each group's record
+  // loads do not wait on a page-table load of their own (gpw <= 2)
+  int32_t pg[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int s = (first_group + t) * 16 + m;
+    pg[t] = (t < gpw && s < n_sub) ? pt[s / U] : 0;
+  }
   for (int t = 0; t < gpw; ++t) {
     const int grp = first_group + t;
     if (grp * 16 >= n_sub) break;  // wave-uniform
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(256) void score_kernel(const uint16_t* __restrict__
     const bool ok = (s < n_sub) && (j * P + u * Lp < L);
     u32x4 bv[KK];
     if (ok) {
-      const uint16_t* rec = bounds + (((int64_t)pt[j] * Hkv + g) * U + u) * (2 * D) + qg * 8;
+      const uint16_t* rec = bounds + (((int64_t)(t == 0 ? pg[0] : pg[1]) * Hkv + g) * U + u) * (2 * D) + qg * 8;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) bv[kk] = ld16(rec + kk * 32);
     } else {
