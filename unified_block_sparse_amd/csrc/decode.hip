@@ -132,8 +132,13 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
   return ch;
 }
 
+// At most 256 registers a lane (two waves per SIMD or more) wherever that costs no spill:
+// the allocator then keeps the INT4 kernel (about 166 registers) in the vector file alone,
+// three waves per SIMD (measured on MI355X: about 10% faster than two), and the bf16
+// kernel at G = 8, D = 128 at two waves instead of one. At G = 16 the bf16 kernel's
+// double-buffered K/V rows and G-wide accumulators need more than 256.
 template <int D, int G, bool Q4>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((Q4 || G <= 8) ? 2 : 1))) void decode_kernel(const DecodeArgs a) {
   constexpr int KK = D / 32;   // QK MFMA steps (16x16x32)
   constexpr int CH = D / 8;    // lanes per V row (16-byte pieces)
   constexpr int TG = 64 / CH;  // token groups in P.V
