@@ -34,9 +34,11 @@ __device__ __forceinline__ uint32_t pos_part_bf16x2(uint32_t w) {
 
 // Grid: blockIdx.x = ((b * n_dense) + dense index) * chunks + chunk. Each wave scores
 // `gpw` groups of 16 consecutive sub-pages of its (b, g); with U = P/Lp sub-pages per
-// page a group covers 16/U whole pages.
+// page a group covers 16/U whole pages. At most 128 registers a lane: the allocator then
+// keeps the D = 128 kernel in 80 vector registers (6 waves per SIMD) instead of 95 plus 4
+// accumulation registers (4 waves); more waves keep more record loads in flight.
 template <int D, int U, int G>
-__global__ __launch_bounds__(256) void score_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(const uint16_t* __restrict__ q,
                                                     const uint16_t* __restrict__ bounds,
                                                     const int32_t* __restrict__ page_table,
                                                     const int32_t* __restrict__ seq_lens,
