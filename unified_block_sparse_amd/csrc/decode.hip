@@ -67,14 +67,25 @@ __device__ __forceinline__ uint32_t nibble_pair(uint32_t w) {
   constexpr int sh = 4 * J - POS;   // nibble J of each half to bit POS of that half
   return sh >= 0 ? w >> sh : w << -sh;
 }
+// (x & m) | c in one instruction. The three-operand form takes no literal and at most one
+// scalar operand on this architecture: m goes in a scalar register, c in a vector register
+// (loop-invariant, so set once); written with literals, the compiler emits an and and an
+// or, a third more vector instructions for the codes of a chunk.
+__device__ __forceinline__ uint32_t and_or_sv(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+  return r;
+}
 __device__ __forceinline__ bf16x8 codes_bf16(uint32_t w) {
-  const u32x4 r = {(nibble_pair<0, 3>(w) & 0x00780078u) | 0x41804180u, (nibble_pair<1, 3>(w) & 0x00780078u) | 0x41804180u,
-                   (nibble_pair<2, 3>(w) & 0x00780078u) | 0x41804180u, (nibble_pair<3, 3>(w) & 0x00780078u) | 0x41804180u};
+  constexpr uint32_t m = 0x00780078u, c = 0x41804180u;
+  const u32x4 r = {and_or_sv(nibble_pair<0, 3>(w), m, c), and_or_sv(nibble_pair<1, 3>(w), m, c),
+                   and_or_sv(nibble_pair<2, 3>(w), m, c), and_or_sv(nibble_pair<3, 3>(w), m, c)};
   return as_bf16x8(r);
 }
 __device__ __forceinline__ f16x8 codes_f16(uint32_t w) {
-  const u32x4 r = {(nibble_pair<0, 6>(w) & 0x03C003C0u) | 0x4C004C00u, (nibble_pair<1, 6>(w) & 0x03C003C0u) | 0x4C004C00u,
-                   (nibble_pair<2, 6>(w) & 0x03C003C0u) | 0x4C004C00u, (nibble_pair<3, 6>(w) & 0x03C003C0u) | 0x4C004C00u};
+  constexpr uint32_t m = 0x03C003C0u, c = 0x4C004C00u;
+  const u32x4 r = {and_or_sv(nibble_pair<0, 6>(w), m, c), and_or_sv(nibble_pair<1, 6>(w), m, c),
+                   and_or_sv(nibble_pair<2, 6>(w), m, c), and_or_sv(nibble_pair<3, 6>(w), m, c)};
   return __builtin_bit_cast(f16x8, r);
 }
 
