@@ -182,7 +182,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     const int j = tid * EPT + e;
     key[e] = (j < n) ? float_order_key(sc[j]) : 0u;  // valid keys are > 0
   }
-  // k-th largest key: the largest tau with #(key >= tau) >= k.
+  // k-th largest key: the largest tau with #(key >= tau) >= k. A candidate with exactly
+  // k keys at or above it ends the search early: those keys are the k largest, with no
+  // tie at the threshold (it falls between the k-th and the (k+1)-th key, whose bits
+  // first differ at this round), and the selection below takes exactly them. (total
+  // is the same in every thread, so the exit is uniform.)
   uint32_t tau = 0;
   const int w = tid >> 6, lane = lane_id();
   for (int bit = 31; bit >= 0; --bit) {
@@ -195,8 +199,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
     __syncthreads();
     const int total = cnt[slot][0] + cnt[slot][1] + cnt[slot][2] + cnt[slot][3];
     if (total >= k) tau = cand;
+    if (total == k) break;
   }
-  // #(key > tau) < k <= #(key >= tau): take all keys above tau and the lowest-index ties.
+  // #(key > tau) < k <= #(key >= tau) (after an early exit: #(key >= tau) = k and every
+  // key equal to tau is taken): take all keys above tau and the lowest-index ties.
   int gt = 0, ties = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
