@@ -126,9 +126,11 @@ __global__ __launch_bounds__(256) void mask_row_kernel(const MaskArgs a) {
 #pragma unroll
       for (int e = 0; e < EPT; ++e) c += __popcll(__ballot(key[e] >= cand));
       if (c >= take) tau = cand;
+      if (c == take) break;   // exactly take keys at or above: the answer, no tie at tau
     }
   }
-  // #(key > tau) < take <= #(key >= tau): every key above tau, then ties by ascending j
+  // #(key > tau) < take <= #(key >= tau) (after an early exit #(key >= tau) = take, and
+  // every key equal to tau is kept): every key above tau, then ties by ascending j
   int n_gt = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) n_gt += __popcll(__ballot(key[e] > tau && key[e] != 0u));
