@@ -85,10 +85,14 @@ def test_select_matches_oracle(lens, Hq, Hkv, D, P, Lp, hk, budget):
     check_selection(sel_g, num_g, sel_o, scores, hk, budget // P)
 
 
-def test_select_exact_ties_break_to_lower_index():
+@pytest.mark.parametrize("lens,P,Lp,budget", [
+    ([3000, 777, 4096], 64, 16, 10 * 64),   # rows of at most 64 pages: the one-wave top-k
+    ([20000, 3000], 16, 16, 40 * 16),       # a row of 1,250 pages: the work-group top-k
+])
+def test_select_exact_ties_break_to_lower_index(lens, P, Lp, budget):
     """Integer-valued q and keys make many page scores tie exactly (the sums are exact in
     fp32 and fp64), so the tie-break must match the oracle bit for bit."""
-    c = cases.make_decode("t", [3000, 777, 4096], 8, 2, 128, 64, 16, [0, 0], 10 * 64, 4, 8, 33, DEV)
+    c = cases.make_decode("t", lens, 8, 2, 128, P, Lp, [0, 0], budget, 4, 8, 33, DEV)
     for t in (c.k_cache, c.q):
         t.copy_(t.float().mul(0.7).round().clamp(-1, 1).to(torch.bfloat16))
     sel_g, num_g = _gpu_select(c)
