@@ -593,11 +593,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
     for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, c_m[h][sp]);
     float O = 0.f, S = 0.f;
     if (M != kNegInf) {
-      for (int sp = 0; sp < n_splits; ++sp) {
-        const float f = fast_exp2(c_m[h][sp] - M);
-        const float* pp = part + (qh * a.max_splits + sp) * (D + 2);
-        O = fmaf(f, pp[c], O);
-        S = fmaf(f, c_w[h][sp], S);
+      // 8 splits at a time, their loads issued before any is used (one at a time, each
+      // load waited for by its FMA, the splits cost one cache round trip each)
+      const float* pc = part + qh * a.max_splits * (D + 2) + c;
+      for (int sp0 = 0; sp0 < n_splits; sp0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = sp0 + u < n_splits ? pc[(int64_t)(sp0 + u) * (D + 2)] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (sp0 + u < n_splits) {
+            const float f = fast_exp2(c_m[h][sp0 + u] - M);
+            O = fmaf(f, v[u], O);
+            S = fmaf(f, c_w[h][sp0 + u], S);
+          }
+        }
       }
     }
     a.out[qh * D + c] = (S > 0.f) ? O / S : 0.f;
