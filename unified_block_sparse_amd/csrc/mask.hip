@@ -84,21 +84,35 @@ __global__ __launch_bounds__(256) void mask_row_kernel(const MaskArgs a) {
     const int w = x / D, c = x % D;
     qv[w][c] = (i0 + w < a.nT) ? a.qmean[((int64_t)slot * a.nT + i0 + w) * D + c] : 0.f;
   }
-  // ---- scores of the candidates j < i: lane l, register e -> j = 64e + l
+  // ---- scores of the candidates j < i: lane l, register e -> j = 64e + l. Chunk e of 64
+  // K-tile means goes through LDS; its loads are issued into registers while chunk e-1 is
+  // scored (thread tid holds pieces tid + 256u of the chunk).
+  constexpr int NPC = 64 * (D / 4) / 256;   // 16-byte pieces per thread and chunk
   uint32_t key[EPT];   // order-preserving key of the score, 0 = not a candidate
   const int nchunks = (i_last + 63) / 64;
+  f32x4 nxt[NPC];
+  auto load_chunk = [&](int e) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NPC; ++u) {
+      const int x = tid + 256 * u;
+      const int t = x / (D / 4), c4 = x % (D / 4);
+      const int j = e * 64 + t;
+      nxt[u] = j < a.nT ? *reinterpret_cast<const f32x4*>(a.kmean + ((int64_t)kslot * a.nT + j) * D + c4 * 4)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if (nchunks > 0) load_chunk(0);
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     key[e] = 0u;
     if (e < nchunks) {   // uniform over the work-group
       __syncthreads();   // the previous chunk is consumed (and qv is written)
-      for (int x = tid; x < 64 * (D / 4); x += 256) {
-        const int t = x / (D / 4), c4 = x % (D / 4);
-        const int j = e * 64 + t;
-        const f32x4 v = j < a.nT ? *reinterpret_cast<const f32x4*>(a.kmean + ((int64_t)kslot * a.nT + j) * D + c4 * 4)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(&kb[t][c4 * 4]) = v;
+#pragma unroll
+      for (int u = 0; u < NPC; ++u) {
+        const int x = tid + 256 * u;
+        *reinterpret_cast<f32x4*>(&kb[x / (D / 4)][(x % (D / 4)) * 4]) = nxt[u];
       }
+      if (e + 1 < nchunks) load_chunk(e + 1);
       __syncthreads();
       float s = 0.f;
 #pragma unroll 8
