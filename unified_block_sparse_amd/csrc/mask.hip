@@ -26,8 +26,11 @@ __global__ __launch_bounds__(256) void tile_mean_kernel(const MaskArgs a) {
   constexpr int RPP = 256 / CPR;   // rows per pass
   __shared__ float part[RPP][D + 1];
   const int nq = a.dense_kv.n * a.G;
-  const int slot = blockIdx.x / a.nT;
-  const int tile = blockIdx.x % a.nT;
+  // head slot fastest: the work-groups running together read the dense heads of the same
+  // tiles, whole runs of each token's [Hq][D] row of q (and whole K pages), instead of
+  // one head's 2*D bytes out of many rows
+  const int slot = blockIdx.x % (nq + a.dense_kv.n);
+  const int tile = blockIdx.x / (nq + a.dense_kv.n);
   const int tid = threadIdx.x, rr = tid / CPR, cc = tid % CPR;
   const int r0 = tile * a.T, r1 = min(r0 + a.T, a.L);
   const bool isq = slot < nq;
