@@ -238,69 +238,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   if (tid == 0) num_selected[bg] = k;
 }
 
-// Rows of at most 64 * KPL pages: one wave per (b, KV head), four rows per work-group, no
-// barrier and no LDS. Lane l holds pages e*64 + l (e < KPL); the bitwise search is the
-// one above with counts from ballots alone, and kept pages are written in ascending
-// order by ballot ranks (page e*64 + l after every kept page of a lower e, or of the same
-// e and a lower lane); ties at the threshold go to the lower pages the same way.
-template <int KPL>
-__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores,
-                                                        const int32_t* __restrict__ seq_lens,
-                                                        int max_pages, int Hkv, int P, int k, int n_rows,
-                                                        uint64_t streaming_mask,
-                                                        int32_t* __restrict__ selected,
-                                                        int32_t* __restrict__ num_selected) {
-  const int bg = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bg >= n_rows) return;   // (whole wave)
-  const int lane = lane_id();
-  const int g = bg % Hkv;
-  const int b = bg / Hkv;
-  int32_t* sel = selected + (int64_t)bg * k;
-  const bool streaming = (streaming_mask >> g) & 1ull;
-  const int L = seq_lens[b];
-  const int n = streaming ? 0 : (L + P - 1) / P;
-  if (n <= k) {
-    for (int i = lane; i < k; i += 64) sel[i] = (i < n) ? i : -1;
-    if (lane == 0) num_selected[bg] = n;
-    return;
-  }
-  const float* sc = scores + (int64_t)bg * max_pages;
-  uint32_t key[KPL];
-#pragma unroll
-  for (int e = 0; e < KPL; ++e) {
-    const int j = e * 64 + lane;
-    key[e] = (j < n) ? float_order_key(sc[j]) : 0u;  // valid keys are > 0
-  }
-  // tau ends as the k-th largest key (n > k valid keys, so tau >= 1 and the zero keys of
-  // pages past n are never counted, kept or tied)
-  uint32_t tau = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = tau | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < KPL; ++e) c += __popcll(__ballot(key[e] >= cand));
-    if (c >= k) tau = cand;
-    if (c == k) break;
-  }
-  int n_gt = 0;
-#pragma unroll
-  for (int e = 0; e < KPL; ++e) n_gt += __popcll(__ballot(key[e] > tau));
-  const int take_ties = k - n_gt;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int tie_base = 0, base = 0;
-#pragma unroll
-  for (int e = 0; e < KPL; ++e) {
-    const bool tie = key[e] == tau;
-    const uint64_t tm = __ballot(tie);
-    const bool kept = key[e] > tau || (tie && tie_base + __popcll(tm & below) < take_ties);
-    tie_base += __popcll(tm);
-    const uint64_t km = __ballot(kept);
-    if (kept) sel[base + __popcll(km & below)] = e * 64 + lane;
-    base += __popcll(km);
-  }
-  if (lane == 0) num_selected[bg] = k;
-}
-
 template <int D, int U>
 static hipError_t launch_score_du(const SelectArgs& a, int G, int chunks, int gpw, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.dense.n * chunks));
@@ -333,21 +270,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 #undef UBS_SCORE_DU
     if (e != hipSuccess) return e;
   }
-  const int n_rows = a.B * a.Hkv;
-  // rows of up to 1,024 pages: one wave each (measured on MI355X: the 512-page rows of 4
-  // x 32K-token sequences select in 13.1-13.6 us against 14-18; 2,048-page rows were
-  // slower that way, 148-150 us against 131-134 with the work-group search below)
-  const int kpl = (a.max_pages + 63) / 64;
-#define UBS_TOPK_WAVE(K)                                                                                \
-  if (kpl <= K) {                                                                                       \
-    hipLaunchKernelGGL((topk_wave_kernel<K>), dim3((unsigned)((n_rows + 3) / 4)), dim3(256), 0, s,      \
-                       a.scores, a.seq_lens, a.max_pages, a.Hkv, a.P, a.k, n_rows, a.streaming_mask,    \
-                       a.selected, a.num_selected);                                                     \
-    return hipGetLastError();                                                                           \
-  }
-  UBS_TOPK_WAVE(1) UBS_TOPK_WAVE(2) UBS_TOPK_WAVE(4) UBS_TOPK_WAVE(8) UBS_TOPK_WAVE(16)
-#undef UBS_TOPK_WAVE
-  const dim3 grid((unsigned)n_rows);
+  const dim3 grid((unsigned)(a.B * a.Hkv));
   const int need = (a.max_pages + 255) / 256;
 #define UBS_TOPK(E)                                                                               \
   if (need <= E) {                                                                                \
@@ -355,7 +278,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
                        a.Hkv, a.P, a.k, a.streaming_mask, a.selected, a.num_selected);            \
     return hipGetLastError();                                                                     \
   }
-  UBS_TOPK(8) UBS_TOPK(16) UBS_TOPK(32) UBS_TOPK(64)   // (more than 1,024 pages: need >= 5)
+  UBS_TOPK(1) UBS_TOPK(2) UBS_TOPK(4) UBS_TOPK(8) UBS_TOPK(16) UBS_TOPK(32) UBS_TOPK(64)
 #undef UBS_TOPK
   return hipErrorInvalidValue;
 }
