@@ -149,7 +149,8 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
 // kernel at G = 8, D = 128 at two waves instead of one. At G = 16 the bf16 kernel's
 // double-buffered K/V rows and G-wide accumulators need more than 256.
 template <int D, int G, bool Q4>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((Q4 || G <= 8) ? 2 : 1))) void decode_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((Q4 || G <= 8) ? 2 : 1)))
+void decode_kernel(const DecodeArgs a) {
   constexpr int KK = D / 32;   // QK MFMA steps (16x16x32)
   constexpr int CH = D / 8;    // lanes per V row (16-byte pieces)
   constexpr int TG = 64 / CH;  // token groups in P.V

@@ -38,13 +38,14 @@ __device__ __forceinline__ uint32_t pos_part_bf16x2(uint32_t w) {
 // keeps the D = 128 kernel in 80 vector registers (6 waves per SIMD) instead of 95 plus 4
 // accumulation registers (4 waves); more waves keep more record loads in flight.
 template <int D, int U, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ bounds,
-                                                    const int32_t* __restrict__ page_table,
-                                                    const int32_t* __restrict__ seq_lens,
-                                                    int max_pages, int Hq, int Hkv, int P, int Lp,
-                                                    HeadList dense, int chunks, int gpw,
-                                                    float* __restrict__ scores) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+void score_kernel(const uint16_t* __restrict__ q,
+                  const uint16_t* __restrict__ bounds,
+                  const int32_t* __restrict__ page_table,
+                  const int32_t* __restrict__ seq_lens,
+                  int max_pages, int Hq, int Hkv, int P, int Lp,
+                  HeadList dense, int chunks, int gpw,
+                  float* __restrict__ scores) {
   constexpr int KK = D / 16;  // MFMA steps over the 2D-long record (K = 32 each)
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
