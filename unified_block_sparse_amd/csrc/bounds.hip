@@ -55,6 +55,12 @@ __global__ __launch_bounds__(256) void bounds_kernel(const uint16_t* __restrict_
     if (lo >= valid) break;
     if (j * P + lo + Lp <= from) continue;   // no new token in this sub-page (updates only)
     const int hi = min(lo + Lp, valid);
+    // (an empty asm that claims to change the rows: the rows do not change over the
+    // sub-page loop, so the compiler would convert all NR x 8 values to fp32 once, ahead
+    // of it, and keep them live beside the raw rows, 192 registers at D = 128, P = 64 and
+    // two waves per SIMD instead of 118 and four)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(rows[i]));
     float mn[8], mx[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { mn[e] = __builtin_inff(); mx[e] = -__builtin_inff(); }
