@@ -12,16 +12,23 @@ build_page_bounds, sparse_prefill, select_pages, sparse_decode in that order: th
 streams > 1.5 GB, which evicts the bounds and K/V pages from L2 and the 256 MB Infinity
 Cache, so selection and decode read cold HBM.
 
-The line also reports, outside the step and outside `value`, selection + decode on
-decode_ragged (B=64 sequences of 16K-128K tokens, Lp=16): the decode path at a batch large
-enough to amortise launches (--no-ragged skips it).
-
 value = 100 * (sum over the step's ops of their roofline time) / (measured step time),
 i.e. the step's speed as a percentage of the MI355X roofline: prefill counted as
 kept-tile flops against dense bf16 MFMA peak, bounds / selection / decode as their
 algorithmic HBM bytes against peak HBM bandwidth.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-ragged]
+The same line carries, outside `value`, one roofline fraction per named workload
+(`per_config`): prefill_tiny, the decode_llama8b step replayed as a HIP graph over 24
+cache instances, prefill_llama8b, the decode_ragged step (64 sequences of 16K-128K tokens)
+and prefill_extreme (262,144 tokens, Llama-3-70B heads), plus further legs (mask
+estimation, batched prefill, reused selection, INT4 pages) and the fp64 oracle timed on
+the host cores (`cpu_baseline`).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs LIST] [--no-cpu-baseline]
+
+--legs selects what runs (default: all): step, tiny, graph, ragged, extreme, mask,
+varlen, cpu. Without `step` the line holds only the selected legs' results; profiling
+runs use this to trace one workload at a time.
 """
 from __future__ import annotations
 
@@ -39,6 +46,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 PEAK_HBM_GBPS = 8000.0
 METRIC = "sparse prefill TFLOP/s (kept tiles) + decode KV GB/s, as % of MI355X roofline"
+LEGS = ("step", "tiny", "graph", "ragged", "extreme", "mask", "varlen", "cpu")
+# The pages' own figures for this method, quoted as context (relative speedups, no hardware
+# or absolute numbers given): LServe index page, Abstract.
+PAGES_CONTEXT = ("LServe (arXiv 2502.14866) abstract: up to 2.9x prefill and 1.3-2.1x decode speedup over "
+                 "vLLM on long-sequence serving; hardware, precision and absolute rates not stated")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_llama8b_traffic.json")
 KERNEL_SOURCES = ["unified_block_sparse_amd/csrc/prefill.hip", "unified_block_sparse_amd/csrc/common.h",
                   "unified_block_sparse_amd/csrc/launch.h"]
@@ -56,10 +68,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows-per-head", type=int, default=384)
-    ap.add_argument("--no-ragged", action="store_true",
-                    help="skip the separate decode_ragged step measurement (64 sequences, 16K-128K tokens)")
+    ap.add_argument("--legs", default=",".join(LEGS),
+                    help="comma-separated subset of: " + ", ".join(LEGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="same as leaving `cpu` out of --legs")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=256)
+    ap.add_argument("--no-ragged", action="store_true", help="same as leaving `ragged` out of --legs")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (5 times) and exit: "
                          "the known-size kernel that scales the HBM byte counters")
@@ -158,27 +171,33 @@ def decode_bytes(d, sel_pages):
 
 # ----------------------------------------------------------------------------- cpu baseline
 
-def cpu_baseline(c, d, kept_tiles: int, rows_per_head: int, ideal_s: float):
-    """Time the fp64 oracle on a bounded sample of the same step; extrapolate to a step."""
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def _host_bits(t):
+    import numpy as np
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def oracle_prefill_sample(c, rows_per_head: int, seed: int = 11):
+    """The fp64 oracle on `rows_per_head` seeded query rows of every head of prefill case c.
+    Returns (seconds for the sample, the oracle's fixed per-call part (K/V gather and
+    decode), seconds extrapolated to all L rows)."""
     import numpy as np
     import torch
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-
-    def bits(t):
-        return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-    rng = np.random.default_rng(11)
-    rows = sorted(rng.choice(c.L, size=rows_per_head, replace=False).tolist())
+    rng = np.random.default_rng(seed)
+    rows = sorted(rng.choice(c.L, size=min(rows_per_head, c.L), replace=False).tolist())
     q_host = np.zeros(tuple(c.q.shape), dtype=np.uint16)
-    q_host[rows] = bits(c.q[torch.tensor(rows, device=c.q.device)])
-    kb, vb = bits(c.k_cache), bits(c.v_cache)
+    q_host[rows] = _host_bits(c.q[torch.tensor(rows, device=c.q.device)])
+    kb, vb = _host_bits(c.k_cache), _host_bits(c.v_cache)
     pt, mask = c.page_table.cpu().numpy(), c.block_mask.cpu().numpy()
-    # the oracle gathers the sequence's K/V once per call (fixed), then works per row
     t0 = time.perf_counter()
     oracle.prefill_ref(q_host, kb, vb, pt, c.L, c.Hq, c.Hkv, c.D, c.P, c.T, c.head_kind, mask, c.sink_tiles,
                        c.local_tiles, c.sm_scale, rows=[])
@@ -186,14 +205,22 @@ def cpu_baseline(c, d, kept_tiles: int, rows_per_head: int, ideal_s: float):
     t0 = time.perf_counter()
     oracle.prefill_ref(q_host, kb, vb, pt, c.L, c.Hq, c.Hkv, c.D, c.P, c.T, c.head_kind, mask, c.sink_tiles,
                        c.local_tiles, c.sm_scale, rows=rows)
-    t_pf = time.perf_counter() - t0
-    # every sequence of the decode step, end to end (bounds -> selection -> decode)
+    t = time.perf_counter() - t0
+    return t, t_fixed, t_fixed + max(t - t_fixed, 0.0) * (c.L / len(rows)), len(rows)
+
+
+def oracle_decode_sample(d, batches):
+    """The fp64 oracle's whole decode step (bounds -> selection -> decode) on sequences
+    `batches` of decode case d, timed sequence by sequence (host copies of each sequence's
+    pages are made outside the timed part). Returns seconds."""
+    import numpy as np
+    import oracle
     t_dec = 0.0
-    for b in range(d.B):
-        dq = bits(d.q[b:b + 1])
+    for b in batches:
+        dq = _host_bits(d.q[b:b + 1])
         nb = (d.seq_lens[b] + d.P - 1) // d.P
         idx = d.page_table[b, :nb].long()
-        dk, dv = bits(d.k_cache[idx]), bits(d.v_cache[idx])
+        dk, dv = _host_bits(d.k_cache[idx]), _host_bits(d.v_cache[idx])
         dpt = np.arange(nb, dtype=np.int32)[None]
         t0 = time.perf_counter()
         sel, _ = oracle.select_ref(dq, dk, dpt, d.seq_lens[b:b + 1], d.Hq, d.Hkv, d.P, d.Lp, d.token_budget,
@@ -201,20 +228,67 @@ def cpu_baseline(c, d, kept_tiles: int, rows_per_head: int, ideal_s: float):
         oracle.decode_ref(dq, dk, dv, dpt, d.seq_lens[b:b + 1], d.Hq, d.Hkv, d.P, d.head_kind, sel,
                           d.sink_tokens, d.local_tokens, d.sm_scale, batches=[0])
         t_dec += time.perf_counter() - t0
-    step_s = t_fixed + max(t_pf - t_fixed, 0.0) * (c.L / len(rows)) + t_dec
+    return t_dec
+
+
+def cpu_baseline(c, d, rows_per_head: int, ideal_s: float, extra: dict):
+    """The fp64 oracle as it stands, on the host cores, on a bounded sample of the step's
+    workloads (prefill_llama8b rows, every decode_llama8b sequence); per-workload figures
+    for the other configurations come in `extra` (measured by their legs while their
+    inputs are resident). A one-thread figure of a smaller sample is added."""
+    threads = _blas_threads()
+    t_pf, t_fixed, pf_full, n_rows = oracle_prefill_sample(c, rows_per_head)
+    t_dec = oracle_decode_sample(d, range(d.B))
+    step_s = pf_full + t_dec
+    per_config = {
+        "prefill_llama8b": {"rows_per_s": round(n_rows * c.Hq / max(t_pf - t_fixed, 1e-9), 1),
+                            "sample": f"{n_rows} seeded rows x {c.Hq} heads, {t_pf:.2f} s",
+                            "full_config_s_extrapolated": round(pf_full, 1)},
+        "decode_llama8b": {"steps_per_s": round(1.0 / t_dec, 3),
+                           "sample": f"all {d.B} sequences (bounds, selection, decode), {t_dec:.2f} s"},
+    }
+    per_config.update(extra)
+    one = {}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1, f1, full1, n1 = oracle_prefill_sample(c, 32, seed=12)
+            td1 = oracle_decode_sample(d, range(d.B))
+        one = {"cores": 1, "prefill_llama8b_rows_per_s": round(n1 * c.Hq / max(t1 - f1, 1e-9), 1),
+               "decode_llama8b_steps_per_s": round(1.0 / td1, 3),
+               "step_s_extrapolated": round(full1 + td1, 1),
+               "value": 100.0 * ideal_s / (full1 + td1),
+               "sample": f"{n1} seeded prefill rows x {c.Hq} heads ({t1:.2f} s) + decode_llama8b "
+                         f"({td1:.2f} s) with BLAS limited to one thread"}
+    except Exception as e:   # threadpoolctl missing: say so instead
+        one = {"error": f"one-thread figure not taken: {e}"}
     return {
         "value": 100.0 * ideal_s / step_s,
         "unit": "% of MI355X roofline",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: {c.name} {len(rows)} seeded rows x {c.Hq} heads "
+        "sample": (f"fp64 NumPy oracle: {c.name} {n_rows} seeded rows x {c.Hq} heads "
                    f"({t_pf:.2f} s incl. {t_fixed:.2f} s K/V gather; per-row part extrapolated "
-                   f"x{c.L / len(rows):.1f} to all {c.L} rows) + {d.name} "
+                   f"x{c.L / n_rows:.1f} to all {c.L} rows) + {d.name} "
                    f"bounds/selection/decode of all {d.B} sequences ({t_dec:.2f} s); "
                    f"extrapolated step {step_s:.1f} s"),
         "step_seconds_extrapolated": step_s,
         "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+        "cpu_model": _cpu_model(),
+        "per_config": per_config,
+        "one_thread": one,
     }
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ----------------------------------------------------------------------------- mask estimation
@@ -382,7 +456,7 @@ def decode_graph_step(R: int = 24, replays: int = 10):
 
 # ----------------------------------------------------------------------------- ragged decode
 
-def ragged_decode_step(steps: int, warmup: int):
+def ragged_decode_step(steps: int, warmup: int, cpu: bool = False):
     """Selection + decode on decode_ragged (B=64, L_b in [16384, 131072], Lp=16), timed alone.
 
     Not part of the step above (and not of `value`): it reports the decode path at a batch
@@ -451,6 +525,17 @@ def ragged_decode_step(steps: int, warmup: int):
                                         "gbps": round(b_r / t_r / 1e9, 1),
                                         "frac": round(b_r / t_r / 1e9 / PEAK_HBM_GBPS, 4)}}
     res["int4"] = ragged_int4(r, sel, num, sel_pages, b_select, op_select, steps, warmup)
+    if cpu:
+        # the oracle's whole step (bounds, selection, decode) on 16 seeded sequences
+        import numpy as np
+        batches = sorted(np.random.default_rng(13).choice(r.B, size=16, replace=False).tolist())
+        t = oracle_decode_sample(r, batches)
+        res["_oracle"] = {
+                          "sample": f"16 seeded sequences of {r.B} ({sum(r.seq_lens[b] for b in batches)} "
+                                    f"tokens), {t:.2f} s; the step over all {r.B} extrapolated by tokens x "
+                                    f"{sum(r.seq_lens) / sum(r.seq_lens[b] for b in batches):.2f}",
+                          "step_s_extrapolated": round(t * sum(r.seq_lens) / sum(r.seq_lens[b] for b in batches),
+                                                       2)}
     del r, bnd
     torch.cuda.empty_cache()
     return res
@@ -524,6 +609,51 @@ def ragged_int4(r, sel, num, sel_pages, b_select, op_select, steps: int, warmup:
                                              "frac": round((b_select + b_d) / t_step / 1e9 / PEAK_HBM_GBPS, 4)}}
 
 
+# ----------------------------------------------------------------------------- single prefill legs
+
+def time_calls(f, steps: int, warmup: int, stream):
+    """Mean seconds per call of f over `steps` calls, HIP events on `stream` around each."""
+    import torch
+    for _ in range(warmup):
+        f()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        f()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(e[0].elapsed_time(e[1]) * 1e-3 for e in ev)
+    return sum(ts) / len(ts), ts[0], ts[len(ts) // 2]
+
+
+def prefill_leg(c, steps: int, warmup: int, cpu_rows: int = 0):
+    """sparse_prefill of one case timed call by call: kept-tile TFLOP/s against the bf16
+    MFMA peak. With cpu_rows > 0 the oracle is timed on that many rows per head while the
+    inputs are resident."""
+    import torch
+    import unified_block_sparse_amd as ubs
+    kept = kept_tile_count(c)
+    flops = prefill_flops(c, kept)
+    out = torch.empty((c.L, c.Hq, c.D), dtype=torch.float32, device=c.q.device)
+    f = lambda: ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, c.head_kind, c.block_mask,
+                                   c.sink_tiles, c.local_tiles, c.T, c.sm_scale, out=out)
+    t, t_min, t_med = time_calls(f, steps, warmup, torch.cuda.current_stream(c.q.device))
+    res = {"workload": f"{c.name} (L={c.L}, Hq={c.Hq}, Hkv={c.Hkv}, D={c.D}, T={c.T}, P={c.P}, "
+                       f"sink {c.sink_tiles} + local {c.local_tiles} tiles on streaming heads)",
+           "calls": steps, "ms": round(t * 1e3, 4), "ms_min": round(t_min * 1e3, 4), "ms_median": round(t_med * 1e3, 4),
+           "kept_tiles": kept, "tflop": round(flops / 1e12, 4), "tflops": round(flops / t / 1e12, 2),
+           "frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del out
+    if cpu_rows:
+        t_s, t_fixed, full, n = oracle_prefill_sample(c, cpu_rows, seed=14)
+        res["_oracle"] = {"rows_per_s": round(n * c.Hq / max(t_s - t_fixed, 1e-9), 1),
+                          "sample": f"{n} seeded rows x {c.Hq} heads, {t_s:.2f} s incl. {t_fixed:.2f} s "
+                                    f"K/V gather; all {c.L} rows extrapolated",
+                          "full_config_s_extrapolated": round(full, 1)}
+    return res
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -538,6 +668,16 @@ def main():
     if args.gemm_ceiling:
         gemm_ceiling()
         return
+    legs = [x.strip() for x in args.legs.split(",") if x.strip()]
+    bad = [x for x in legs if x not in LEGS]
+    if bad:
+        print(f"unknown legs {bad}; choose from {list(LEGS)}", file=sys.stderr)
+        sys.exit(2)
+    if args.no_cpu_baseline and "cpu" in legs:
+        legs.remove("cpu")
+    if args.no_ragged and "ragged" in legs:
+        legs.remove("ragged")
+    cpu = "cpu" in legs
     import torch
     import unified_block_sparse_amd as ubs
     from workloads import cases
@@ -545,119 +685,171 @@ def main():
     ubs.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    c = cases.prefill_llama8b(dev)
-    d = cases.decode_llama8b(dev)
-    kept = kept_tile_count(c)
-    out = torch.empty((c.L, c.Hq, c.D), dtype=torch.float32, device=dev)
-    bnd = torch.zeros((d.num_physical_pages, d.Hkv, d.P // d.Lp, 2, d.D), dtype=torch.bfloat16, device=dev)
-    sel = torch.empty((d.B, d.Hkv, d.k_pages), dtype=torch.int32, device=dev)
-    num = torch.empty((d.B, d.Hkv), dtype=torch.int32, device=dev)
-    dout = torch.empty((d.B, d.Hq, d.D), dtype=torch.float32, device=dev)
-
-    def op_prefill():
-        ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, c.head_kind, c.block_mask, c.sink_tiles,
-                           c.local_tiles, c.T, c.sm_scale, out=out)
-
-    def op_bounds():
-        ubs.build_page_bounds(d.k_cache, d.page_table, d.seq_lens_t, d.head_kind, d.Lp, bounds=bnd)
-
-    def op_select():
-        ubs.select_pages(d.q, bnd, d.page_table, d.seq_lens_t, d.head_kind, d.P, d.token_budget, selected=sel,
-                         num_selected=num)
-
-    def op_decode():
-        ubs.sparse_decode(d.q, d.k_cache, d.v_cache, d.page_table, d.seq_lens_t, d.head_kind, sel, num,
-                          d.sink_tokens, d.local_tokens, d.sm_scale, out=dout)
-
-    # The bounds are built before the prefill so that the prefill's > 1.5 GB stream evicts
-    # the K pages build_page_bounds just read: selection and decode then read cold HBM.
-    ops = [("build_page_bounds", op_bounds), ("sparse_prefill", op_prefill), ("select_pages", op_select),
-           ("sparse_decode", op_decode)]
-    for _ in range(args.warmup):
-        for _, f in ops:
-            f()
-    torch.cuda.synchronize(dev)
-    sel_h, num_h = sel.cpu().tolist(), num.cpu().tolist()
-    sel_pages = [[sel_h[b][g][:num_h[b][g]] for g in range(d.Hkv)] for b in range(d.B)]
-    flops = prefill_flops(c, kept)
-    b_bounds, b_select, b_decode = decode_bytes(d, sel_pages)
-
-    # ---- timed region: K whole steps, events between the ops (same stream as the kernels)
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev[s][0].record(stream)
-        for i, (_, f) in enumerate(ops):
-            f()
-            ev[s][i + 1].record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    per_op = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps * 1e-3
-              for i, (name, _) in enumerate(ops)}
-    ms_per_step = wall / args.steps * 1e3
-    step_s = wall / args.steps
+    oracle_extra = {}
+    per_config = {}
+    legs_out = {}
+    result = None
 
-    ideal = {
-        "sparse_prefill": flops / (PEAK_BF16_TFLOPS * 1e12),
-        "build_page_bounds": b_bounds / (PEAK_HBM_GBPS * 1e9),
-        "select_pages": b_select / (PEAK_HBM_GBPS * 1e9),
-        "sparse_decode": b_decode / (PEAK_HBM_GBPS * 1e9),
-    }
-    ideal_s = sum(ideal.values())
-    value = 100.0 * ideal_s / step_s
+    if "step" in legs:
+        c = cases.prefill_llama8b(dev)
+        d = cases.decode_llama8b(dev)
+        kept = kept_tile_count(c)
+        out = torch.empty((c.L, c.Hq, c.D), dtype=torch.float32, device=dev)
+        bnd = torch.zeros((d.num_physical_pages, d.Hkv, d.P // d.Lp, 2, d.D), dtype=torch.bfloat16, device=dev)
+        sel = torch.empty((d.B, d.Hkv, d.k_pages), dtype=torch.int32, device=dev)
+        num = torch.empty((d.B, d.Hkv), dtype=torch.int32, device=dev)
+        dout = torch.empty((d.B, d.Hq, d.D), dtype=torch.float32, device=dev)
 
-    t_pf = per_op["sparse_prefill"]
-    achieved = flops / t_pf / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_source_hash") == kernel_source_hash():
-            traffic = tr.get("hbm_bytes_per_launch")
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "prefill_kernel<128,128> (sparse_prefill)", "flops_per_launch": flops,
-                "kept_tiles": kept, "avg_launch_ms": round(t_pf * 1e3, 4)}
-    t_dstep = per_op["select_pages"] + per_op["sparse_decode"]
-    breakdown = {
-        name: {"ms": round(per_op[name] * 1e3, 4), "roofline_ms": round(ideal[name] * 1e3, 4),
-               "frac": round(ideal[name] / per_op[name], 4)} for name, _ in ops}
-    breakdown["sparse_prefill"]["tflops"] = round(achieved, 2)
-    breakdown["build_page_bounds"]["gbps"] = round(b_bounds / per_op["build_page_bounds"] / 1e9, 1)
-    breakdown["select_pages"]["gbps"] = round(b_select / per_op["select_pages"] / 1e9, 1)
-    breakdown["sparse_decode"]["gbps"] = round(b_decode / per_op["sparse_decode"] / 1e9, 1)
-    breakdown["decode_step"] = {"ms": round(t_dstep * 1e3, 4), "bytes": b_select + b_decode,
-                                "gbps": round((b_select + b_decode) / t_dstep / 1e9, 1),
-                                "frac": round((b_select + b_decode) / t_dstep / 1e9 / PEAK_HBM_GBPS, 4)}
+        def op_prefill():
+            ubs.sparse_prefill(c.q, c.k_cache, c.v_cache, c.page_table, c.head_kind, c.block_mask, c.sink_tiles,
+                               c.local_tiles, c.T, c.sm_scale, out=out)
 
-    result = {
-        "metric": METRIC,
-        "value": round(value, 3),
-        "unit": "% of MI355X roofline",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "llama3_8b_layer: prefill_llama8b (L=65536, Hq=32, Hkv=8, D=128, T=128, "
-                               "half KV heads streaming) + decode_llama8b (B=4, L=32768, P=64, budget 4096)",
-                   "prefill_kept_tiles": kept, "prefill_tflop": round(flops / 1e12, 4),
-                   "decode_bytes": b_bounds + b_select + b_decode},
-        "roofline": roofline,
-        "breakdown": breakdown,
-    }
-    breakdown["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
-    breakdown["decode_step_graph"] = decode_graph_step()
-    breakdown["sparse_prefill_varlen"] = varlen_prefill(max(2, args.steps // 4), 2)
-    if not args.no_ragged:
-        breakdown["decode_ragged_step"] = ragged_decode_step(args.steps, args.warmup)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(c, d, kept, args.cpu_rows_per_head, ideal_s)
+        def op_bounds():
+            ubs.build_page_bounds(d.k_cache, d.page_table, d.seq_lens_t, d.head_kind, d.Lp, bounds=bnd)
+
+        def op_select():
+            ubs.select_pages(d.q, bnd, d.page_table, d.seq_lens_t, d.head_kind, d.P, d.token_budget, selected=sel,
+                             num_selected=num)
+
+        def op_decode():
+            ubs.sparse_decode(d.q, d.k_cache, d.v_cache, d.page_table, d.seq_lens_t, d.head_kind, sel, num,
+                              d.sink_tokens, d.local_tokens, d.sm_scale, out=dout)
+
+        # The bounds are built before the prefill so that the prefill's > 1.5 GB stream evicts
+        # the K pages build_page_bounds just read: selection and decode then read cold HBM.
+        ops = [("build_page_bounds", op_bounds), ("sparse_prefill", op_prefill), ("select_pages", op_select),
+               ("sparse_decode", op_decode)]
+        for _ in range(args.warmup):
+            for _, f in ops:
+                f()
+        torch.cuda.synchronize(dev)
+        flops = prefill_flops(c, kept)
+
+        # ---- timed region: K whole steps, events between the ops (same stream as the kernels)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            ev[s][0].record(stream)
+            for i, (_, f) in enumerate(ops):
+                f()
+                ev[s][i + 1].record(stream)
+        torch.cuda.synchronize(dev)
+        wall = time.perf_counter() - t0
+        per_op = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps * 1e-3
+                  for i, (name, _) in enumerate(ops)}
+        # the selection every timed step made (the same in each: same inputs)
+        sel_h, num_h = sel.cpu().tolist(), num.cpu().tolist()
+        sel_pages = [[sel_h[b][g][:num_h[b][g]] for g in range(d.Hkv)] for b in range(d.B)]
+        b_bounds, b_select, b_decode = decode_bytes(d, sel_pages)
+        ms_per_step = wall / args.steps * 1e3
+        step_s = wall / args.steps
+
+        ideal = {
+            "sparse_prefill": flops / (PEAK_BF16_TFLOPS * 1e12),
+            "build_page_bounds": b_bounds / (PEAK_HBM_GBPS * 1e9),
+            "select_pages": b_select / (PEAK_HBM_GBPS * 1e9),
+            "sparse_decode": b_decode / (PEAK_HBM_GBPS * 1e9),
+        }
+        ideal_s = sum(ideal.values())
+        value = 100.0 * ideal_s / step_s
+
+        t_pf = per_op["sparse_prefill"]
+        achieved = flops / t_pf / 1e12
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("kernel_source_hash") == kernel_source_hash():
+                traffic = tr.get("hbm_bytes_per_launch")
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "kernel": "prefill_kernel<128,128> (sparse_prefill)", "flops_per_launch": flops,
+                    "kept_tiles": kept, "avg_launch_ms": round(t_pf * 1e3, 4)}
+        t_dstep = per_op["select_pages"] + per_op["sparse_decode"]
+        breakdown = {
+            name: {"ms": round(per_op[name] * 1e3, 4), "roofline_ms": round(ideal[name] * 1e3, 4),
+                   "frac": round(ideal[name] / per_op[name], 4)} for name, _ in ops}
+        breakdown["sparse_prefill"]["tflops"] = round(achieved, 2)
+        breakdown["build_page_bounds"]["gbps"] = round(b_bounds / per_op["build_page_bounds"] / 1e9, 1)
+        breakdown["select_pages"]["gbps"] = round(b_select / per_op["select_pages"] / 1e9, 1)
+        breakdown["sparse_decode"]["gbps"] = round(b_decode / per_op["sparse_decode"] / 1e9, 1)
+        breakdown["decode_step"] = {"ms": round(t_dstep * 1e3, 4), "bytes": b_select + b_decode,
+                                    "gbps": round((b_select + b_decode) / t_dstep / 1e9, 1),
+                                    "frac": round((b_select + b_decode) / t_dstep / 1e9 / PEAK_HBM_GBPS, 4)}
+        per_config["prefill_llama8b"] = {"frac": round(achieved / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+                                         "ms": round(t_pf * 1e3, 4), "tflops": round(achieved, 2)}
+        result = {
+            "metric": METRIC,
+            "value": round(value, 3),
+            "unit": "% of MI355X roofline",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "llama3_8b_layer: prefill_llama8b (L=65536, Hq=32, Hkv=8, D=128, T=128, "
+                                   "half KV heads streaming) + decode_llama8b (B=4, L=32768, P=64, budget 4096)",
+                       "prefill_kept_tiles": kept, "prefill_tflop": round(flops / 1e12, 4),
+                       "decode_bytes": b_bounds + b_select + b_decode},
+            "roofline": roofline,
+            "per_config": per_config,
+            "breakdown": breakdown,
+            "context": PAGES_CONTEXT,
+        }
+        legs_out = breakdown
+        del out
+        if "mask" in legs:
+            breakdown["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
+        if cpu:
+            cpu_args = (c, d, args.cpu_rows_per_head, ideal_s)
+        else:
+            del c, d
+        torch.cuda.empty_cache()
+    elif "mask" in legs:
+        c = cases.prefill_llama8b(dev)
+        legs_out["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
+        del c
+        torch.cuda.empty_cache()
+
+    if "tiny" in legs:
+        r = prefill_leg(cases.prefill_tiny(dev), args.steps, args.warmup)
+        legs_out["prefill_tiny"] = r
+        per_config["prefill_tiny"] = {"frac": r["frac"], "bound": "mfma", "ms": r["ms"], "tflops": r["tflops"],
+                                      "note": "276 kept 64x64 tiles, 0.29 GFLOP: launch-bound, parity case"}
+    if "graph" in legs:
+        r = decode_graph_step()
+        legs_out["decode_step_graph"] = r
+        per_config["decode_llama8b_step"] = {"frac": r["frac"], "bound": "hbm", "ms": r["ms"], "gbps": r["gbps"],
+                                             "note": "select_pages + sparse_decode, HIP graph over 24 instances"}
+    if "varlen" in legs:
+        legs_out["sparse_prefill_varlen"] = varlen_prefill(max(2, args.steps // 4), 2)
+    if "ragged" in legs:
+        r = ragged_decode_step(args.steps, args.warmup, cpu=cpu)
+        if "_oracle" in r:
+            oracle_extra["decode_ragged"] = r.pop("_oracle")
+        legs_out["decode_ragged_step"] = r
+        per_config["decode_ragged_step"] = {"frac": r["frac"], "bound": "hbm", "ms": r["ms"], "gbps": r["gbps"],
+                                            "note": "select_pages + sparse_decode, 64 sequences"}
+    if "extreme" in legs:
+        c5 = cases.prefill_extreme(dev)
+        r = prefill_leg(c5, max(2, args.steps // 4), min(args.warmup, 1), cpu_rows=8 if cpu else 0)
+        del c5
+        torch.cuda.empty_cache()
+        if "_oracle" in r:
+            oracle_extra["prefill_extreme"] = r.pop("_oracle")
+        legs_out["prefill_extreme"] = r
+        per_config["prefill_extreme"] = {"frac": r["frac"], "bound": "mfma", "ms": r["ms"], "tflops": r["tflops"]}
+
+    if result is None:
+        print(json.dumps({"legs": legs_out, "per_config": per_config, "oracle": oracle_extra}), flush=True)
+        return
+    if cpu:
+        result["cpu_baseline"] = cpu_baseline(*cpu_args, oracle_extra)
     print(json.dumps(result), flush=True)
 
 

@@ -33,7 +33,11 @@
  *   must be in [0, NP); entries past a sequence's last page are never read.
  * - head_kind is HOST memory, uint8 [Hkv]: 0 = dense (retrieval) KV head,
  *   1 = streaming KV head. Query head h belongs to KV head h / (Hq / Hkv).
- *   Hkv <= 64.
+ *   Hkv <= 64. The call reads it on the host before it returns and passes the head
+ *   lists to its kernels by value, so a call captured into a HIP graph keeps the head
+ *   kinds it was captured with (like every other scalar argument): replays ignore later
+ *   changes to the array, which may be freed once the call has returned.
+ * - sm_scale (attention calls) must be finite and positive.
  * - The library never allocates device memory, never synchronises and keeps
  *   no pointer after it returns. Work is enqueued on `stream`; results are
  *   valid once the stream has reached that point, and inputs must stay alive

@@ -56,7 +56,10 @@ def _err():
     (dict(L=-1), -1, "L=-1"),
     (dict(sink=-1), -1, "sink_tiles"),
     (dict(q=A + 8), -1, "aligned"),
-    (dict(scale=float("nan")), -1, "NaN"),
+    (dict(scale=float("nan")), -1, "sm_scale"),
+    (dict(scale=0.0), -1, "sm_scale"),
+    (dict(scale=-0.1), -1, "sm_scale"),
+    (dict(scale=float("inf")), -1, "sm_scale"),
 ])
 def test_prefill_validation(kw, code, frag):
     assert _prefill(**kw) == code
@@ -133,7 +136,7 @@ def _decode(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(P=40), -2), (dict(P=512), -2), (dict(Hq=24), -2), (dict(Hq=136, Hkv=8), -2), (dict(D=80), -2),
     (dict(sink=-1), -1), (dict(wsb=100), -3), (dict(nsel=None), -1), (dict(out=None), -1),
-    (dict(k=A + 4), -1),
+    (dict(k=A + 4), -1), (dict(scale=0.0), -1), (dict(scale=-1.0), -1), (dict(scale=float("nan")), -1),
 ])
 def test_decode_validation(kw, code):
     assert _decode(**kw) == code

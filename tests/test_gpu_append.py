@@ -68,7 +68,8 @@ def test_append_matches_oracle(n_new, P, Lp):
 
 
 def test_append_decode_loop_keeps_bounds_exact():
-    """Twenty single-token appends (a decode loop) leave the same bounds as one full build."""
+    """Twenty single-token appends (a decode loop): the bounds they leave equal the oracle's
+    bounds of the final sequences bit for bit (and so equal one full build)."""
     n_steps = 20
     final = [1000, 129, 64 * 7]
     d, kind, old = _setup(final, n_steps, 64, 16, 2203)
@@ -80,8 +81,10 @@ def test_append_decode_loop_keeps_bounds_exact():
         kn, vn = _gather_new(k_full, d, cur, 1), _gather_new(v_full, d, cur, 1)
         ubs.append_kv(kn, vn, d.page_table, lens, kind, d.k_cache, d.v_cache, bounds=bnd, Lp=16)
         lens += 1
-    ref = ubs.build_page_bounds(k_full, d.page_table, lens, kind, 16)
     torch.cuda.synchronize(DEV)
+    assert lens.cpu().tolist() == final
     pt = d.page_table.cpu().numpy()
-    _, defined = oracle.bounds_ref(bits(k_full), pt, final, 64, 16, kind)
-    assert np.array_equal(bits(bnd)[defined], bits(ref)[defined])
+    assert np.array_equal(bits(d.k_cache), bits(k_full)) and np.array_equal(bits(d.v_cache), bits(v_full))
+    vals, defined = oracle.bounds_ref(bits(k_full), pt, final, 64, 16, kind)
+    got = oracle.bf16_to_f64(bits(bnd))
+    assert defined.any() and np.array_equal(got[defined], vals[defined])

@@ -2,8 +2,8 @@
 
 prefill_tiny and decode_llama8b are compared in full. For the large ones the oracle
 evaluates samples: 64 query rows per head of prefill_llama8b ({0, T-1, T, L-1} plus
-seeded rows), 32 per head of prefill_extreme, and 4 seeded sequences of
-decode_ragged (every page of each, every head)."""
+seeded rows), 32 per head of prefill_extreme; decode_ragged is compared on all 64
+sequences (every page of each, every head), 16 per test."""
 import numpy as np
 import pytest
 import torch
@@ -119,12 +119,26 @@ def test_decode_llama8b_full():
     _decode_parity(c, list(range(c.B)), "decode_llama8b")
 
 
-def test_decode_ragged_sampled_sequences():
+@pytest.fixture(scope="module")
+def ragged_case():
     c = cases.decode_ragged(DEV)
-    rng = np.random.default_rng(4)
-    longest = int(np.argmax(c.seq_lens))
-    batches = sorted(set([longest] + rng.choice(c.B, size=3, replace=False).tolist()))
-    _decode_parity(c, batches, "decode_ragged")
+    yield c
+    del c
+    torch.cuda.empty_cache()
+
+
+RAGGED_PARTS = 4   # the 64 sequences in four groups of 16 (bounded host memory per test)
+
+
+@pytest.mark.parametrize("part", range(RAGGED_PARTS))
+def test_decode_ragged_every_sequence(ragged_case, part):
+    """All 64 sequences of decode_ragged (the shortest and the longest among them), a
+    group of 16 per test: bounds bit-exact, selection to the threshold band, decode on the
+    oracle's selection."""
+    c = ragged_case
+    n = c.B // RAGGED_PARTS
+    batches = list(range(part * n, (part + 1) * n))
+    _decode_parity(c, batches, f"decode_ragged sequences {batches[0]}-{batches[-1]}")
 
 
 def test_decode_reused_selection():

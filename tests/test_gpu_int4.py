@@ -1,7 +1,7 @@
 """INT4 KV pages on the GPU against the oracle: quantize_kv_int4 bit-exact (codes and
 fp16 params of every valid row; other rows untouched), sparse_decode_int4 on the
 oracle's codes and selection within the attention tolerance, and both at the ragged
-serving shape on sampled sequences."""
+serving shape on all of its sequences."""
 import numpy as np
 import pytest
 import torch
@@ -124,13 +124,23 @@ def test_int4_pipeline_close_to_bf16_decode():
     assert d.mean().item() < 0.2 and d.max().item() < 3.0, (d.mean().item(), d.max().item())
 
 
-def test_int4_ragged_sampled_sequences():
+@pytest.fixture(scope="module")
+def ragged_int4():
     c = cases.decode_ragged(DEV)
-    rng = np.random.default_rng(9)
-    longest = int(np.argmax(c.seq_lens))
-    batches = sorted(set([longest] + rng.choice(c.B, size=2, replace=False).tolist()))
     kc, vc, kp, vp = ubs.quantize_kv_int4(c.k_cache, c.v_cache, c.page_table, c.seq_lens_t)
     _sync()
+    yield c, kc, vc, kp, vp
+    del c, kc, vc, kp, vp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_int4_ragged_every_sequence(ragged_int4, part):
+    """All 64 sequences of decode_ragged, 16 per test: codes and params bit-exact, decode
+    over the oracle's codes and selection within the attention tolerance."""
+    c, kc, vc, kp, vp = ragged_int4
+    n = c.B // 4
+    batches = list(range(part * n, (part + 1) * n))
     qb, kb, vb, pt, lens = decode_subset(c, batches)
     kq, vq, kpr, vpr, written = oracle.quantize_cache_int4_ref(kb, vb, pt, lens, c.P)
     pages = torch.tensor([int(c.page_table[b, j]) for b in batches for j in range((c.seq_lens[b] + c.P - 1) // c.P)],

@@ -69,7 +69,10 @@ def test_mask_small_cases(L, Hq, Hkv, D, P, T, keep):
     n = (L + P - 1) // P
     q = gen.normal_bf16((L, Hq, D), 2001, 1, DEV)
     k_cache = gen.normal_bf16((n + 3, Hkv, P, D), 2001, 2, DEV)
-    pt = gen.randperm(n + 3, 2001, 3, DEV)[:n].to(torch.int32).contiguous()
+    # an exactly sized page table (its own allocation, not a view of a longer one), so that
+    # a read past entry n - 1 would leave the table
+    pt = gen.randperm(n + 3, 2001, 3, DEV)[:n].to(torch.int32).clone()
+    assert pt.numel() == n and pt.untyped_storage().nbytes() == 4 * n
     _run(q, k_cache, pt, L, Hq, Hkv, D, P, T, kind, keep, f"mask L={L} D={D} T={T}", fill=7)
 
 

@@ -15,7 +15,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libubs.so")
+# UBS_LIBRARY names another build of the same library (the host-sanitizer build that the
+# CPU-side ABI tests run under); by default the in-tree libubs.so
+LIB_PATH = os.environ.get("UBS_LIBRARY") or os.path.join(_HERE, "libubs.so")
 
 UBS_OK = 0
 ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}

@@ -1,5 +1,6 @@
 // C ABI of libubs: argument validation (host only, before any HIP call), workspace
 // sizing and dispatch to the gfx950 kernels. See include/ubs.h for the contract.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -103,7 +104,8 @@ int sparse_prefill_chunk(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const u
   REQUIRE(Hq <= ubs::kMaxQHeads, UBS_ERR_UNSUPPORTED, "Hq=%d above %d", Hq, ubs::kMaxQHeads);
   REQUIRE(sink_tiles >= 0 && local_tiles >= 0, UBS_ERR_INVALID_ARGUMENT,
           "sink_tiles=%d, local_tiles=%d must be >= 0", sink_tiles, local_tiles);
-  REQUIRE(sm_scale == sm_scale, UBS_ERR_INVALID_ARGUMENT, "sm_scale is NaN");
+  REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, UBS_ERR_INVALID_ARGUMENT,
+          "sm_scale=%g must be finite and positive", (double)sm_scale);
   ubs::HeadList dense, streaming;
   uint64_t smask;
   rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
@@ -158,7 +160,8 @@ int sparse_prefill_varlen(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const 
   REQUIRE(Hq <= ubs::kMaxQHeads, UBS_ERR_UNSUPPORTED, "Hq=%d above %d", Hq, ubs::kMaxQHeads);
   REQUIRE(sink_tiles >= 0 && local_tiles >= 0, UBS_ERR_INVALID_ARGUMENT,
           "sink_tiles=%d, local_tiles=%d must be >= 0", sink_tiles, local_tiles);
-  REQUIRE(sm_scale == sm_scale, UBS_ERR_INVALID_ARGUMENT, "sm_scale is NaN");
+  REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, UBS_ERR_INVALID_ARGUMENT,
+          "sm_scale=%g must be finite and positive", (double)sm_scale);
   REQUIRE((int64_t)max_pages * P >= max_seqlen, UBS_ERR_INVALID_ARGUMENT,
           "max_pages=%d pages of %d tokens cannot hold max_seqlen=%d", max_pages, P, max_seqlen);
   ubs::HeadList dense, streaming;
@@ -321,7 +324,8 @@ static int decode_impl(const char* name, bool int4, const ubs_bf16_t* q, const v
   REQUIRE(max_selected >= 0 && sink_tokens >= 0 && local_tokens >= 0, UBS_ERR_INVALID_ARGUMENT,
           "max_selected=%d, sink_tokens=%d, local_tokens=%d must be >= 0", max_selected, sink_tokens,
           local_tokens);
-  REQUIRE(sm_scale == sm_scale, UBS_ERR_INVALID_ARGUMENT, "sm_scale is NaN");
+  REQUIRE(std::isfinite(sm_scale) && sm_scale > 0.f, UBS_ERR_INVALID_ARGUMENT,
+          "sm_scale=%g must be finite and positive", (double)sm_scale);
   ubs::HeadList dense, streaming;
   uint64_t smask;
   rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);

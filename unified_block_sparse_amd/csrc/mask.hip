@@ -44,10 +44,13 @@ __global__ __launch_bounds__(256) void tile_mean_kernel(const MaskArgs a) {
   u32x4 v[MAXR];
 #pragma unroll
   for (int x = 0; x < MAXR; ++x) {
+    // (rows past the tile's end are clamped to its last row for the address, so that no
+    // page-table entry past the sequence is read; their values are not used)
     const int r = r0 + rr + x * RPP;
+    const int rc = min(r, r1 - 1);
     const uint16_t* src =
-        isq ? a.q + ((int64_t)r * a.Hq + h) * D + cc * 8
-            : a.k_cache + (((int64_t)a.page_table[r >> a.log2_P] * a.Hkv + g) * a.P + (r & (a.P - 1))) * D + cc * 8;
+        isq ? a.q + ((int64_t)rc * a.Hq + h) * D + cc * 8
+            : a.k_cache + (((int64_t)a.page_table[rc >> a.log2_P] * a.Hkv + g) * a.P + (rc & (a.P - 1))) * D + cc * 8;
     v[x] = (r < r1) ? ld16(src) : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
