@@ -64,6 +64,7 @@ typedef uint16_t ubs_bf16_t; /* raw bfloat16 bits */
 #define UBS_ERR_UNSUPPORTED (-2)      /* a size outside the shapes the kernels implement */
 #define UBS_ERR_WORKSPACE_TOO_SMALL (-3)
 #define UBS_ERR_HIP (-4)              /* a HIP launch failed; message from the runtime */
+#define UBS_ERR_OUT_OF_RANGE (-5)     /* checked mode: an index input outside its range */
 
 /* Thread-local description of the last failing call (empty string if none). */
 const char* ubs_last_error(void);
@@ -362,6 +363,37 @@ int estimate_block_mask(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const in
                         int32_t L, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t T,
                         const uint8_t* head_kind /* host */, int32_t keep_num, int32_t keep_den,
                         uint8_t* block_mask, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Checked mode -- device-side validation of the index inputs every paged call trusts.
+ *
+ * The kernels read through page ids, sequence lengths and selected page lists without
+ * bounds checks (page ids must lie in [0, NP), which no call can know). A caller that
+ * wants them verified enqueues ubs_check_paged on the stream before the calls, and asks
+ * ubs_check_status afterwards. What is checked, for every sequence b < B:
+ *   - its length L_b (seq_lens[b], or cu_seqlens[b+1] - cu_seqlens[b] with cu_seqlens
+ *     starting at 0 and not decreasing) lies in [0, max_pages * P];
+ *   - page_table[b][j] lies in [0, num_pages) for every page j < ceil(L_b / P) of it;
+ *   - when selected is given: for every DENSE KV head g (head_kind, host), num_selected
+ *     [b][g] lies in [0, min(max_selected, ceil(L_b / P))] and selected[b][g][0 .. n) are
+ *     pages of the sequence, strictly ascending (as select_pages writes them).
+ * The first violation found is recorded in `status` (device memory, at least
+ * UBS_CHECK_STATUS_BYTES bytes, 4-byte aligned, zeroed by the caller before its first
+ * use; later checks keep a recorded violation until it is reported). Arguments follow the
+ * conventions above: page_table int32 [B][max_pages]; exactly one of seq_lens (int32
+ * [B]) and cu_seqlens (int32 [B + 1]) non-NULL; selected int32 [B][Hkv][max_selected]
+ * and num_selected int32 [B][Hkv], or both NULL.
+ *
+ * ubs_check_status waits for `stream` (the one call here that synchronises), reads the
+ * record and returns UBS_OK, or UBS_ERR_OUT_OF_RANGE with ubs_last_error() naming the
+ * violation; it then clears the record.
+ */
+#define UBS_CHECK_STATUS_BYTES 64
+int ubs_check_paged(const int32_t* page_table, int32_t B, int32_t max_pages, const int32_t* seq_lens,
+                    const int32_t* cu_seqlens, int32_t num_pages, int32_t P, const uint8_t* head_kind /* host */,
+                    int32_t Hkv, const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
+                    void* status, hipStream_t stream);
+int ubs_check_status(void* status, hipStream_t stream);
 
 #ifdef __cplusplus
 }

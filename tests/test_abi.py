@@ -325,3 +325,4 @@ def test_prefill_varlen_validation(kw, code, frag):
 def test_prefill_varlen_nothing_to_do():
     assert _varlen(B=0, q=None, k=None, v=None, pt=None, cu=None, mask=None, out=None) == 0
     assert _varlen(tot=0, q=None, k=None, v=None, pt=None, cu=None, mask=None, out=None) == 0
+

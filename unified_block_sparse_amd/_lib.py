@@ -20,10 +20,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("UBS_LIBRARY") or os.path.join(_HERE, "libubs.so")
 
 UBS_OK = 0
-ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR"}
+ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL", -4: "HIP_ERROR",
+             -5: "OUT_OF_RANGE"}
+CHECK_STATUS_BYTES = 64
 EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "sparse_prefill_varlen", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
             "append_kv", "quantize_kv_int4", "sparse_decode_int4",
+            "ubs_check_paged", "ubs_check_status",
             "ubs_last_error", "ubs_version")
 
 
@@ -85,6 +88,10 @@ def load() -> ctypes.CDLL:
         lib.ubs_mask_workspace_size.argtypes = [_i, _i, _i, _i, _i]
         lib.estimate_block_mask.restype = ctypes.c_int
         lib.estimate_block_mask.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _i, _i, _p, _p, _sz, _p]
+        lib.ubs_check_paged.restype = ctypes.c_int
+        lib.ubs_check_paged.argtypes = [_p, _i, _i, _p, _p, _i, _i, _p, _i, _p, _p, _i, _p, _p]
+        lib.ubs_check_status.restype = ctypes.c_int
+        lib.ubs_check_status.argtypes = [_p, _p]
         _lib = lib
         return lib
 
@@ -530,3 +537,46 @@ def append_kv(k_new: torch.Tensor, v_new: torch.Tensor, page_table: torch.Tensor
                        Hkv, D, P, int(Lp if Lp is not None else P), _kinds(head_kind), _ptr(k_cache), _ptr(v_cache),
                        _ptr(bounds), _stream(dev))
     _check("append_kv", rc)
+
+
+def check_paged(page_table: torch.Tensor, num_pages: int, P: int, seq_lens: Optional[torch.Tensor] = None,
+                cu_seqlens: Optional[torch.Tensor] = None, head_kind: Optional[Sequence[int]] = None,
+                selected: Optional[torch.Tensor] = None, num_selected: Optional[torch.Tensor] = None,
+                status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Checked mode: enqueue the device-side validation of page ids, lengths and (when
+    given) the selection; returns the status record to pass to check_status."""
+    lib = load()
+    if page_table.dim() == 1:
+        page_table = page_table.view(1, -1)
+    B, max_pages = page_table.shape
+    dev = page_table.device
+    _need(page_table, "page_table", torch.int32, device=dev)
+    if (seq_lens is None) == (cu_seqlens is None):
+        raise ValueError("give exactly one of seq_lens and cu_seqlens")
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    else:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, shape=(B + 1,), device=dev)
+    if status is None:
+        status = torch.zeros(CHECK_STATUS_BYTES // 4, dtype=torch.int32, device=dev)
+    _need(status, "status", torch.int32, device=dev)
+    Hkv, ms, kinds = 0, 0, None
+    if selected is not None:
+        if head_kind is None or num_selected is None:
+            raise ValueError("selected needs head_kind and num_selected")
+        _, Hkv, ms = selected.shape
+        _need(selected, "selected", torch.int32, shape=(B, Hkv, ms), device=dev)
+        _need(num_selected, "num_selected", torch.int32, shape=(B, Hkv), device=dev)
+        kinds = _kinds(head_kind)
+    rc = lib.ubs_check_paged(_ptr(page_table), B, max_pages, _ptr(seq_lens), _ptr(cu_seqlens), int(num_pages), P,
+                             kinds, Hkv, _ptr(selected), _ptr(num_selected), ms, _ptr(status), _stream(dev))
+    _check("ubs_check_paged", rc)
+    return status
+
+
+def check_status(status: torch.Tensor) -> None:
+    """Wait for the stream, then raise UBSError (OUT_OF_RANGE) if a violation was recorded
+    (the record is cleared)."""
+    lib = load()
+    rc = lib.ubs_check_status(_ptr(status), _stream(status.device))
+    _check("ubs_check_status", rc)

@@ -519,4 +519,76 @@ int append_kv(const ubs_bf16_t* k_new, const ubs_bf16_t* v_new, const int32_t* p
   return hip_status(ubs::launch_bounds(b, stream), "append_kv bounds launch");
 }
 
+int ubs_check_paged(const int32_t* page_table, int32_t B, int32_t max_pages, const int32_t* seq_lens,
+                    const int32_t* cu_seqlens, int32_t num_pages, int32_t P, const uint8_t* head_kind, int32_t Hkv,
+                    const int32_t* selected, const int32_t* num_selected, int32_t max_selected, void* status,
+                    hipStream_t stream) {
+  REQUIRE(B >= 0 && max_pages >= 0 && num_pages >= 0 && max_selected >= 0, UBS_ERR_INVALID_ARGUMENT,
+          "B=%d, max_pages=%d, num_pages=%d, max_selected=%d must be >= 0", B, max_pages, num_pages, max_selected);
+  REQUIRE(P > 0, UBS_ERR_INVALID_ARGUMENT, "P=%d must be positive", P);
+  REQUIRE((seq_lens == nullptr) != (cu_seqlens == nullptr), UBS_ERR_INVALID_ARGUMENT,
+          "exactly one of seq_lens and cu_seqlens must be given");
+  REQUIRE(status != nullptr && ((uintptr_t)status % 4) == 0, UBS_ERR_INVALID_ARGUMENT,
+          "status must be a 4-byte aligned device buffer of UBS_CHECK_STATUS_BYTES bytes");
+  ubs::HeadList dense, streaming;
+  uint64_t smask;
+  if (selected) {
+    REQUIRE(num_selected != nullptr, UBS_ERR_INVALID_ARGUMENT, "num_selected is NULL but selected is given");
+    int rc = head_lists(head_kind, Hkv, &dense, &streaming, &smask);
+    if (rc) return rc;
+  } else {
+    dense.n = 0;
+  }
+  if (B == 0) return ok();
+  REQUIRE(page_table != nullptr || max_pages == 0, UBS_ERR_INVALID_ARGUMENT, "page_table is NULL");
+  ubs::CheckArgs a{};
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.cu_seqlens = cu_seqlens;
+  a.B = B;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.P = P;
+  a.Hkv = selected ? Hkv : 0;
+  a.dense = dense;
+  a.selected = (selected && dense.n > 0 && max_selected > 0) ? selected : nullptr;
+  a.num_selected = num_selected;
+  a.max_selected = max_selected;
+  a.status = static_cast<int32_t*>(status);
+  return hip_status(ubs::launch_check(a, stream), "ubs_check_paged launch");
+}
+
+int ubs_check_status(void* status, hipStream_t stream) {
+  REQUIRE(status != nullptr, UBS_ERR_INVALID_ARGUMENT, "status is NULL");
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "ubs_check_status: stream synchronisation");
+  int32_t st[5] = {0, 0, 0, 0, 0};
+  e = hipMemcpy(st, status, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_status(e, "ubs_check_status: reading the status record");
+  if (st[0] == 0) return ok();
+  const int32_t zero[5] = {0, 0, 0, 0, 0};
+  e = hipMemcpy(status, zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_status(e, "ubs_check_status: clearing the status record");
+  switch (st[0]) {
+    case ubs::kCheckSeqLen:
+      return fail(UBS_ERR_OUT_OF_RANGE, "sequence %d: length %d outside [0, max_pages * P]", st[1], st[3]);
+    case ubs::kCheckCuSeqlens:
+      return fail(UBS_ERR_OUT_OF_RANGE, "cu_seqlens[%d] = %d: offsets must start at 0 and not decrease", st[2],
+                  st[3]);
+    case ubs::kCheckPageId:
+      return fail(UBS_ERR_OUT_OF_RANGE, "page_table[%d][%d] = %d is outside [0, num_pages)", st[1], st[2], st[3]);
+    case ubs::kCheckNumSelected:
+      return fail(UBS_ERR_OUT_OF_RANGE, "num_selected[%d][%d] = %d exceeds max_selected or the sequence's pages",
+                  st[1], st[4], st[3]);
+    case ubs::kCheckSelected:
+      return fail(UBS_ERR_OUT_OF_RANGE, "selected[%d][%d][%d] = %d is not a page of the sequence", st[1], st[4],
+                  st[2], st[3]);
+    case ubs::kCheckSelectedOrder:
+      return fail(UBS_ERR_OUT_OF_RANGE, "selected[%d][%d] is not strictly ascending at slot %d (%d)", st[1], st[4],
+                  st[2], st[3]);
+    default:
+      return fail(UBS_ERR_OUT_OF_RANGE, "violation of kind %d recorded", st[0]);
+  }
+}
+
 }  // extern "C"

@@ -31,6 +31,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace ubs {
 
@@ -629,6 +630,12 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   const int64_t total = (int64_t)B * ((int64_t)n_dense * pl.chunks_dense + (int64_t)(Hkv - n_dense) * pl.chunks_stream);
   constexpr int64_t kWaveSlots = 4 * 2 * 256;
   int cpw = (int)std::min<int64_t>(8, std::max<int64_t>(4, (total + kWaveSlots - 1) / kWaveSlots));
+  // (measurement override: UBS_DECODE_CPW sets the chunks per wave; the result does not
+  // depend on it beyond the order of the split merge)
+  if (const char* e = getenv("UBS_DECODE_CPW")) {
+    const int v = atoi(e);
+    if (v >= 1 && v <= 64) cpw = v;
+  }
   for (;;) {
     const int sd = n_dense > 0 ? (pl.chunks_dense + 4 * cpw - 1) / (4 * cpw) : 1;
     const int ss = (Hkv - n_dense) > 0 ? (pl.chunks_stream + 4 * cpw - 1) / (4 * cpw) : 1;

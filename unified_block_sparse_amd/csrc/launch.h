@@ -119,6 +119,29 @@ struct MaskArgs {
   float* kmean;          // workspace [n_dense_kv][nT][D]
 };
 
+// Checked mode: what ubs_check_paged validates and the status record it fills
+// (int32 [kind, b, index, value, head]; kind 0 = no violation).
+enum CheckKind : int {
+  kCheckSeqLen = 1,         // seq_lens[b] (or a cu_seqlens length) outside [0, max_pages * P]
+  kCheckCuSeqlens = 2,      // cu_seqlens not starting at 0 or decreasing
+  kCheckPageId = 3,         // page_table[b][j] outside [0, num_pages) for a page of the sequence
+  kCheckNumSelected = 4,    // num_selected[b][g] outside [0, min(max_selected, pages of b)]
+  kCheckSelected = 5,       // selected[b][g][slot] outside [0, pages of b)
+  kCheckSelectedOrder = 6,  // selected[b][g] not strictly ascending
+};
+struct CheckArgs {
+  const int32_t* page_table;
+  const int32_t* seq_lens;     // or
+  const int32_t* cu_seqlens;   // [B + 1]
+  int B, max_pages, num_pages, P, Hkv;
+  HeadList dense;
+  const int32_t* selected;     // NULL: no selection to check
+  const int32_t* num_selected;
+  int max_selected;
+  int32_t* status;
+};
+hipError_t launch_check(const CheckArgs& a, hipStream_t s);
+
 // Decode split planning (shared by the workspace query and the launch).
 struct DecodePlan {
   int chunks_dense, chunks_stream;  // upper bounds of key chunks per (b, KV head)

@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
                                                    int32_t* __restrict__ num_selected) {
   __shared__ int tmp[4];
   __shared__ int cnt[2][4];
+  __shared__ uint32_t rng[2][4];
   const int bg = blockIdx.x;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
@@ -178,19 +179,39 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   }
   const float* sc = scores + (int64_t)bg * max_pages;
   uint32_t key[EPT];
+  uint32_t kmin = ~0u, kmax = 0u;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const int j = tid * EPT + e;
     key[e] = (j < n) ? float_order_key(sc[j]) : 0u;  // valid keys are > 0
+    if (j < n) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
   }
   // k-th largest key: the largest tau with #(key >= tau) >= k. A candidate with exactly
   // k keys at or above it ends the search early: those keys are the k largest, with no
   // tie at the threshold (it falls between the k-th and the (k+1)-th key, whose bits
   // first differ at this round), and the selection below takes exactly them. (total
   // is the same in every thread, so the exit is uniform.)
-  uint32_t tau = 0;
   const int w = tid >> 6, lane = lane_id();
-  for (int bit = 31; bit >= 0; --bit) {
+  // every key, and so the k-th largest, shares the bits above the first bit where the
+  // smallest and the largest key differ: the search starts there
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) {
+    rng[0][w] = kmin;
+    rng[1][w] = kmax;
+  }
+  __syncthreads();
+  kmin = min(min(rng[0][0], rng[0][1]), min(rng[0][2], rng[0][3]));
+  kmax = max(max(rng[1][0], rng[1][1]), max(rng[1][2], rng[1][3]));
+  const int top = kmin == kmax ? -1 : 31 - __builtin_clz(kmin ^ kmax);
+  uint32_t tau = kmin == kmax ? kmax : (top == 31 ? 0u : (kmax & ~((2u << top) - 1u)));
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = tau | (1u << bit);
     int c = 0;
 #pragma unroll
