@@ -261,6 +261,33 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * sparse_decode_static -- sparse_decode that allocates nothing and takes no workspace.
+ *
+ * For callers that cannot allocate device memory or manage a workspace: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The arguments,
+ * key sets, results and supported shapes are those of sparse_decode, minus workspace and
+ * workspace_bytes; the same kernels run. The split partials live in a library-owned
+ * scratch array of UBS_STATIC_SCRATCH_BYTES in device memory: one copy per GPU, loaded
+ * with the library's code and held until the process ends; its device address is looked
+ * up on the first call on each device (the calling thread's current device must be the
+ * device of `stream` and of the pointers).
+ * - A call needing more than UBS_STATIC_SCRATCH_BYTES of partials
+ *   (ubs_decode_workspace_size(...) > UBS_STATIC_SCRATCH_BYTES) returns
+ *   UBS_ERR_WORKSPACE_TOO_SMALL before any HIP call.
+ * - Every call on one GPU shares that GPU's scratch. Calls that may overlap on one GPU
+ *   (different streams, or threads enqueueing concurrently) race on it and must be
+ *   ordered by the caller. Nothing in the scratch needs clearing: each call writes every
+ *   partial it reads.
+ */
+#define UBS_STATIC_SCRATCH_BYTES (16u << 20)
+int sparse_decode_static(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                         const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind /* host */,
+                         const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
+                         int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
+                         hipStream_t stream);
+
+/*
  * INT4 KV pages -- quantize_kv_int4 and sparse_decode_int4.
  *
  * The blog's "LServe -- Decode Phase" section and its Figure 2 caption: INT4 KV

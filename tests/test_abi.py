@@ -326,3 +326,18 @@ def test_prefill_varlen_nothing_to_do():
     assert _varlen(B=0, q=None, k=None, v=None, pt=None, cu=None, mask=None, out=None) == 0
     assert _varlen(tot=0, q=None, k=None, v=None, pt=None, cu=None, mask=None, out=None) == 0
 
+
+def test_decode_static_rejects_oversized_scratch_before_any_hip_call():
+    """sparse_decode_static keeps its split partials in a 16 MiB library-owned scratch: a
+    call needing more is refused with WORKSPACE_TOO_SMALL, validated on the host."""
+    lib = ubs.load()
+    B, Hq, Hkv, D, P, ms = 1024, 32, 8, 128, 64, 64
+    need = lib.ubs_decode_workspace_size(B, Hq, Hkv, D, P, ms, 128, 512)
+    assert need > 16 << 20
+    rc = lib.sparse_decode_static(A, A, A, A, A, B, 512, Hq, Hkv, D, P, KIND, A, A, ms, 128, 512, 0.088, A, NULL,
+                                  NULL)
+    assert rc == -3 and "static scratch" in _err()
+    assert lib.sparse_decode_static(A, A, A, A, A, 4, 512, Hq, Hkv, 96, P, KIND, A, A, ms, 128, 512, 0.088, A,
+                                    NULL, NULL) == -2
+    assert lib.sparse_decode_static(A, A, A, A, A, 0, 512, Hq, Hkv, D, P, KIND, A, A, ms, 128, 512, 0.088, A,
+                                    NULL, NULL) == 0

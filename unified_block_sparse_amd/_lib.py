@@ -25,7 +25,7 @@ ERR_NAMES = {-1: "INVALID_ARGUMENT", -2: "UNSUPPORTED", -3: "WORKSPACE_TOO_SMALL
 CHECK_STATUS_BYTES = 64
 EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "sparse_prefill_varlen", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
-            "append_kv", "quantize_kv_int4", "sparse_decode_int4",
+            "append_kv", "quantize_kv_int4", "sparse_decode_int4", "sparse_decode_static",
             "ubs_check_paged", "ubs_check_status",
             "ubs_last_error", "ubs_version")
 
@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
         lib.sparse_decode_int4.restype = ctypes.c_int
         lib.sparse_decode_int4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i,
                                            _i, _f, _p, _p, _p, _sz, _p]
+        lib.sparse_decode_static.restype = ctypes.c_int
+        lib.sparse_decode_static.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _i,
+                                             _f, _p, _p, _p]
         lib.quantize_kv_int4.restype = ctypes.c_int
         lib.quantize_kv_int4.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p]
         lib.append_kv.restype = ctypes.c_int

@@ -79,6 +79,7 @@ int paged_P(int P) {
 }
 
 constexpr int kMaxSelectPages = 16384;
+static_assert(UBS_STATIC_SCRATCH_BYTES == ubs::kStaticScratchBytes, "static scratch size in ubs.h and launch.h");
 
 }  // namespace
 
@@ -309,7 +310,7 @@ size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
 
 // Shared body of sparse_decode (bf16 pages: k, v are the caches) and sparse_decode_int4
 // (k, v are the code arrays, kp, vp the row params).
-static int decode_impl(const char* name, bool int4, const ubs_bf16_t* q, const void* k, const void* v,
+static int decode_impl(const char* name, bool int4, bool use_static, const ubs_bf16_t* q, const void* k, const void* v,
                        const uint16_t* kp, const uint16_t* vp, const int32_t* page_table, const int32_t* seq_lens,
                        int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                        const uint8_t* head_kind, const int32_t* selected, const int32_t* num_selected,
@@ -346,6 +347,14 @@ static int decode_impl(const char* name, bool int4, const ubs_bf16_t* q, const v
           "selected / num_selected are NULL but a KV head is dense");
   REQUIRE(dense.n == 0 || num_selected, UBS_ERR_INVALID_ARGUMENT, "num_selected is NULL but a KV head is dense");
   const size_t need = ubs_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens);
+  if (use_static) {
+    REQUIRE(need <= ubs::kStaticScratchBytes, UBS_ERR_WORKSPACE_TOO_SMALL,
+            "%s needs %zu bytes of scratch for B=%d, Hq=%d, D=%d; its static scratch holds %zu "
+            "(use sparse_decode with a workspace)", name, need, B, Hq, D, ubs::kStaticScratchBytes);
+    const hipError_t e = ubs::static_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e, "static scratch address");
+    workspace_bytes = ubs::kStaticScratchBytes;
+  }
   REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
           "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens);
@@ -396,9 +405,20 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
                   const int32_t* num_selected, int32_t max_selected, int32_t sink_tokens, int32_t local_tokens,
                   float sm_scale, float* out, float* lse, void* workspace, size_t workspace_bytes,
                   hipStream_t stream) {
-  return decode_impl("sparse_decode", false, q, k_cache, v_cache, nullptr, nullptr, page_table, seq_lens, B,
+  return decode_impl("sparse_decode", false, false, q, k_cache, v_cache, nullptr, nullptr, page_table, seq_lens, B,
                      max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, max_selected, sink_tokens,
                      local_tokens, sm_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+int sparse_decode_static(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
+                         const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind,
+                         const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
+                         int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
+                         hipStream_t stream) {
+  return decode_impl("sparse_decode_static", false, true, q, k_cache, v_cache, nullptr, nullptr, page_table,
+                     seq_lens, B, max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, max_selected,
+                     sink_tokens, local_tokens, sm_scale, out, lse, nullptr, 0, stream);
 }
 
 int sparse_decode_int4(const ubs_bf16_t* q, const uint8_t* k_codes, const uint8_t* v_codes, const uint16_t* k_params,
@@ -407,7 +427,7 @@ int sparse_decode_int4(const ubs_bf16_t* q, const uint8_t* k_codes, const uint8_
                        const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
                        int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return decode_impl("sparse_decode_int4", true, q, k_codes, v_codes, k_params, v_params, page_table, seq_lens, B,
+  return decode_impl("sparse_decode_int4", true, false, q, k_codes, v_codes, k_params, v_params, page_table, seq_lens, B,
                      max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, max_selected, sink_tokens,
                      local_tokens, sm_scale, out, lse, workspace, workspace_bytes, stream);
 }

@@ -32,6 +32,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 
 namespace ubs {
 
@@ -649,6 +650,39 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   }
   pl.max_splits = pl.splits_dense > pl.splits_stream ? pl.splits_dense : pl.splits_stream;
   return pl;
+}
+
+// ----------------------------------------------------------------------------- static scratch
+//
+// The split partials of sparse_decode_static: a file-scope device array instead of a
+// caller workspace, for callers that cannot allocate. Each GPU the library runs on holds
+// its own copy (loaded with the code object) until the process ends. Host code never
+// passes the array's name to a kernel (there it names a host-side stand-in): the first
+// call on a device resolves the device address with hipGetSymbolAddress, with that device
+// current, and keeps it per device; every later use goes through that address.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {

@@ -150,6 +150,11 @@ struct DecodePlan {
 };
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local);
 
+// Size of the library-owned scratch of sparse_decode_static (per GPU), and its device
+// address on the current device (resolved on the first call there).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
