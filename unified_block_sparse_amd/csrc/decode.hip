@@ -3,12 +3,16 @@
 // Figure 2: token-level attention only inside the selected pages; LServe abstract:
 // streaming heads in decode as well).
 //
-// Work split: (sequence b, KV head g, split s) per 256-thread work-group. The key set
-// of (b, g) is a list of 32-token chunks, each inside one physical page (a part of a
-// selected page, or of a page of the sink / local window); wave w of split s streams
-// chunks (s*4 + w)*cpw ... + cpw - 1. It first resolves all their pages (one round
-// trip through the selection and the page table for up to 64 chunks), then keeps the
-// K/V loads of chunk t+1 in flight while it computes chunk t:
+// Work split: one (sequence b, KV head g, split s) per WAVE, four independent waves per
+// 256-thread work-group. The key set of (b, g) is a list of 32-token chunks, each inside
+// one physical page (a part of a selected page, or of a page of the sink / local window),
+// cut into balanced splits; split s of (b, g) streams its chunks s*cpw ... + cpw - 1. The
+// split size is chosen so that every wave of the launch is resident at once (one round of
+// at most 2,048 waves on the 256 CUs): each wave resolves its pages at the start, while
+// the memory system is idle (one round trip through the selection and the page table for
+// up to 64 chunks; under load that chain costs several microseconds a link), then streams
+// to its end with no barrier. It keeps the K/V loads of chunk t+1 in flight while it
+// computes chunk t:
 //   S = Q_g K^T  : bf16 MFMA 16x16x32 (rows = the G query heads, columns = 16 keys),
 //                  K rows read straight from HBM, each load instruction 64 contiguous
 //                  bytes of each of 16 rows;
@@ -23,10 +27,9 @@
 // through LDS as the B operand, and sum p z - 16 sum fp16(p s) joins every channel at the
 // end. (fp16 rather than bf16 for P.V: its 11-bit weights keep the rounding of p s well
 // inside the attention tolerance.)
-// Partial (max, sum, output) triples of the 4 waves are merged through LDS; the
-// work-group writes one partial per split (or the output when the key set has one
-// split), and a second launch merges the splits of each (b, g) with a log-sum-exp
-// combine staged in LDS.
+// Each wave writes its split's partial (max, sum, output) triple (or the output when the
+// key set has one split), and a second launch merges the splits of each (b, g) with a
+// log-sum-exp combine staged in LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -113,8 +116,10 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
   const int P = a.P;
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
   if (!streaming) {
+    // (the selection entry is read before num_selected is known, so that the two loads,
+    // and the sequence length, make one round trip; every slot below max_selected exists)
+    const int j = c < a.max_selected ? a.selected[((int64_t)b * a.Hkv + g) * a.max_selected + c] : -1;
     if (c >= nsel) return ch;
-    const int j = a.selected[((int64_t)b * a.Hkv + g) * a.max_selected + c];
     if (j < 0 || (int64_t)j * P >= L) return ch;
     ch.page = pt[j];
     ch.row_base = j * P;
@@ -162,17 +167,19 @@ void decode_kernel(const DecodeArgs a) {
   __shared__ float p_lds[Q4 ? 1 : 4][CT][G];
   __shared__ __attribute__((aligned(16))) float p_t[Q4 ? 4 : 1][16][CT + 4];   // INT4: fp16(p s) [head][token]
   __shared__ float a_lds[4][16];                                                // INT4: per-head factors
-  __shared__ float w_m[4][G], w_l[4][G];
-  __shared__ float w_o[4][G][D];
+  __shared__ float h_m[Q4 ? 4 : 1][16], h_l[Q4 ? 4 : 1][16];                     // INT4: per-head max, sum
 
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int tid = threadIdx.x;
+  // (wave-uniform, and said so: every index derived from it then stays scalar)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // ---- which (b, g, split)
+  // ---- which (b, g, split): one per wave (the last work-group's spare waves return;
+  // the kernel has no work-group barrier)
   const int per_b = a.dense.n * a.splits_dense + a.streaming.n * a.splits_stream;
-  const int b = blockIdx.x / per_b;
-  int r = blockIdx.x % per_b;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  if (gw >= (int64_t)a.B * per_b) return;
+  const int b = (int)(gw / per_b);
+  int r = (int)(gw % per_b);
   bool streaming;
   int g, split, n_splits;
   if (r < a.dense.n * a.splits_dense) {
@@ -191,12 +198,13 @@ void decode_kernel(const DecodeArgs a) {
   const int nsel = streaming ? 0 : min(a.num_selected[(int64_t)b * a.Hkv + g], a.max_selected);
   const float scale_log2 = a.sm_scale * kLog2e;
 
-  // ---- this wave's chunks c0 .. c0 + cpw - 1 (chunk c: part c % CPP of page-level
-  // chunk c / CPP, CT tokens)
+  // ---- this wave's chunks c0 .. c0 + cpw - 1 of the (b, g) list (chunk c: part c % CPP
+  // of page-level chunk c / CPP, CT tokens); the last split may hold fewer
   const int P = a.P;
   const int CPP = (P + CT - 1) / CT;
-  const int cpw = a.chunks_per_wave;
-  const int c0 = (split * 4 + wave) * cpw;
+  const int cps = streaming ? a.cpw_stream : a.cpw_dense;
+  const int c0 = split * cps;
+  const int cpw = max(0, min(cps, (streaming ? a.chunks_stream : a.chunks_dense) - c0));
 
   // ---- Q as the MFMA A operand: row m = query head (zero rows past G); k-slot group
   // qg = l/16 holds channels kk*32 + qg*8 + [0, 8) for step kk (so that one K load
@@ -476,9 +484,10 @@ void decode_kernel(const DecodeArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // ---- the wave's split partial (max, sum, output), merged by the second launch
   if constexpr (Q4) {
-    // ---- the wave's partial: sums over the 16 key lanes of each head group; O^T plus
-    // the zero term of its head
+    // sums over the 16 key lanes of each head group; O^T plus the zero term of its head,
+    // exchanged through the wave's LDS rows
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -490,24 +499,27 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = qg * 4 + i;
-        if (h < G) {
-          w_m[wave][h] = m_run[i];
-          w_l[wave][h] = lsum4[i];
-        }
         a_lds[wave][h] = zacc4[i];
+        h_m[wave][h] = m_run[i];
+        h_l[wave][h] = lsum4[i];
       }
     }
     wave_sync_lds();
     if (m < G) {
       const float z = a_lds[wave][m];
+      float* pp = a.partials + (((int64_t)b * a.Hq + (int64_t)g * G + m) * a.max_splits + split) * (D + 2);
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w_o[wave][m][cb * 16 + 4 * qg + i] = oT[cb][i] + z;
+        for (int i = 0; i < 4; ++i) pp[cb * 16 + 4 * qg + i] = oT[cb][i] + z;
+      if (qg == 0) {
+        pp[D] = h_m[wave][m];
+        pp[D + 1] = h_l[wave][m];
+      }
     }
-    __syncthreads();
   } else {
-    // ---- reduce the token groups of the wave
+    // reduce the token groups of the wave; lanes of token group 0 then hold channels
+    // cc*8 .. cc*8 + 7 of every head
 #pragma unroll
     for (int x = CH; x < 64; x <<= 1) {
 #pragma unroll
@@ -517,105 +529,72 @@ void decode_kernel(const DecodeArgs a) {
         for (int e = 0; e < 8; ++e) o[h][e] += shfl_xor(o[h][e], x);
       }
     }
-    // ---- stage the wave's partial in LDS
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float mh = readlane_f(m_run[h & 3], 16 * (h >> 2));
-      if (lane == 0) {
-        w_m[wave][h] = mh;
-        w_l[wave][h] = lsum[h];
-      }
+      float* pp = a.partials + (((int64_t)b * a.Hq + (int64_t)g * G + h) * a.max_splits + split) * (D + 2);
       if (tg == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w_o[wave][h][cc * 8 + e] = o[h][e];
+        for (int e = 0; e < 8; ++e) pp[cc * 8 + e] = o[h][e];
       }
-    }
-    __syncthreads();
-  }
-
-  // ---- merge the 4 waves: element (h, c) per thread
-  const bool single = (n_splits == 1);
-  float* part = a.partials;
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, c = idx % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, w_m[w][h]);
-    float O = 0.f, S = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = fast_exp2(w_m[w][h] - M);
-        O = fmaf(f, w_o[w][h][c], O);
-        S = fmaf(f, w_l[w][h], S);
-      }
-    }
-    const int64_t qh = (int64_t)b * a.Hq + (int64_t)g * G + h;
-    if (single) {
-      a.out[qh * D + c] = (S > 0.f) ? O / S : 0.f;
-      if (c == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
-    } else {
-      float* pp = part + (qh * a.max_splits + split) * (D + 2);
-      pp[c] = O;
-      if (c == 0) {
-        pp[D] = M;
-        pp[D + 1] = S;
+      if (lane == 0) {
+        pp[D] = mh;
+        pp[D + 1] = lsum[h];
       }
     }
   }
 }
 
-// Merge of the split partials of one (b, KV head): log-sum-exp combine staged in LDS.
-// A separate launch (rather than a last-arriving work-group) so that no work-group has
-// to publish its partials with a device-scope fence, which on this GPU writes back and
-// invalidates a whole L2.
-template <int D, int G>
+// Merge of the split partials of one (sequence b, query head): log-sum-exp combine. The
+// head's partials are one contiguous block of n_splits rows of D + 2 floats; the work-group
+// stages the whole block in LDS with every load issued at once (one round trip, however
+// many splits), then every channel combines its n_splits values (one split: the partial
+// normalised).
+template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
-  __shared__ float c_m[G][kMaxSplits], c_w[G][kMaxSplits];
+  constexpr int RW = D + 2;
+  __shared__ __attribute__((aligned(16))) float blk[(kMaxSplits * RW + 255) / 256 * 256];
+  __shared__ float wgt[kMaxSplits];
   const int tid = threadIdx.x;
-  // blocks: (b, dense KV head) if dense heads are split, then (b, streaming KV head)
-  const int nd = a.splits_dense > 1 ? a.dense.n : 0;
-  const int ns = a.splits_stream > 1 ? a.streaming.n : 0;
-  const int b = blockIdx.x / (nd + ns);
-  const int r = blockIdx.x % (nd + ns);
-  const int g = r < nd ? a.dense.h[r] : a.streaming.h[r - nd];
-  const int n_splits = r < nd ? a.splits_dense : a.splits_stream;
-  const float* part = a.partials;
-  for (int idx = tid; idx < G * n_splits; idx += 256) {
-    const int h = idx / n_splits, sp = idx % n_splits;
-    const int64_t qh = (int64_t)b * a.Hq + (int64_t)g * G + h;
-    const float* pp = part + (qh * a.max_splits + sp) * (D + 2);
-    c_m[h][sp] = pp[D];
-    c_w[h][sp] = pp[D + 1];
+  const int G = a.Hq / a.Hkv;
+  const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+  const int g = h / G;
+  bool streaming = false;
+  for (int i = 0; i < a.streaming.n; ++i) streaming |= (a.streaming.h[i] == g);
+  const int n_splits = streaming ? a.splits_stream : a.splits_dense;
+  const int64_t qh = (int64_t)b * a.Hq + h;
+  const float* src = a.partials + qh * a.max_splits * RW;
+  const int n = n_splits * RW;
+  {
+    // direct-to-LDS loads: instruction k of wave w moves floats (4k + w)*64 .. + 63 of the
+    // block, lane l the one at + l; the buffer resource ends at the block, so lanes past it
+    // read zeros (and write them inside blk, which is sized in whole rounds of 256)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint64_t addr = (uint64_t)src;
+    const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, n * 4, 0x00020000);
+    const int rounds = (n + 255) / 256;
+    for (int k = 0; k < rounds; ++k) {
+      const int row = 4 * k + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(blk + row * 64), 4,
+                                               (uint32_t)(row * 64 + lane_id()) * 4, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's loads have landed
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int h = idx / D, c = idx % D;
-    const int64_t qh = (int64_t)b * a.Hq + (int64_t)g * G + h;
-    float M = kNegInf;
-    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, c_m[h][sp]);
-    float O = 0.f, S = 0.f;
-    if (M != kNegInf) {
-      // 8 splits at a time, their loads issued before any is used (one at a time, each
-      // load waited for by its FMA, the splits cost one cache round trip each)
-      const float* pc = part + qh * a.max_splits * (D + 2) + c;
-      for (int sp0 = 0; sp0 < n_splits; sp0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = sp0 + u < n_splits ? pc[(int64_t)(sp0 + u) * (D + 2)] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (sp0 + u < n_splits) {
-            const float f = fast_exp2(c_m[h][sp0 + u] - M);
-            O = fmaf(f, v[u], O);
-            S = fmaf(f, c_w[h][sp0 + u], S);
-          }
-        }
-      }
-    }
+  float M = kNegInf;
+  for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, blk[sp * RW + D]);
+  if (tid < n_splits) wgt[tid] = (M == kNegInf) ? 0.f : fast_exp2(blk[tid * RW + D] - M);
+  __syncthreads();
+  float S = 0.f;
+  for (int sp = 0; sp < n_splits; ++sp) S = fmaf(wgt[sp], blk[sp * RW + D + 1], S);
+  for (int c = tid; c < D; c += 256) {
+    float O = 0.f;
+    for (int sp = 0; sp < n_splits; ++sp) O = fmaf(wgt[sp], blk[sp * RW + c], O);
     a.out[qh * D + c] = (S > 0.f) ? O / S : 0.f;
-    if (c == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
   }
+  if (tid == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
 }
 
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local) {
@@ -623,31 +602,32 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   const int cpp = (P + 31) / 32;   // 32-token chunks per page
   pl.chunks_dense = max_selected * cpp;
   pl.chunks_stream = ((sink + P - 1) / P + (local + P - 1) / P + 1) * cpp;
-  // Chunks per wave: 4 to 8, so that each wave streams several chunks (the loads of the
-  // next overlap the compute of this one and the index chain is paid once per wave);
-  // 8 once the batch fills two work-groups per CU with 4 (measured on MI355X: 4 is best
-  // for 4 x 32K-token sequences, 8 for 64 sequences of 16K-128K tokens). More if the split
-  // count would exceed what the merge can combine.
-  const int64_t total = (int64_t)B * ((int64_t)n_dense * pl.chunks_dense + (int64_t)(Hkv - n_dense) * pl.chunks_stream);
-  constexpr int64_t kWaveSlots = 4 * 2 * 256;
-  int cpw = (int)std::min<int64_t>(8, std::max<int64_t>(4, (total + kWaveSlots - 1) / kWaveSlots));
-  // (measurement override: UBS_DECODE_CPW sets the chunks per wave; the result does not
+  const int nd = n_dense, ns = Hkv - n_dense;
+  const int cd = std::max(pl.chunks_dense, 1), cs = std::max(pl.chunks_stream, 1);
+  // Chunks per split: the fewest that keep every wave of the launch resident at once
+  // (2 work-groups of 4 waves on each of the 256 CUs): all waves then resolve their pages
+  // before the memory system fills up, and none starts its index chain behind the K/V
+  // traffic of others; and few enough splits for the merge. Splits of a list are then
+  // evened out (ceil(chunks / splits) each).
+  constexpr int64_t kWaves = 4 * 2 * 256;
+  auto waves = [&](int c) {
+    return (int64_t)B * ((int64_t)nd * ((cd + c - 1) / c) + (int64_t)ns * ((cs + c - 1) / c));
+  };
+  const int64_t total = (int64_t)B * ((int64_t)nd * cd + (int64_t)ns * cs);
+  int cpw = (int)std::max<int64_t>(1, (total + kWaves - 1) / kWaves);
+  while (cpw < std::max(cd, cs) && waves(cpw) > kWaves) ++cpw;
+  // (measurement override: UBS_DECODE_CPW sets the chunks per split; the result does not
   // depend on it beyond the order of the split merge)
   if (const char* e = getenv("UBS_DECODE_CPW")) {
     const int v = atoi(e);
-    if (v >= 1 && v <= 64) cpw = v;
+    if (v >= 1 && v <= 4096) cpw = v;
   }
-  for (;;) {
-    const int sd = n_dense > 0 ? (pl.chunks_dense + 4 * cpw - 1) / (4 * cpw) : 1;
-    const int ss = (Hkv - n_dense) > 0 ? (pl.chunks_stream + 4 * cpw - 1) / (4 * cpw) : 1;
-    if ((sd <= kMaxSplits && ss <= kMaxSplits) || cpw >= (1 << 20)) {
-      pl.chunks_per_wave = cpw;
-      pl.splits_dense = sd < 1 ? 1 : sd;
-      pl.splits_stream = ss < 1 ? 1 : ss;
-      break;
-    }
-    cpw *= 2;
-  }
+  while ((cd + cpw - 1) / cpw > kMaxSplits || (cs + cpw - 1) / cpw > kMaxSplits) ++cpw;
+  pl.chunks_per_wave = cpw;
+  pl.splits_dense = nd > 0 ? (cd + cpw - 1) / cpw : 1;
+  pl.splits_stream = ns > 0 ? (cs + cpw - 1) / cpw : 1;
+  pl.cpw_dense = (cd + pl.splits_dense - 1) / pl.splits_dense;
+  pl.cpw_stream = (cs + pl.splits_stream - 1) / pl.splits_stream;
   pl.max_splits = pl.splits_dense > pl.splits_stream ? pl.splits_dense : pl.splits_stream;
   return pl;
 }
@@ -687,11 +667,10 @@ hipError_t static_scratch(void** ptr) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int per_b = a.dense.n * a.splits_dense + a.streaming.n * a.splits_stream;
-  const int64_t blocks = (int64_t)a.B * per_b;
+  const int64_t blocks = ((int64_t)a.B * per_b + 3) / 4;   // one split per wave
   if (blocks == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
-  const int merge_per_b = (a.splits_dense > 1 ? a.dense.n : 0) + (a.splits_stream > 1 ? a.streaming.n : 0);
-  const int64_t merge_blocks = (int64_t)a.B * merge_per_b;
+  const int64_t merge_blocks = (int64_t)a.B * a.Hq;   // one work-group per (b, query head)
 #define UBS_DECODE(DD, GG)                                                                            \
   if (a.D == DD && G == GG) {                                                                         \
     if (a.int4)                                                                                       \
@@ -700,7 +679,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((decode_kernel<DD, GG, false>), dim3((unsigned)blocks), dim3(256), 0, s, a); \
     hipError_t e = hipGetLastError();                                                                 \
     if (e != hipSuccess || merge_blocks == 0) return e;                                               \
-    hipLaunchKernelGGL((decode_merge_kernel<DD, GG>), dim3((unsigned)merge_blocks), dim3(256), 0, s, a); \
+    hipLaunchKernelGGL((decode_merge_kernel<DD>), dim3((unsigned)merge_blocks), dim3(256), 0, s, a);     \
     return hipGetLastError();                                                                         \
   }
   UBS_DECODE(64, 1) UBS_DECODE(64, 2) UBS_DECODE(64, 4) UBS_DECODE(64, 8) UBS_DECODE(64, 16)

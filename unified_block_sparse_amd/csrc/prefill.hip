@@ -357,13 +357,19 @@ __global__ __launch_bounds__(2 * T) __attribute__((amdgpu_waves_per_eu(2))) void
         st[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kf[kk][tb]), qb[kk], st[tb], 0, 0, 0);
   };
   // causal cut on the diagonal tile: keys hf*SK + (the step's key index) past the query
+  // (the query index goes through an empty asm first: the comparisons are then made on
+  // the diagonal step itself, instead of the compiler precomputing all 32 lane masks
+  // ahead of the loop, where their 64 scalar registers spill into vector lanes and the
+  // reloads run on every step)
   auto diag_cut = [&](f32x16 (&st)[TB], int hf) __attribute__((always_inline)) {
+    int qrel = qi - hf * SK - 4 * q2;
+    asm volatile("" : "+v"(qrel));
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = hf * SK + tb * 32 + 8 * (e >> 2) + 4 * q2 + (e & 3);
-        if (key > qi) st[tb][e] = kNegInf;
+        const int key = tb * 32 + 8 * (e >> 2) + (e & 3);
+        if (key > qrel) st[tb][e] = kNegInf;
       }
   };
   // Online softmax of one step's scores in two parts. softmax_max: row max, then lazy
