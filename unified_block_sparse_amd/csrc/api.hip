@@ -301,10 +301,11 @@ size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
   // the split plan depends only on these sizes and the number of dense KV heads: take
   // the largest over every count
   int ms = 1;
-  for (int nd = 0; nd <= Hkv; ++nd) {
-    const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, nd, P, max_selected, sink_tokens, local_tokens);
-    ms = pl.max_splits > ms ? pl.max_splits : ms;
-  }
+  for (int nd = 0; nd <= Hkv; ++nd)
+    for (int q4 = 0; q4 < 2; ++q4) {
+      const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, nd, P, max_selected, sink_tokens, local_tokens, q4 != 0);
+      ms = pl.max_splits > ms ? pl.max_splits : ms;
+    }
   return ((size_t)B * Hq * ms * (D + 2) * sizeof(float) + 255) / 256 * 256;
 }
 
@@ -357,7 +358,7 @@ static int decode_impl(const char* name, bool int4, bool use_static, const ubs_b
   }
   REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
           "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens);
+  const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens, int4);
   const int64_t blocks = (int64_t)B * (dense.n * pl.splits_dense + streaming.n * pl.splits_stream);
   REQUIRE(blocks < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large", (long long)blocks);
   ubs::DecodeArgs a{};

@@ -42,6 +42,7 @@ namespace ubs {
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kMaxSplits = 128;
 constexpr int kChunkTokens = 32;   // tokens per chunk
@@ -49,8 +50,8 @@ constexpr int kChunkTokens = 32;   // tokens per chunk
 // K and V of one chunk in registers, per lane: bf16 rows, or INT4 codes and row params
 template <int D, bool Q4>
 struct ChunkRegs {
-  u32x4 k[kChunkTokens / 16][D / 32];
-  u32x4 v[D / 16];
+  u32x4 k[kChunkTokens / 16][D / 32];      // K rows of the two 16-row halves (A operand)
+  uint32_t v[kChunkTokens / 4][D / 32];    // V: key slot s, the lane's D/16 channels
 };
 template <int D>
 struct ChunkRegs<D, true> {
@@ -100,8 +101,24 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float readlane_f(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+// max of v over lanes l and l ^ 16 (rows 2r and 2r + 1 of 16 lanes swapped), and over l
+// and l ^ 32 (the two halves of the wave swapped): with both operands v, the two results
+// of a swap hold v and its partner, in some order, in every lane
+__device__ __forceinline__ float max_swap16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_swap32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_swap16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_swap32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 struct Chunk {
@@ -150,24 +167,23 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
   return ch;
 }
 
-// At most 256 registers a lane (two waves per SIMD or more) wherever that costs no spill:
-// the allocator then keeps the INT4 kernel (about 166 registers) in the vector file alone,
-// three waves per SIMD (measured on MI355X: about 10% faster than two), and the bf16
-// kernel at G = 8, D = 128 at two waves instead of one. At G = 16 the bf16 kernel's
-// double-buffered K/V rows and G-wide accumulators need more than 256.
+// At most 256 registers a lane (two waves per SIMD) wherever that costs no spill: the
+// allocator then keeps the INT4 kernel (about 166 registers) in the vector file alone,
+// three waves per SIMD (measured on MI355X: about 10% faster than two).
 template <int D, int G, bool Q4>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((Q4 || G <= 8) ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(const DecodeArgs a) {
   constexpr int KK = D / 32;   // QK MFMA steps (16x16x32)
-  constexpr int CH = D / 8;    // lanes per V row (16-byte pieces)
-  constexpr int TG = 64 / CH;  // token groups in P.V
   constexpr int CT = kChunkTokens;
   constexpr int NB = CT / 16;  // 16-key MFMA blocks per chunk
-  constexpr int VR = CT / TG;  // V rows per lane and chunk
-  __shared__ float p_lds[Q4 ? 1 : 4][CT][G];
+  constexpr int U = Q4 ? 32 : 16;   // rows per unit (the part of one page a lane resolves)
+  constexpr int UPC = CT / U;       // units per chunk
+  constexpr int NTR = 64 / UPC;     // chunks resolved per round trip (one unit a lane)
+  constexpr int CPL = D / 16;       // bf16: V channels a lane holds of each row
+  constexpr int WPR = D / 32;       // ... as words
   __shared__ __attribute__((aligned(16))) float p_t[Q4 ? 4 : 1][16][CT + 4];   // INT4: fp16(p s) [head][token]
-  __shared__ float a_lds[4][16];                                                // INT4: per-head factors
-  __shared__ float h_m[Q4 ? 4 : 1][16], h_l[Q4 ? 4 : 1][16];                     // INT4: per-head max, sum
+  __shared__ float a_lds[Q4 ? 4 : 1][16];                                       // INT4: per-head factors
+  __shared__ float h_m[Q4 ? 4 : 1][16], h_l[Q4 ? 4 : 1][16];                    // INT4: per-head max, sum
 
   const int lane = lane_id();
   // (wave-uniform, and said so: every index derived from it then stays scalar)
@@ -194,22 +210,25 @@ void decode_kernel(const DecodeArgs a) {
     split = r % a.splits_stream;
     n_splits = a.splits_stream;
   }
+  (void)n_splits;
   const int L = a.seq_lens[b];
   const int nsel = streaming ? 0 : min(a.num_selected[(int64_t)b * a.Hkv + g], a.max_selected);
   const float scale_log2 = a.sm_scale * kLog2e;
 
-  // ---- this wave's chunks c0 .. c0 + cpw - 1 of the (b, g) list (chunk c: part c % CPP
-  // of page-level chunk c / CPP, CT tokens); the last split may hold fewer
+  // ---- this wave's chunks c0 .. c0 + cpw - 1 of the (b, g) list: chunk c is units
+  // c*UPC .. c*UPC + UPC - 1, unit u is rows (u % UPP)*U .. + U - 1 of the list's page
+  // u / UPP; the last split may hold fewer chunks
   const int P = a.P;
-  const int CPP = (P + CT - 1) / CT;
+  const int UPP = (P + U - 1) / U;
   const int cps = streaming ? a.cpw_stream : a.cpw_dense;
   const int c0 = split * cps;
   const int cpw = max(0, min(cps, (streaming ? a.chunks_stream : a.chunks_dense) - c0));
 
-  // ---- Q as the MFMA A operand: row m = query head (zero rows past G); k-slot group
-  // qg = l/16 holds channels kk*32 + qg*8 + [0, 8) for step kk (so that one K load
-  // instruction reads 64 contiguous bytes of each of its 16 rows); with INT4 pages,
-  // channels qg*D/4 + kk*8 + [0, 8) (one load brings a lane's codes for every step).
+  // ---- Q in MFMA operand form: lane (qg, m) holds head m (zero past G), channels
+  // kk*32 + qg*8 + [0, 8) for step kk (so that one K load instruction reads 64 contiguous
+  // bytes of each of its 16 rows); with INT4 pages, channels qg*D/4 + kk*8 + [0, 8) (one
+  // load brings a lane's codes for every step). bf16 pages take it as the B operand of
+  // S^T = K Q^T, INT4 pages as the A operand of S = Q K^T.
   const int m = lane & 15;
   const int qg = lane >> 4;
   bf16x8 qa[KK];
@@ -236,35 +255,32 @@ void decode_kernel(const DecodeArgs a) {
     for (int i = 0; i < 4; ++i) qsum[i] = __shfl(sq, 4 * qg + i, 64);
   }
 
-  float m_run[4];   // running max of heads 4*qg + i (lane-replicated within a 16-lane group)
+  // INT4: running max of heads 4*qg + i (lane-replicated within a 16-lane group); O^T
+  // blocks (lane: channels cb*16 + 4*qg + i of head m), and the lane's sums over its key
+  // rows of p and of p z - 16 fp16(p s) for heads 4*qg + i
+  float m_run[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) m_run[i] = kNegInf;
-  float o[G][8];
-  float lsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lsum[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  }
-  // INT4: O^T blocks (lane: channels cb*16 + 4*qg + i of head m), and the lane's sums
-  // over its key rows of p and of p z - 16 fp16(p s) for heads 4*qg + i
   f32x4 oT[Q4 ? D / 16 : 1];
   float lsum4[4], zacc4[4];
 #pragma unroll
   for (int cb = 0; cb < (Q4 ? D / 16 : 1); ++cb) oT[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) lsum4[i] = zacc4[i] = 0.f;
-  const int cc = lane % CH;
-  const int tg = lane / CH;
+  // bf16: lane (qg, m) runs head m: its running max (replicated over qg), its sum over the
+  // lane's key slots, and O^T block j = channels CPL*(4*qg + i) + j of head m
+  float mh = kNegInf, lh = 0.f;
+  f32x4 ov[Q4 ? 1 : CPL];
+#pragma unroll
+  for (int j = 0; j < (Q4 ? 1 : CPL); ++j) ov[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   const int64_t head_stride = (int64_t)P * D;  // one (page, KV head) slab
-  int d_page = -1, d_r0 = 0, d_lo = 0, d_hi = 0;   // chunk descriptors, one chunk per lane
+  int d_page = -1, d_r0 = 0, d_lo = 0, d_hi = 0;   // unit descriptors, one unit per lane
 
   // ---- K and V of one chunk into registers, branch-free: each tensor through a buffer
-  // resource over its (page, KV head) slab, of size zero for an empty chunk (the loads
+  // resource over its (page, KV head) slab, of size zero for an empty unit (the loads
   // then read nothing and return zeros). Without a branch the compiler can count the
-  // loads in flight and wait for chunk t alone while chunk t+1's are outstanding. Rows
-  // are clamped into the page; rows outside [lo, hi) are loaded but never weighted.
+  // loads in flight and wait for chunk t alone while chunk t+1's are outstanding.
   auto slab_rsrc = [&](const uint16_t* cache, int page) __attribute__((always_inline)) {
     const uint64_t addr = (uint64_t)(cache + ((int64_t)max(page, 0) * a.Hkv + g) * head_stride);
     const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
@@ -279,10 +295,15 @@ void decode_kernel(const DecodeArgs a) {
                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)addr);
     return __builtin_amdgcn_make_buffer_rsrc((void*)addr_u, 0, page >= 0 ? P * row_bytes : 0, 0x00020000);
   };
+  auto unit_page = [&](int t, int nt, int h) __attribute__((always_inline)) {
+    return t < nt ? __builtin_amdgcn_readlane(d_page, min(t * UPC + h, 63)) : -1;
+  };
   auto load = [&](int t, int nt, ChunkRegs<D, Q4>& R) __attribute__((always_inline)) {
-    const int page = t < nt ? __builtin_amdgcn_readlane(d_page, min(t, 63)) : -1;
-    const int r0 = __builtin_amdgcn_readlane(d_r0, min(t, 63));
     if constexpr (Q4) {
+      // one unit of 32 rows of one page; rows are clamped into the page, and rows outside
+      // [lo, hi) are loaded but never weighted
+      const int page = unit_page(t, nt, 0);
+      const int r0 = __builtin_amdgcn_readlane(d_r0, min(t, 63));
       const __amdgpu_buffer_rsrc_t rk = slab_rsrc4(a.k_codes, page, D / 2);
       const __amdgpu_buffer_rsrc_t rkp = slab_rsrc4(a.k_params, page, 4);
       const __amdgpu_buffer_rsrc_t rv = slab_rsrc4(a.v_codes, page, D / 2);
@@ -310,64 +331,74 @@ void decode_kernel(const DecodeArgs a) {
       for (int cb = 0; cb < D / 16; ++cb)
         R.v[cb] = __builtin_amdgcn_raw_buffer_load_b32(rv, (cb * 16 + m) * (P / 2) + (r0 + 8 * qg) / 2, 0, 0);
     } else {
-      const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache, page);
-      const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache, page);
+      // two units of 16 rows (halves h = 0, 1; P is a multiple of 16, so a unit never
+      // crosses its page). K: the A operand of half h, row r0_h + m, 16 bytes at channel
+      // kk*32 + 8*qg. V: key slot s of the lane holds row r0_h + 4*qg + (s & 3) of half
+      // h = s / 4 (the rows of the lane's scores), channels CPL*m .. + CPL - 1, the row
+      // clamped into the half's valid rows [lo, hi) so that every value read is one the
+      // cache defines (the weights of clamped slots are zero).
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const int row = min(r0 + blk * 16 + m, P - 1);
-        const int off = (row * D + qg * 8) * 2;
+      for (int h = 0; h < 2; ++h) {
+        const int page = unit_page(t, nt, h);
+        const int u = min(t * UPC + h, 63);
+        const int r0 = __builtin_amdgcn_readlane(d_r0, u);
+        const int lo = __builtin_amdgcn_readlane(d_lo, u), hi = __builtin_amdgcn_readlane(d_hi, u);
+        const __amdgpu_buffer_rsrc_t rk = slab_rsrc(a.k_cache, page);
+        const __amdgpu_buffer_rsrc_t rv = slab_rsrc(a.v_cache, page);
+        const int off = ((r0 + m) * D + qg * 8) * 2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) R.k[blk][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 64, 0, 0);
-      }
+        for (int kk = 0; kk < KK; ++kk) R.k[h][kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, off + kk * 64, 0, 0);
 #pragma unroll
-      for (int x = 0; x < VR; ++x) {
-        const int row = min(r0 + tg + TG * x, P - 1);
-        R.v[x] = __builtin_amdgcn_raw_buffer_load_b128(rv, (row * D + cc * 8) * 2, 0, 0);
+        for (int s = 0; s < 4; ++s) {
+          const int row = min(max(r0 + 4 * qg + s, lo), hi - 1);
+          const int voff = (row * D + CPL * m) * 2;
+          if constexpr (D == 128) {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
+#pragma unroll
+            for (int e = 0; e < WPR; ++e) R.v[4 * h + s][e] = w[e];
+          } else {
+            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, 0);
+#pragma unroll
+            for (int e = 0; e < WPR; ++e) R.v[4 * h + s][e] = w[e];
+          }
+        }
       }
     }
   };
   // ---- online softmax and P.V over one chunk already in registers
   auto compute = [&](int t, int nt, const ChunkRegs<D, Q4>& R) __attribute__((always_inline)) {
-    const int page = t < nt ? __builtin_amdgcn_readlane(d_page, min(t, 63)) : -1;
-    if (page < 0) return;
-    const int r0 = __builtin_amdgcn_readlane(d_r0, t);
-    const int lo = __builtin_amdgcn_readlane(d_lo, t), hi = __builtin_amdgcn_readlane(d_hi, t);
-    // S for NB blocks of 16 rows
-    f32x4 s[NB];
+    if constexpr (Q4) {
+      const int page = unit_page(t, nt, 0);
+      if (page < 0) return;
+      const int r0 = __builtin_amdgcn_readlane(d_r0, t);
+      const int lo = __builtin_amdgcn_readlane(d_lo, t), hi = __builtin_amdgcn_readlane(d_hi, t);
+      // S for NB blocks of 16 rows: lane (qg, m) holds heads 4*qg + i, key blk*16 + m
+      f32x4 s[NB];
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int row = r0 + blk * 16 + m;
-      const bool ok = row >= lo && row < hi;
-      if constexpr (Q4) {
+      for (int blk = 0; blk < NB; ++blk) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int row = r0 + blk * 16 + m;
+        const bool ok = row >= lo && row < hi;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], codes_bf16(R.k[blk][kk]), acc, 0, 0, 0);
         const float sk = half_lo(R.kp[blk]), zk = half_hi(R.kp[blk]) - 16.f * sk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[blk][i] = ok ? fmaf(sk, acc[i], zk * qsum[i]) * scale_log2 : kNegInf;
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], as_bf16x8(R.k[blk][kk]), acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[blk][i] = ok ? acc[i] * scale_log2 : kNegInf;
       }
-    }
-    // chunk max per head (heads 4*qg + i), then running max and weights
-    float alpha_i[4];
+      // chunk max per head (heads 4*qg + i), then running max and weights
+      float alpha_i[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = s[0][i];
+      for (int i = 0; i < 4; ++i) {
+        float mx = s[0][i];
 #pragma unroll
-      for (int blk = 1; blk < NB; ++blk) mx = fmaxf(mx, s[blk][i]);
+        for (int blk = 1; blk < NB; ++blk) mx = fmaxf(mx, s[blk][i]);
 #pragma unroll
-      for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, shfl_xor(mx, o2));
-      const float mn = fmaxf(m_run[i], mx);
-      alpha_i[i] = rescale_factor(m_run[i], mn);
-      m_run[i] = mn;
-    }
-    if constexpr (Q4) {
+        for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, shfl_xor(mx, o2));
+        const float mn = fmaxf(m_run[i], mx);
+        alpha_i[i] = rescale_factor(m_run[i], mn);
+        m_run[i] = mn;
+      }
       // weights: p_t[head][token] = fp16(p s_v) (exact as fp32), and the lane's sums
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
@@ -406,62 +437,90 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
         oT[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_f16(R.v[cb]), pb, oT[cb], 0, 0, 0);
+      wave_sync_lds();
     } else {
+      const int page0 = unit_page(t, nt, 0), page1 = unit_page(t, nt, 1);
+      if (page0 < 0 && page1 < 0) return;
+      // S^T = K Q^T per half: lane (qg, m) holds head m, keys 4*qg + i of each half
+      f32x4 s[2];
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
+      for (int h = 0; h < 2; ++h) {
+        const int u = min(t * UPC + h, 63);
+        const int r0 = __builtin_amdgcn_readlane(d_r0, u);
+        const int lo = __builtin_amdgcn_readlane(d_lo, u), hi = __builtin_amdgcn_readlane(d_hi, u);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.k[h][kk]), qa[kk], acc, 0, 0, 0);
+        // (row - lo < hi - lo as unsigned: one compare for both bounds)
+        const uint32_t n_ok = (uint32_t)(hi - lo);
+        const int d0 = 4 * qg + (r0 - lo);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[h][i] = ((uint32_t)(d0 + i) < n_ok) ? acc[i] * scale_log2 : kNegInf;
+      }
+      // chunk max of head m over the lane's 8 keys and the 4 lane groups (row pairs, then
+      // halves of the wave, by lane swaps), running max
+      float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+      mx = max_swap16(mx);
+      mx = max_swap32(mx);
+      const float mn = fmaxf(mh, mx);
+      // (mr: the max, or 0 while every key so far is masked; the scores are then -inf, so
+      // every weight is 0, and so is alpha, applied to a zero state)
+      const float mr = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(mh - mr);
+      mh = mn;
+      // weights, rounded to bf16 as the B operand of O^T += V^T P^T: key slot 2e, 2e + 1
+      // of word e are the lane's keys (h = e/2, i = 2*(e&1)) and + 1
+      float p[2][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int h = qg * 4 + i;
-          if (h < G) p_lds[wave][blk * 16 + m][h] = softmax_weight(s[blk][i], m_run[i]);
+          p[h][i] = fast_exp2(s[h][i] - mr);
+          ps += p[h][i];
         }
-      wave_sync_lds();
-      float alpha[G];
+      lh = fmaf(lh, alpha, ps);
+      u32x4 pw;
 #pragma unroll
-      for (int h = 0; h < G; ++h) alpha[h] = readlane_f(alpha_i[h & 3], 16 * (h >> 2));
+      for (int e = 0; e < 4; ++e)
+        pw[e] = __builtin_bit_cast(uint32_t,
+                                   __builtin_convertvector((f32x2{p[e >> 1][2 * (e & 1)], p[e >> 1][2 * (e & 1) + 1]}), bf16x2));
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+      if (__ballot(alpha != 1.f)) {   // (a head's max grew: rare after the first chunks)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        lsum[h] *= alpha[h];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] *= alpha[h];
+        for (int j = 0; j < CPL; ++j) ov[j] *= alpha;
       }
-      // O += P V over the chunk's rows tg, tg + TG, ... (weights of rows outside [lo, hi)
-      // are zero and their V values are replaced by zero)
+      // A operand of block j: V^T rows = channels CPL*m' + j (m' the MFMA row), key slots
+      // as above; word e pairs slot 2e (low half) with slot 2e + 1 (high half), both the
+      // half j & 1 of word j/2 of their V row
 #pragma unroll
-      for (int x = 0; x < VR; ++x) {
-        const int rr = tg + TG * x;
-        const int row = r0 + rr;
-        const bool ok = row >= lo && row < hi;
-        float vf[8];
+      for (int j = 0; j < CPL; ++j) {
+        constexpr uint32_t kSelLo = 0x05040100u, kSelHi = 0x07060302u;
+        u32x4 va;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[2 * e] = ok ? bf16_lo(R.v[x][e]) : 0.f;
-          vf[2 * e + 1] = ok ? bf16_hi(R.v[x][e]) : 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = p_lds[wave][rr][h];
-          lsum[h] += p;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          va[e] = __builtin_amdgcn_perm(R.v[2 * e + 1][j >> 1], R.v[2 * e][j >> 1], (j & 1) ? kSelHi : kSelLo);
+        ov[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), pb, ov[j], 0, 0, 0);
       }
     }
-    wave_sync_lds();
   };
-  // ---- the wave's chunks, 64 at a time. Lane t resolves chunk c0 + t0 + t to its
-  // physical page and valid rows [lo, hi) of the page, so the index chain (selection ->
-  // page table) costs one round trip per 64 chunks, before any of their K/V loads. Then
-  // the loads of chunk t+1 are in flight while chunk t is computed (register double
-  // buffer; unrolled by two so each buffer is a fixed register set).
+  // ---- the wave's chunks, NTR at a time. Lane l resolves unit l of them to its physical
+  // page and valid rows [lo, hi) of the page, so the index chain (selection -> page
+  // table) costs one round trip per NTR chunks, before any of their K/V loads. Then the
+  // loads of chunk t+1 are in flight while chunk t is computed (register double buffer;
+  // unrolled by two so each buffer is a fixed register set).
   ChunkRegs<D, Q4> ra, rb;
-  for (int t0 = 0; t0 < cpw; t0 += 64) {
-    const int nt = min(64, cpw - t0);
+  for (int t0 = 0; t0 < cpw; t0 += NTR) {
+    const int nt = min(NTR, cpw - t0);
     d_page = -1;
-    if (lane < nt) {
-      const int c = c0 + t0 + lane;
-      const Chunk ch = decode_chunk(a, streaming, b, g, c / CPP, L, nsel);
-      const int r0 = (c % CPP) * CT;                    // first row of the part in the page
-      const int lo = max(ch.t0 - ch.row_base, r0), hi = min(ch.t1 - ch.row_base, r0 + CT);
+    d_r0 = d_lo = d_hi = 0;
+    if (lane < nt * UPC) {
+      const int u = (c0 + t0) * UPC + lane;
+      const Chunk ch = decode_chunk(a, streaming, b, g, u / UPP, L, nsel);
+      const int r0 = (u % UPP) * U;                     // first row of the unit in the page
+      const int lo = max(ch.t0 - ch.row_base, r0), hi = min(ch.t1 - ch.row_base, r0 + U);
       if (ch.page >= 0 && lo < hi) {
         d_page = ch.page;
         d_r0 = r0;
@@ -485,6 +544,9 @@ void decode_kernel(const DecodeArgs a) {
     }
   }
   // ---- the wave's split partial (max, sum, output), merged by the second launch
+  float* const part = a.partials + ((int64_t)b * a.Hq + (int64_t)g * G) * a.max_splits * (D + 2) +
+                      (int64_t)split * (D + 2);
+  const int64_t head_pitch = (int64_t)a.max_splits * (D + 2);
   if constexpr (Q4) {
     // sums over the 16 key lanes of each head group; O^T plus the zero term of its head,
     // exchanged through the wave's LDS rows
@@ -507,7 +569,7 @@ void decode_kernel(const DecodeArgs a) {
     wave_sync_lds();
     if (m < G) {
       const float z = a_lds[wave][m];
-      float* pp = a.partials + (((int64_t)b * a.Hq + (int64_t)g * G + m) * a.max_splits + split) * (D + 2);
+      float* pp = part + m * head_pitch;
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
@@ -518,28 +580,19 @@ void decode_kernel(const DecodeArgs a) {
       }
     }
   } else {
-    // reduce the token groups of the wave; lanes of token group 0 then hold channels
-    // cc*8 .. cc*8 + 7 of every head
+    // head m: the sum over the 4 lane groups; lane (qg, m) holds channels
+    // CPL*(4*qg + i) + j, that is 4*CPL contiguous channels from 4*CPL*qg
+    lh = sum_swap16(lh);
+    lh = sum_swap32(lh);
+    if (m < G) {
+      float* pp = part + m * head_pitch;
 #pragma unroll
-    for (int x = CH; x < 64; x <<= 1) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        lsum[h] += shfl_xor(lsum[h], x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] += shfl_xor(o[h][e], x);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mh = readlane_f(m_run[h & 3], 16 * (h >> 2));
-      float* pp = a.partials + (((int64_t)b * a.Hq + (int64_t)g * G + h) * a.max_splits + split) * (D + 2);
-      if (tg == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pp[cc * 8 + e] = o[h][e];
-      }
-      if (lane == 0) {
+        for (int j = 0; j < CPL; ++j) pp[CPL * (4 * qg + i) + j] = ov[j][i];
+      if (qg == 0) {
         pp[D] = mh;
-        pp[D + 1] = lsum[h];
+        pp[D + 1] = lh;
       }
     }
   }
@@ -597,11 +650,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
   if (tid == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
 }
 
-DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local) {
+DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4) {
   DecodePlan pl{};
-  const int cpp = (P + 31) / 32;   // 32-token chunks per page
-  pl.chunks_dense = max_selected * cpp;
-  pl.chunks_stream = ((sink + P - 1) / P + (local + P - 1) / P + 1) * cpp;
+  // key lists in units of U rows of one page (16 for bf16 pages, 32 for INT4), two or one
+  // units a 32-token chunk
+  const int U = int4 ? 32 : 16;
+  const int upp = (P + U - 1) / U, upc = kChunkTokens / U;
+  const int64_t units_dense = (int64_t)max_selected * upp;
+  const int64_t units_stream = ((int64_t)(sink + P - 1) / P + (local + P - 1) / P + 1) * upp;
+  pl.chunks_dense = (int)((units_dense + upc - 1) / upc);
+  pl.chunks_stream = (int)((units_stream + upc - 1) / upc);
   const int nd = n_dense, ns = Hkv - n_dense;
   const int cd = std::max(pl.chunks_dense, 1), cs = std::max(pl.chunks_stream, 1);
   // Chunks per split: the fewest that keep every wave of the launch resident at once

@@ -151,7 +151,7 @@ struct DecodePlan {
   int cpw_dense, cpw_stream;        // chunks per split of each kind (balanced)
   int splits_dense, splits_stream, max_splits;
 };
-DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local);
+DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4);
 
 // Size of the library-owned scratch of sparse_decode_static (per GPU), and its device
 // address on the current device (resolved on the first call there).
