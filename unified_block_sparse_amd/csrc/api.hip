@@ -394,8 +394,6 @@ static int decode_impl(const char* name, bool int4, bool use_static, const ubs_b
   a.chunks_per_wave = pl.chunks_per_wave;
   a.chunks_dense = pl.chunks_dense;
   a.chunks_stream = pl.chunks_stream;
-  a.cpw_dense = pl.cpw_dense;
-  a.cpw_stream = pl.cpw_stream;
   a.out = out;
   a.lse = lse;
   a.partials = static_cast<float*>(workspace);

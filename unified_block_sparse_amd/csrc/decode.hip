@@ -44,7 +44,9 @@ typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
-constexpr int kMaxSplits = 128;
+// At most 96 splits a key list: the merge stages a query head's partials in at most
+// 96 * 130 floats + weights, under 64 KiB of LDS
+constexpr int kMaxSplits = 96;
 constexpr int kChunkTokens = 32;   // tokens per chunk
 
 // K and V of one chunk in registers, per lane: bf16 rows, or INT4 codes and row params
@@ -190,39 +192,35 @@ void decode_kernel(const DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // ---- which (b, g, split): one per wave (the last work-group's spare waves return;
-  // the kernel has no work-group barrier)
-  const int per_b = a.dense.n * a.splits_dense + a.streaming.n * a.splits_stream;
+  // the kernel has no work-group barrier). The nS streaming-head waves of sequence b are
+  // spread evenly among its dense-head ones (slot r is the j-th streaming wave when
+  // floor(r nS / per_b) steps up there), so that every work-group, and every XCD (work-
+  // groups go to the XCDs in turn), gets the same mix of the two list lengths.
+  const int nS = a.streaming.n * a.splits_stream;
+  const int per_b = a.dense.n * a.splits_dense + nS;
   const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
   if (gw >= (int64_t)a.B * per_b) return;
   const int b = (int)(gw / per_b);
-  int r = (int)(gw % per_b);
-  bool streaming;
-  int g, split, n_splits;
-  if (r < a.dense.n * a.splits_dense) {
-    streaming = false;
-    g = a.dense.h[r / a.splits_dense];
-    split = r % a.splits_dense;
-    n_splits = a.splits_dense;
-  } else {
-    r -= a.dense.n * a.splits_dense;
-    streaming = true;
-    g = a.streaming.h[r / a.splits_stream];
-    split = r % a.splits_stream;
-    n_splits = a.splits_stream;
-  }
-  (void)n_splits;
+  const int r = (int)(gw % per_b);
+  const int s_before = (int)((int64_t)r * nS / per_b), s_through = (int)((int64_t)(r + 1) * nS / per_b);
+  const bool streaming = s_through > s_before;
+  const int idx = streaming ? s_before : r - s_before;
+  const int n_splits = streaming ? a.splits_stream : a.splits_dense;
+  const int g = streaming ? a.streaming.h[idx / n_splits] : a.dense.h[idx / n_splits];
+  const int split = idx % n_splits;
   const int L = a.seq_lens[b];
   const int nsel = streaming ? 0 : min(a.num_selected[(int64_t)b * a.Hkv + g], a.max_selected);
   const float scale_log2 = a.sm_scale * kLog2e;
 
-  // ---- this wave's chunks c0 .. c0 + cpw - 1 of the (b, g) list: chunk c is units
-  // c*UPC .. c*UPC + UPC - 1, unit u is rows (u % UPP)*U .. + U - 1 of the list's page
-  // u / UPP; the last split may hold fewer chunks
+  // ---- this wave's chunks c0 .. c0 + cpw - 1 of the (b, g) list (split s of S takes
+  // chunks floor(s C / S) .. floor((s + 1) C / S) - 1, so splits differ by one chunk at
+  // most): chunk c is units c*UPC .. c*UPC + UPC - 1, unit u is rows (u % UPP)*U .. + U - 1
+  // of the list's page u / UPP
   const int P = a.P;
   const int UPP = (P + U - 1) / U;
-  const int cps = streaming ? a.cpw_stream : a.cpw_dense;
-  const int c0 = split * cps;
-  const int cpw = max(0, min(cps, (streaming ? a.chunks_stream : a.chunks_dense) - c0));
+  const int n_chunks = streaming ? a.chunks_stream : a.chunks_dense;
+  const int c0 = (int)((int64_t)split * n_chunks / n_splits);
+  const int cpw = (int)((int64_t)(split + 1) * n_chunks / n_splits) - c0;
 
   // ---- Q in MFMA operand form: lane (qg, m) holds head m (zero past G), channels
   // kk*32 + qg*8 + [0, 8) for step kk (so that one K load instruction reads 64 contiguous
@@ -606,8 +604,11 @@ void decode_kernel(const DecodeArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
   constexpr int RW = D + 2;
-  __shared__ __attribute__((aligned(16))) float blk[(kMaxSplits * RW + 255) / 256 * 256];
-  __shared__ float wgt[kMaxSplits];
+  // (dynamic LDS, sized by the launch for the plan's largest split count: whole rounds of
+  // 256 floats of partials, then one weight a split)
+  extern __shared__ __attribute__((aligned(16))) float merge_lds[];
+  float* const blk = merge_lds;
+  float* const wgt = merge_lds + (a.max_splits * RW + 255) / 256 * 256;
   const int tid = threadIdx.x;
   const int G = a.Hq / a.Hkv;
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
@@ -621,7 +622,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
   {
     // direct-to-LDS loads: instruction k of wave w moves floats (4k + w)*64 .. + 63 of the
     // block, lane l the one at + l; the buffer resource ends at the block, so lanes past it
-    // read zeros (and write them inside blk, which is sized in whole rounds of 256)
+    // read zeros (and write them inside blk, which holds whole rounds of 256)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint64_t addr = (uint64_t)src;
     const uint64_t addr_u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(addr >> 32)) << 32) |
@@ -665,8 +666,8 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   // Chunks per split: the fewest that keep every wave of the launch resident at once
   // (2 work-groups of 4 waves on each of the 256 CUs): all waves then resolve their pages
   // before the memory system fills up, and none starts its index chain behind the K/V
-  // traffic of others; and few enough splits for the merge. Splits of a list are then
-  // evened out (ceil(chunks / splits) each).
+  // traffic of others; and few enough splits for the merge. The kernel then cuts each
+  // list into that many splits of equal size (to one chunk).
   constexpr int64_t kWaves = 4 * 2 * 256;
   auto waves = [&](int c) {
     return (int64_t)B * ((int64_t)nd * ((cd + c - 1) / c) + (int64_t)ns * ((cs + c - 1) / c));
@@ -684,8 +685,6 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   pl.chunks_per_wave = cpw;
   pl.splits_dense = nd > 0 ? (cd + cpw - 1) / cpw : 1;
   pl.splits_stream = ns > 0 ? (cs + cpw - 1) / cpw : 1;
-  pl.cpw_dense = (cd + pl.splits_dense - 1) / pl.splits_dense;
-  pl.cpw_stream = (cs + pl.splits_stream - 1) / pl.splits_stream;
   pl.max_splits = pl.splits_dense > pl.splits_stream ? pl.splits_dense : pl.splits_stream;
   return pl;
 }
@@ -729,6 +728,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const int G = a.Hq / a.Hkv;
   const int64_t merge_blocks = (int64_t)a.B * a.Hq;   // one work-group per (b, query head)
+  const size_t merge_lds = (size_t)(((int64_t)a.max_splits * (a.D + 2) + 255) / 256 * 256 + a.max_splits) * sizeof(float);
 #define UBS_DECODE(DD, GG)                                                                            \
   if (a.D == DD && G == GG) {                                                                         \
     if (a.int4)                                                                                       \
@@ -737,7 +737,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((decode_kernel<DD, GG, false>), dim3((unsigned)blocks), dim3(256), 0, s, a); \
     hipError_t e = hipGetLastError();                                                                 \
     if (e != hipSuccess || merge_blocks == 0) return e;                                               \
-    hipLaunchKernelGGL((decode_merge_kernel<DD>), dim3((unsigned)merge_blocks), dim3(256), 0, s, a);     \
+    hipLaunchKernelGGL((decode_merge_kernel<DD>), dim3((unsigned)merge_blocks), dim3(256), merge_lds, s, a); \
     return hipGetLastError();                                                                         \
   }
   UBS_DECODE(64, 1) UBS_DECODE(64, 2) UBS_DECODE(64, 4) UBS_DECODE(64, 8) UBS_DECODE(64, 16)

@@ -63,7 +63,6 @@ struct DecodeArgs {
   HeadList dense, streaming;
   int splits_dense, splits_stream, chunks_per_wave;
   int chunks_dense, chunks_stream;   // chunks of a (b, g) list, dense / streaming (upper bounds)
-  int cpw_dense, cpw_stream;         // chunks per split (the last split of a list may hold fewer)
   float* out;
   float* lse;
   float* partials;     // workspace [B][Hq][max_splits][D + 2]
@@ -148,7 +147,6 @@ hipError_t launch_check(const CheckArgs& a, hipStream_t s);
 struct DecodePlan {
   int chunks_dense, chunks_stream;  // upper bounds of key chunks per (b, KV head)
   int chunks_per_wave;
-  int cpw_dense, cpw_stream;        // chunks per split of each kind (balanced)
   int splits_dense, splits_stream, max_splits;
 };
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4);
