@@ -279,7 +279,7 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
  *   ordered by the caller. Nothing in the scratch needs clearing: each call writes every
  *   partial it reads.
  */
-#define UBS_STATIC_SCRATCH_BYTES (16u << 20)
+#define UBS_STATIC_SCRATCH_BYTES (32u << 20)
 int sparse_decode_static(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16_t* v_cache,
                          const int32_t* page_table, const int32_t* seq_lens, int32_t B, int32_t max_pages,
                          int32_t Hq, int32_t Hkv, int32_t D, int32_t P, const uint8_t* head_kind /* host */,

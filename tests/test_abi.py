@@ -328,12 +328,12 @@ def test_prefill_varlen_nothing_to_do():
 
 
 def test_decode_static_rejects_oversized_scratch_before_any_hip_call():
-    """sparse_decode_static keeps its split partials in a 16 MiB library-owned scratch: a
+    """sparse_decode_static keeps its split partials in a 32 MiB library-owned scratch: a
     call needing more is refused with WORKSPACE_TOO_SMALL, validated on the host."""
     lib = ubs.load()
-    B, Hq, Hkv, D, P, ms = 1024, 32, 8, 128, 64, 64
+    B, Hq, Hkv, D, P, ms = 2048, 32, 8, 128, 64, 64
     need = lib.ubs_decode_workspace_size(B, Hq, Hkv, D, P, ms, 128, 512)
-    assert need > 16 << 20
+    assert need > 32 << 20
     rc = lib.sparse_decode_static(A, A, A, A, A, B, 512, Hq, Hkv, D, P, KIND, A, A, ms, 128, 512, 0.088, A, NULL,
                                   NULL)
     assert rc == -3 and "static scratch" in _err()

@@ -298,12 +298,14 @@ size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, 
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_selected < 0 || sink_tokens < 0 ||
       local_tokens < 0)
     return 256;
-  // the split plan depends only on these sizes and the number of dense KV heads: take
-  // the largest over every count
+  // the split plan depends only on these sizes, the number of dense KV heads, the page
+  // format and the waves the device holds at once: take the largest over every count
+  // and both formats, at the most waves a plan spreads over
   int ms = 1;
   for (int nd = 0; nd <= Hkv; ++nd)
     for (int q4 = 0; q4 < 2; ++q4) {
-      const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, nd, P, max_selected, sink_tokens, local_tokens, q4 != 0);
+      const ubs::DecodePlan pl =
+          ubs::plan_decode(B, Hkv, nd, P, max_selected, sink_tokens, local_tokens, q4 != 0, ubs::kMaxWaveSlots);
       ms = pl.max_splits > ms ? pl.max_splits : ms;
     }
   return ((size_t)B * Hq * ms * (D + 2) * sizeof(float) + 255) / 256 * 256;
@@ -358,7 +360,8 @@ static int decode_impl(const char* name, bool int4, bool use_static, const ubs_b
   }
   REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
           "workspace of %zu bytes, need %zu", workspace_bytes, need);
-  const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens, int4);
+  const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens, int4,
+                                              ubs::decode_wave_slots(D, Hq / Hkv, int4 != 0));
   const int64_t blocks = (int64_t)B * (dense.n * pl.splits_dense + streaming.n * pl.splits_stream);
   REQUIRE(blocks < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large", (long long)blocks);
   ubs::DecodeArgs a{};

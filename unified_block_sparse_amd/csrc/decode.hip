@@ -23,10 +23,12 @@
 // (scale s, zero z), x = n s + z. Codes enter the MFMA as the value 16 + n (exact: the
 // code fills the top mantissa bits of 16), so S = s (Q.(16 + n)) + (z - 16 s) sum(Q).
 // P.V runs on the fp16 MFMA, O^T = V^T (P s)^T: V pages are channel-major, so a lane's A
-// operand (8 tokens of one channel) is one word; the weights p s, rounded to fp16, go
-// through LDS as the B operand, and sum p z - 16 sum fp16(p s) joins every channel at the
-// end. (fp16 rather than bf16 for P.V: its 11-bit weights keep the rounding of p s well
-// inside the attention tolerance.)
+// operand (8 tokens of one channel) is one word. The scores are computed transposed as
+// for bf16 pages, with the K rows of the A operand ordered so that lane (qg, m) ends up
+// with head m's scores of tokens 8*qg + [0, 8): the same 8 tokens as its V word, so the
+// weights p s, rounded to fp16, are its B operand as they stand, and sum p z -
+// 16 sum fp16(p s) joins every channel at the end. (fp16 rather than bf16 for P.V: its
+// 11-bit weights keep the rounding of p s well inside the attention tolerance.)
 // Each wave writes its split's partial (max, sum, output) triple (or the output when the
 // key set has one split), and a second launch merges the splits of each (b, g) with a
 // log-sum-exp combine staged in LDS.
@@ -57,9 +59,9 @@ struct ChunkRegs {
 };
 template <int D>
 struct ChunkRegs<D, true> {
-  uint32_t k[kChunkTokens / 16][D / 32];   // K codes of the lane's key rows, 8 per word
-  uint32_t kp[kChunkTokens / 16];          // fp16 (scale, zero) of those K rows
-  uint32_t vp[kChunkTokens / 16];          // ... and of the same V rows
+  uint32_t k[kChunkTokens / 16][D / 32];   // K codes of the lane's two A-operand rows, 8 per word
+  uint32_t kp[8];                          // fp16 (scale, zero) of K rows 8*qg + [0, 8)
+  uint32_t vp[8];                          // ... and of the same V rows
   uint32_t v[D / 16];                      // V codes: channel cb*16 + m, tokens 8*qg + [0, 8)
 };
 
@@ -95,12 +97,6 @@ __device__ __forceinline__ f16x8 codes_f16(uint32_t w) {
   const u32x4 r = {and_or_sv(nibble_pair<0, 6>(w), m, c), and_or_sv(nibble_pair<1, 6>(w), m, c),
                    and_or_sv(nibble_pair<2, 6>(w), m, c), and_or_sv(nibble_pair<3, 6>(w), m, c)};
   return __builtin_bit_cast(f16x8, r);
-}
-
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // max of v over lanes l and l ^ 16 (rows 2r and 2r + 1 of 16 lanes swapped), and over l
@@ -183,9 +179,6 @@ void decode_kernel(const DecodeArgs a) {
   constexpr int NTR = 64 / UPC;     // chunks resolved per round trip (one unit a lane)
   constexpr int CPL = D / 16;       // bf16: V channels a lane holds of each row
   constexpr int WPR = D / 32;       // ... as words
-  __shared__ __attribute__((aligned(16))) float p_t[Q4 ? 4 : 1][16][CT + 4];   // INT4: fp16(p s) [head][token]
-  __shared__ float a_lds[Q4 ? 4 : 1][16];                                       // INT4: per-head factors
-  __shared__ float h_m[Q4 ? 4 : 1][16], h_l[Q4 ? 4 : 1][16];                    // INT4: per-head max, sum
 
   const int lane = lane_id();
   // (wave-uniform, and said so: every index derived from it then stays scalar)
@@ -237,36 +230,27 @@ void decode_kernel(const DecodeArgs a) {
       qa[kk] = as_bf16x8((m < G) ? ld16(qrow + (Q4 ? qg * (D / 4) + kk * 8 : kk * 32 + qg * 8))
                                  : u32x4{0, 0, 0, 0});
   }
-  // INT4: sum of the channels of query heads 4*qg + i (the rows of this lane's scores)
-  float qsum[4] = {0.f, 0.f, 0.f, 0.f};
+  // INT4: sum of the channels of query head m (the head of this lane's scores)
+  float qsum = 0.f;
   if constexpr (Q4) {
-    float sq = 0.f;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const u32x4 w = __builtin_bit_cast(u32x4, qa[kk]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sq += bf16_lo(w[e]) + bf16_hi(w[e]);
+      for (int e = 0; e < 4; ++e) qsum += bf16_lo(w[e]) + bf16_hi(w[e]);
     }
-    sq += shfl_xor(sq, 16);
-    sq += shfl_xor(sq, 32);   // all channels of head m
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qsum[i] = __shfl(sq, 4 * qg + i, 64);
+    qsum = sum_swap16(qsum);
+    qsum = sum_swap32(qsum);   // all channels of head m
   }
 
-  // INT4: running max of heads 4*qg + i (lane-replicated within a 16-lane group); O^T
-  // blocks (lane: channels cb*16 + 4*qg + i of head m), and the lane's sums over its key
-  // rows of p and of p z - 16 fp16(p s) for heads 4*qg + i
-  float m_run[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m_run[i] = kNegInf;
+  // INT4: O^T blocks (lane (qg, m): channels cb*16 + 4*qg + i of head m) and the lane's
+  // sum over its tokens of p z - 16 fp16(p s)
   f32x4 oT[Q4 ? D / 16 : 1];
-  float lsum4[4], zacc4[4];
 #pragma unroll
   for (int cb = 0; cb < (Q4 ? D / 16 : 1); ++cb) oT[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lsum4[i] = zacc4[i] = 0.f;
-  // bf16: lane (qg, m) runs head m: its running max (replicated over qg), its sum over the
-  // lane's key slots, and O^T block j = channels CPL*(4*qg + i) + j of head m
+  float zh = 0.f;
+  // lane (qg, m) runs head m: its running max (replicated over qg), its sum over the
+  // lane's key slots, and (bf16) O^T block j = channels CPL*(4*qg + i) + j of head m
   float mh = kNegInf, lh = 0.f;
   f32x4 ov[Q4 ? 1 : CPL];
 #pragma unroll
@@ -298,8 +282,12 @@ void decode_kernel(const DecodeArgs a) {
   };
   auto load = [&](int t, int nt, ChunkRegs<D, Q4>& R) __attribute__((always_inline)) {
     if constexpr (Q4) {
-      // one unit of 32 rows of one page; rows are clamped into the page, and rows outside
-      // [lo, hi) are loaded but never weighted
+      // one unit of 32 rows of one page. A-operand row m of block blk is token
+      // 8*(m/4) + 4*blk + m%4 (rows clamped into the page), so that the scores of lane
+      // (qg, m') are those of tokens 8*qg + 4*blk + i; the row params of those 8 tokens
+      // (two 16-byte loads each for K and V: 4-row groups lie wholly inside or wholly
+      // past the P*4-byte slab, which reads zeros). Tokens outside [lo, hi) are loaded but
+      // never weighted.
       const int page = unit_page(t, nt, 0);
       const int r0 = __builtin_amdgcn_readlane(d_r0, min(t, 63));
       const __amdgpu_buffer_rsrc_t rk = slab_rsrc4(a.k_codes, page, D / 2);
@@ -308,7 +296,7 @@ void decode_kernel(const DecodeArgs a) {
       const __amdgpu_buffer_rsrc_t rvp = slab_rsrc4(a.v_params, page, 4);
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
-        const int row = min(r0 + blk * 16 + m, P - 1);
+        const int row = min(r0 + 8 * (m >> 2) + 4 * blk + (m & 3), P - 1);
         if constexpr (D == 128) {
           const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rk, row * 64 + qg * 16, 0, 0);
 #pragma unroll
@@ -318,11 +306,18 @@ void decode_kernel(const DecodeArgs a) {
 #pragma unroll
           for (int kk = 0; kk < KK; ++kk) R.k[blk][kk] = w[kk];
         }
-        R.kp[blk] = __builtin_amdgcn_raw_buffer_load_b32(rkp, row * 4, 0, 0);
       }
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk)
-        R.vp[blk] = __builtin_amdgcn_raw_buffer_load_b32(rvp, min(r0 + blk * 16 + m, P - 1) * 4, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int off = (r0 + 8 * qg + 4 * h) * 4;
+        const u32x4 wk = __builtin_amdgcn_raw_buffer_load_b128(rkp, off, 0, 0);
+        const u32x4 wv = __builtin_amdgcn_raw_buffer_load_b128(rvp, off, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          R.kp[4 * h + e] = wk[e];
+          R.vp[4 * h + e] = wv[e];
+        }
+      }
       // (tokens past the page read the next channel's word, or zeros past the slab; their
       // weights are zero)
 #pragma unroll
@@ -370,72 +365,69 @@ void decode_kernel(const DecodeArgs a) {
       if (page < 0) return;
       const int r0 = __builtin_amdgcn_readlane(d_r0, t);
       const int lo = __builtin_amdgcn_readlane(d_lo, t), hi = __builtin_amdgcn_readlane(d_hi, t);
-      // S for NB blocks of 16 rows: lane (qg, m) holds heads 4*qg + i, key blk*16 + m
-      f32x4 s[NB];
+      // S^T per block: lane (qg, m) holds head m, tokens 8*qg + 4*blk + i (A rows ordered
+      // by the load), one score per token j = 4*blk + i of the lane's 8
+      const uint32_t n_ok = (uint32_t)(hi - lo);
+      const int d0 = r0 + 8 * qg - lo;
+      float sj[8];
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int row = r0 + blk * 16 + m;
-        const bool ok = row >= lo && row < hi;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], codes_bf16(R.k[blk][kk]), acc, 0, 0, 0);
-        const float sk = half_lo(R.kp[blk]), zk = half_hi(R.kp[blk]) - 16.f * sk;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s[blk][i] = ok ? fmaf(sk, acc[i], zk * qsum[i]) * scale_log2 : kNegInf;
-      }
-      // chunk max per head (heads 4*qg + i), then running max and weights
-      float alpha_i[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = s[0][i];
-#pragma unroll
-        for (int blk = 1; blk < NB; ++blk) mx = fmaxf(mx, s[blk][i]);
-#pragma unroll
-        for (int o2 = 1; o2 < 16; o2 <<= 1) mx = fmaxf(mx, shfl_xor(mx, o2));
-        const float mn = fmaxf(m_run[i], mx);
-        alpha_i[i] = rescale_factor(m_run[i], mn);
-        m_run[i] = mn;
-      }
-      // weights: p_t[head][token] = fp16(p s_v) (exact as fp32), and the lane's sums
-#pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
-        const int row = r0 + blk * 16 + m;
-        const bool ok = row >= lo && row < hi;   // (params of other rows are not trusted)
-        const float sv = ok ? half_lo(R.vp[blk]) : 0.f, zv = ok ? half_hi(R.vp[blk]) : 0.f;
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(codes_bf16(R.k[blk][kk]), qa[kk], acc, 0, 0, 0);
+        // (the scores are computed for every token and then masked: left to itself the
+        // compiler moves each score into a branch of its own around the mask)
+        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = softmax_weight(s[blk][i], m_run[i]);
-          const float pr = (float)(_Float16)(p * sv);
-          p_t[wave][qg * 4 + i][blk * 16 + m] = pr;
-          lsum4[i] = blk == 0 ? fmaf(lsum4[i], alpha_i[i], p) : lsum4[i] + p;
-          zacc4[i] = fmaf(-16.f, pr, fmaf(p, zv, blk == 0 ? zacc4[i] * alpha_i[i] : zacc4[i]));
+          const int j = 4 * blk + i;
+          const float sk = half_lo(R.kp[j]), zk = half_hi(R.kp[j]) - 16.f * sk;
+          v[i] = fmaf(sk, acc[i], zk * qsum) * scale_log2;
         }
-      }
-      if (m == 0) {
+        asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a_lds[wave][qg * 4 + i] = alpha_i[i];
+        for (int i = 0; i < 4; ++i) sj[4 * blk + i] = ((uint32_t)(d0 + 4 * blk + i) < n_ok) ? v[i] : kNegInf;
       }
-      wave_sync_lds();
-      // B operand: head m, tokens 8*qg + [0, 8); (heads past G give columns never read)
-      const f32x4 p0 = *reinterpret_cast<const f32x4*>(&p_t[wave][m][8 * qg]);
-      const f32x4 p1 = *reinterpret_cast<const f32x4*>(&p_t[wave][m][8 * qg + 4]);
+      // chunk max of head m over the lane's 8 tokens and the 4 lane groups, running max
+      float mx = fmaxf(fmaxf(fmaxf(sj[0], sj[1]), fmaxf(sj[2], sj[3])), fmaxf(fmaxf(sj[4], sj[5]), fmaxf(sj[6], sj[7])));
+      mx = max_swap16(mx);
+      mx = max_swap32(mx);
+      const float mn = fmaxf(mh, mx);
+      // (mr: the max, or 0 while every key so far is masked; the scores are then -inf, so
+      // every weight is 0, and so is alpha, applied to a zero state)
+      const float mr = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(mh - mr);
+      mh = mn;
+      // weights: the B operand fp16(p s_v) of token 2e, 2e + 1 in word e, and the lane's
+      // sums of p and of p z_v - 16 fp16(p s_v) (params of masked tokens are not trusted)
+      float ps = 0.f, pz = 0.f;
       u32x4 pw;
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p0[2 * e], p0[2 * e + 1]}), f16x2));
-        pw[2 + e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{p1[2 * e], p1[2 * e + 1]}), f16x2));
-      }
-      const f16x8 pb = __builtin_bit_cast(f16x8, pw);
-      const float al = a_lds[wave][m];
-      if (__ballot(al != 1.f)) {   // (a head's max grew: rare after the first chunks)
+      for (int e = 0; e < 4; ++e) {
+        float pr[2];
 #pragma unroll
-        for (int cb = 0; cb < D / 16; ++cb) oT[cb] *= al;
+        for (int x = 0; x < 2; ++x) {
+          const int j = 2 * e + x;
+          const bool ok = (uint32_t)(d0 + j) < n_ok;
+          const float sv = ok ? half_lo(R.vp[j]) : 0.f, zv = ok ? half_hi(R.vp[j]) : 0.f;
+          const float p = fast_exp2(sj[j] - mr);
+          pr[x] = (float)(_Float16)(p * sv);
+          ps += p;
+          pz = fmaf(-16.f, pr[x], fmaf(p, zv, pz));
+        }
+        pw[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{pr[0], pr[1]}), f16x2));
+      }
+      lh = fmaf(lh, alpha, ps);
+      zh = fmaf(zh, alpha, pz);
+      const f16x8 pb = __builtin_bit_cast(f16x8, pw);
+      if (__ballot(alpha != 1.f)) {   // (a head's max grew: rare after the first chunks)
+#pragma unroll
+        for (int cb = 0; cb < D / 16; ++cb) oT[cb] *= alpha;
       }
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
         oT[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_f16(R.v[cb]), pb, oT[cb], 0, 0, 0);
-      wave_sync_lds();
     } else {
       const int page0 = unit_page(t, nt, 0), page1 = unit_page(t, nt, 1);
       if (page0 < 0 && page1 < 0) return;
@@ -507,9 +499,12 @@ void decode_kernel(const DecodeArgs a) {
   // ---- the wave's chunks, NTR at a time. Lane l resolves unit l of them to its physical
   // page and valid rows [lo, hi) of the page, so the index chain (selection -> page
   // table) costs one round trip per NTR chunks, before any of their K/V loads. Then the
-  // loads of chunk t+1 are in flight while chunk t is computed (register double buffer;
-  // unrolled by two so each buffer is a fixed register set).
-  ChunkRegs<D, Q4> ra, rb;
+  // loads of chunks t+1 .. t+NBUF-1 are in flight while chunk t is computed (a ring of
+  // NBUF register buffers, the loop unrolled by NBUF so each buffer is a fixed register
+  // set). Two: with INT4 pages a four-deep ring (216 registers, two waves per SIMD) ran
+  // 5% slower than two buffers at three waves per SIMD.
+  constexpr int NBUF = 2;
+  ChunkRegs<D, Q4> rr[NBUF];
   for (int t0 = 0; t0 < cpw; t0 += NTR) {
     const int nt = min(NTR, cpw - t0);
     d_page = -1;
@@ -528,17 +523,17 @@ void decode_kernel(const DecodeArgs a) {
     }
     // (chunks past nt are empty: their loads read nothing and their compute is skipped;
     // the scheduling barriers keep each chunk's loads after the previous compute, so
-    // at most two chunks' registers are live)
-    load(0, nt, ra);
-    for (int t = 0; t < nt; t += 2) {
-      load(t + 1, nt, rb);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(t, nt, ra);
-      __builtin_amdgcn_sched_barrier(0);
-      load(t + 2, nt, ra);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(t + 1, nt, rb);
-      __builtin_amdgcn_sched_barrier(0);
+    // at most NBUF chunks' registers are live)
+#pragma unroll
+    for (int k = 0; k + 1 < NBUF; ++k) load(k, nt, rr[k]);
+    for (int t = 0; t < nt; t += NBUF) {
+#pragma unroll
+      for (int k = 0; k < NBUF; ++k) {
+        load(t + k + NBUF - 1, nt, rr[(k + NBUF - 1) % NBUF]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t + k, nt, rr[k]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   // ---- the wave's split partial (max, sum, output), merged by the second launch
@@ -546,35 +541,21 @@ void decode_kernel(const DecodeArgs a) {
                       (int64_t)split * (D + 2);
   const int64_t head_pitch = (int64_t)a.max_splits * (D + 2);
   if constexpr (Q4) {
-    // sums over the 16 key lanes of each head group; O^T plus the zero term of its head,
-    // exchanged through the wave's LDS rows
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int o2 = 1; o2 < 16; o2 <<= 1) {
-        lsum4[i] += shfl_xor(lsum4[i], o2);
-        zacc4[i] += shfl_xor(zacc4[i], o2);
-      }
-    if (m == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = qg * 4 + i;
-        a_lds[wave][h] = zacc4[i];
-        h_m[wave][h] = m_run[i];
-        h_l[wave][h] = lsum4[i];
-      }
-    }
-    wave_sync_lds();
+    // head m: the sums over the 4 lane groups; lane (qg, m) holds channels cb*16 + 4*qg
+    // + i, each plus the head's zero term
+    lh = sum_swap16(lh);
+    lh = sum_swap32(lh);
+    zh = sum_swap16(zh);
+    zh = sum_swap32(zh);
     if (m < G) {
-      const float z = a_lds[wave][m];
       float* pp = part + m * head_pitch;
 #pragma unroll
       for (int cb = 0; cb < D / 16; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pp[cb * 16 + 4 * qg + i] = oT[cb][i] + z;
+        for (int i = 0; i < 4; ++i) pp[cb * 16 + 4 * qg + i] = oT[cb][i] + zh;
       if (qg == 0) {
-        pp[D] = h_m[wave][m];
-        pp[D + 1] = h_l[wave][m];
+        pp[D] = mh;
+        pp[D + 1] = lh;
       }
     }
   } else {
@@ -651,7 +632,40 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const DecodeArgs a) {
   if (tid == 0 && a.lse) a.lse[qh] = (S > 0.f) ? (M + __log2f(S)) * kLn2 : kNegInf;
 }
 
-DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4) {
+// Waves of the decode kernel for (D, G, int4) that the current device holds at once:
+// work-groups per CU from the occupancy query (registers and LDS of that instance) x 4
+// waves x CUs, at most kMaxWaveSlots; cached per device and instance. 2,048 (two
+// work-groups per CU on 256 CUs) if the query fails.
+int64_t decode_wave_slots(int D, int G, bool int4) {
+  constexpr int64_t kFallback = 2 * 4 * 256;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kFallback;
+  const int gi = 31 - __builtin_clz((unsigned)std::max(G, 1));   // log2 G: 0..4
+  if (gi > 4 || (D != 64 && D != 128)) return kFallback;
+  const int key = ((D == 128) * 5 + gi) * 2 + (int4 ? 1 : 0);   // 0..19
+  static std::mutex mu;
+  static int64_t cache[64][20] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev][key] > 0) return cache[dev][key];
+  const void* fn = nullptr;
+#define UBS_DECODE_FN(DD, GG)                                                                     \
+  if (D == DD && G == GG)                                                                         \
+    fn = int4 ? reinterpret_cast<const void*>(&decode_kernel<DD, GG, true>)                        \
+              : reinterpret_cast<const void*>(&decode_kernel<DD, GG, false>);
+  UBS_DECODE_FN(64, 1) UBS_DECODE_FN(64, 2) UBS_DECODE_FN(64, 4) UBS_DECODE_FN(64, 8) UBS_DECODE_FN(64, 16)
+  UBS_DECODE_FN(128, 1) UBS_DECODE_FN(128, 2) UBS_DECODE_FN(128, 4) UBS_DECODE_FN(128, 8) UBS_DECODE_FN(128, 16)
+#undef UBS_DECODE_FN
+  int n_cu = 0, per_cu = 0;
+  if (fn == nullptr || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 256, 0) != hipSuccess || n_cu <= 0 || per_cu <= 0)
+    return kFallback;
+  const int64_t slots = std::min<int64_t>((int64_t)per_cu * 4 * n_cu, kMaxWaveSlots);
+  cache[dev][key] = slots;
+  return slots;
+}
+
+DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4,
+                       int64_t wave_slots) {
   DecodePlan pl{};
   // key lists in units of U rows of one page (16 for bf16 pages, 32 for INT4), two or one
   // units a 32-token chunk
@@ -664,11 +678,11 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   const int nd = n_dense, ns = Hkv - n_dense;
   const int cd = std::max(pl.chunks_dense, 1), cs = std::max(pl.chunks_stream, 1);
   // Chunks per split: the fewest that keep every wave of the launch resident at once
-  // (2 work-groups of 4 waves on each of the 256 CUs): all waves then resolve their pages
-  // before the memory system fills up, and none starts its index chain behind the K/V
-  // traffic of others; and few enough splits for the merge. The kernel then cuts each
-  // list into that many splits of equal size (to one chunk).
-  constexpr int64_t kWaves = 4 * 2 * 256;
+  // (wave_slots: what the device holds of this kernel): all waves then resolve their
+  // pages before the memory system fills up, and none starts its index chain behind the
+  // K/V traffic of others; and few enough splits for the merge. The kernel then cuts
+  // each list into that many splits of equal size (to one chunk).
+  const int64_t kWaves = std::max<int64_t>(1, std::min(wave_slots, kMaxWaveSlots));
   auto waves = [&](int c) {
     return (int64_t)B * ((int64_t)nd * ((cd + c - 1) / c) + (int64_t)ns * ((cs + c - 1) / c));
   };

@@ -149,11 +149,16 @@ struct DecodePlan {
   int chunks_per_wave;
   int splits_dense, splits_stream, max_splits;
 };
-DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4);
+// Largest number of decode waves a plan spreads a launch over (4 waves per SIMD on 256
+// CUs); the workspace size is computed for it, an upper bound of every launch's plan.
+constexpr int64_t kMaxWaveSlots = 4 * 4 * 256;
+int64_t decode_wave_slots(int D, int G, bool int4);
+DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4,
+                       int64_t wave_slots);
 
 // Size of the library-owned scratch of sparse_decode_static (per GPU), and its device
 // address on the current device (resolved on the first call there).
-constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
 hipError_t static_scratch(void** ptr);
 
 hipError_t launch_bounds(const BoundsArgs& a, hipStream_t s);
