@@ -73,6 +73,11 @@ DECODE4_CASES = [
     ([1000, 129, 5000], 4, 4, 64, 128, 8, [0, 0, 1, 0], 3 * 128, 128, 1024),
     ([20000, 777], 16, 2, 128, 64, 16, [1, 0], 64 * 64, 100, 3000),
     ([3000, 20], 2, 2, 128, 16, 16, [0, 1], 16 * 16, 7, 33),
+    # 16-row units that straddle pages (P = 48, 80: not powers of two), G = 1 with D = 64,
+    # G = 16 over 256-token pages with a long local window
+    ([3000, 1234, 77], 16, 4, 128, 48, 16, [0, 1, 1, 0], 10 * 48, 40, 200),
+    ([9000, 300], 8, 8, 64, 80, 16, [0, 1, 0, 1, 0, 1, 0, 1], 7 * 80, 16, 500),
+    ([40000], 64, 4, 128, 256, 64, [0, 1, 0, 0], 20 * 256, 256, 2048),
 ]
 
 

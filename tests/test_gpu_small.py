@@ -114,6 +114,11 @@ DECODE_CASES = [
     ([50000], 8, 1, 128, 64, 64, [0], 600 * 64, 0, 0),
     ([20000, 777], 16, 2, 128, 64, 16, [1, 1], 64, 1000, 3000),
     ([3000, 20], 2, 2, 128, 16, 1 * 16, [0, 1], 16 * 16, 7, 33),
+    # 16-row units that straddle pages (P = 48, 80: not powers of two), G = 1 with D = 64,
+    # G = 16 over 256-token pages with a long local window
+    ([3000, 1234, 77], 16, 4, 128, 48, 16, [0, 1, 1, 0], 10 * 48, 40, 200),
+    ([9000, 300], 8, 8, 64, 80, 16, [0, 1, 0, 1, 0, 1, 0, 1], 7 * 80, 16, 500),
+    ([40000], 64, 4, 128, 256, 64, [0, 1, 0, 0], 20 * 256, 256, 2048),
 ]
 
 
