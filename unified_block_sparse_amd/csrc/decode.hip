@@ -4,21 +4,23 @@
 // streaming heads in decode as well).
 //
 // Work split: one (sequence b, KV head g, split s) per WAVE, four independent waves per
-// 256-thread work-group. The key set of (b, g) is a list of 32-token chunks, each inside
-// one physical page (a part of a selected page, or of a page of the sink / local window),
-// cut into balanced splits; split s of (b, g) streams its chunks s*cpw ... + cpw - 1. The
-// split size is chosen so that every wave of the launch is resident at once (one round of
-// at most 2,048 waves on the 256 CUs): each wave resolves its pages at the start, while
-// the memory system is idle (one round trip through the selection and the page table for
-// up to 64 chunks; under load that chain costs several microseconds a link), then streams
-// to its end with no barrier. It keeps the K/V loads of chunk t+1 in flight while it
-// computes chunk t:
-//   S = Q_g K^T  : bf16 MFMA 16x16x32 (rows = the G query heads, columns = 16 keys),
-//                  K rows read straight from HBM, each load instruction 64 contiguous
-//                  bytes of each of 16 rows;
-//   online softmax in the log2 domain (fp32);
-//   O += P V     : fp32 FMAs, each lane owning 8 channels of one key row, V read with
-//                  16-byte loads that cover whole rows, P broadcast through LDS.
+// 256-thread work-group. The key set of (b, g) is a list of 16-row units, each inside one
+// physical page (a part of a selected page, or of a page of the sink / local window), two
+// units a 32-key chunk (INT4 pages: 32-row units, one a chunk), cut into splits of equal
+// size. The split size is chosen so that
+// every wave of the launch is resident at once (as many waves as the GPU holds of this
+// kernel): each wave resolves its pages at the start, while the memory system is idle
+// (one round trip through the selection and the page table for up to 64 units; under
+// load that chain costs several microseconds a link), then streams to its end with no
+// barrier. It keeps the K/V loads of chunk t+1 in flight while it computes chunk t:
+//   S^T = K Q_g^T : bf16 MFMA 16x16x32 (rows = 16 keys of a unit, columns = the G query
+//                   heads), K rows read straight from HBM, each load instruction 64
+//                   contiguous bytes of each of 16 rows; lane (qg, m) then holds head
+//                   m's scores of its 8 key slots;
+//   online softmax in the log2 domain (fp32), row max by lane swaps;
+//   O^T += V^T P^T: bf16 MFMA 16x16x32; the lane's weights (bf16) are its B operand as
+//                   they stand, and its A operand (8 keys of one channel) comes from its
+//                   own 16-byte V row loads by byte permutes.
 // INT4 pages (same kernel, Q4 = true): rows come as 4-bit codes n with a per-row fp16
 // (scale s, zero z), x = n s + z. Codes enter the MFMA as the value 16 + n (exact: the
 // code fills the top mantissa bits of 16), so S = s (Q.(16 + n)) + (z - 16 s) sum(Q).
@@ -29,9 +31,8 @@
 // weights p s, rounded to fp16, are its B operand as they stand, and sum p z -
 // 16 sum fp16(p s) joins every channel at the end. (fp16 rather than bf16 for P.V: its
 // 11-bit weights keep the rounding of p s well inside the attention tolerance.)
-// Each wave writes its split's partial (max, sum, output) triple (or the output when the
-// key set has one split), and a second launch merges the splits of each (b, g) with a
-// log-sum-exp combine staged in LDS.
+// Each wave writes its split's partial (max, sum, output) triple, and a second launch
+// merges the splits of each (b, query head) with a log-sum-exp combine staged in LDS.
 #include "common.h"
 #include "launch.h"
 
