@@ -46,7 +46,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 PEAK_HBM_GBPS = 8000.0
 METRIC = "sparse prefill TFLOP/s (kept tiles) + decode KV GB/s, as % of MI355X roofline"
-LEGS = ("step", "tiny", "graph", "ragged", "extreme", "mask", "varlen", "cpu")
+LEGS = ("step", "tiny", "graph", "ragged", "extreme", "mask", "varlen", "peaks", "cpu")
 # The pages' own figures for this method, quoted as context (relative speedups, no hardware
 # or absolute numbers given): LServe index page, Abstract.
 PAGES_CONTEXT = ("LServe (arXiv 2502.14866) abstract: up to 2.9x prefill and 1.3-2.1x decode speedup over "
@@ -116,6 +116,55 @@ def gemm_ceiling():
         ms = e0.elapsed_time(e1) / reps
         print(json.dumps({"gemm_bf16_n": n, "ms": round(ms, 4), "tflops": round(2 * n ** 3 / ms / 1e9, 1),
                           "frac_of_peak": round(2 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}), flush=True)
+
+
+def measured_peaks():
+    """What this GPU sustains, measured beside the published peaks:
+    - the matrix cores on back-to-back bf16 MFMAs from registers (ubs_bench_mfma: no
+      memory traffic, at whatever clock the GPU holds under that load);
+    - the vendor bf16 GEMM (hipBLASLt through torch.matmul, n = 16384, compute-bound);
+    - a plain HBM read of 8 GiB (ubs_bench_read: 16-byte loads, one contiguous share per
+      work-group) and a 4 GiB device copy (torch; read + written bytes).
+    The per-workload fractions are also given against the GEMM and the plain read."""
+    import torch
+    import unified_block_sparse_amd as ubs
+    dev = torch.device("cuda:0")
+
+    def timed(f, reps, warm=2):
+        for _ in range(warm):
+            f()
+        torch.cuda.synchronize(dev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            f()
+            ev[i + 1].record()
+        torch.cuda.synchronize(dev)
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(reps))
+        return t[len(t) // 2]
+
+    out = torch.zeros(4, dtype=torch.float32, device=dev)
+    iters = 40000
+    flops = ubs.bench_mfma(iters, out)
+    t_m = timed(lambda: ubs.bench_mfma(iters, out), 5)
+    n = 16384
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    t_g = timed(lambda: a @ b, 5)
+    del a, b
+    x = torch.ones(8 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    t_r = timed(lambda: ubs.bench_read(x, sink), 10)
+    del x
+    src = torch.ones(4 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t_c = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"mfma_loop_bf16_tflops": round(flops / t_m / 1e12, 1),
+            "gemm_bf16_tflops": round(2 * n ** 3 / t_g / 1e12, 1), "gemm_n": n,
+            "hbm_read_gbps": round((8 << 30) / t_r / 1e9, 1), "hbm_copy_gbps": round((8 << 30) / t_c / 1e9, 1),
+            "note": "medians of timed calls; copy counts bytes read + written"}
 
 
 # ----------------------------------------------------------------------------- work accounting
@@ -739,6 +788,8 @@ def main():
         wall = time.perf_counter() - t0
         per_op = {name: sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)) / args.steps * 1e-3
                   for i, (name, _) in enumerate(ops)}
+        i_pf = [name for name, _ in ops].index("sparse_prefill")
+        t_pf_all = sorted(ev[s][i_pf].elapsed_time(ev[s][i_pf + 1]) for s in range(args.steps))
         # the selection every timed step made (the same in each: same inputs)
         sel_h, num_h = sel.cpu().tolist(), num.cpu().tolist()
         sel_pages = [[sel_h[b][g][:num_h[b][g]] for g in range(d.Hkv)] for b in range(d.B)]
@@ -771,6 +822,8 @@ def main():
             name: {"ms": round(per_op[name] * 1e3, 4), "roofline_ms": round(ideal[name] * 1e3, 4),
                    "frac": round(ideal[name] / per_op[name], 4)} for name, _ in ops}
         breakdown["sparse_prefill"]["tflops"] = round(achieved, 2)
+        breakdown["sparse_prefill"]["ms_median"] = round(t_pf_all[len(t_pf_all) // 2], 4)
+        breakdown["sparse_prefill"]["ms_min"] = round(t_pf_all[0], 4)
         breakdown["build_page_bounds"]["gbps"] = round(b_bounds / per_op["build_page_bounds"] / 1e9, 1)
         breakdown["select_pages"]["gbps"] = round(b_select / per_op["select_pages"] / 1e9, 1)
         breakdown["sparse_decode"]["gbps"] = round(b_decode / per_op["sparse_decode"] / 1e9, 1)
@@ -844,6 +897,17 @@ def main():
             oracle_extra["prefill_extreme"] = r.pop("_oracle")
         legs_out["prefill_extreme"] = r
         per_config["prefill_extreme"] = {"frac": r["frac"], "bound": "mfma", "ms": r["ms"], "tflops": r["tflops"]}
+
+    if "peaks" in legs:
+        pk = measured_peaks()
+        legs_out["measured_peaks"] = pk
+        for name, pc in per_config.items():
+            if pc.get("bound") == "mfma" and "tflops" in pc:
+                pc["frac_of_measured"] = round(pc["tflops"] / pk["gemm_bf16_tflops"], 4)
+            elif pc.get("bound") == "hbm" and "gbps" in pc:
+                pc["frac_of_measured"] = round(pc["gbps"] / pk["hbm_read_gbps"], 4)
+        if result is not None:
+            result["measured_peaks"] = pk
 
     if result is None:
         print(json.dumps({"legs": legs_out, "per_config": per_config, "oracle": oracle_extra}), flush=True)

@@ -1,5 +1,5 @@
 """C ABI checks that need no GPU: the library loads, exports every function that
-include/ubs.h declares, and host-side validation returns the documented error codes
+include/*.h declares, and host-side validation returns the documented error codes
 before any HIP call (so only fake, never-dereferenced pointers are passed)."""
 import ctypes
 import os
@@ -16,9 +16,14 @@ NULL = None
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "ubs.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*[\s\*]+([A-Za-z_]\w*)\s*\(", src, flags=re.M))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*[\s\*]+([A-Za-z_]\w*)\s*\(", src, flags=re.M))
+    return names
 
 
 def test_library_exports_every_declared_symbol():
@@ -341,3 +346,14 @@ def test_decode_static_rejects_oversized_scratch_before_any_hip_call():
                                     NULL, NULL) == -2
     assert lib.sparse_decode_static(A, A, A, A, A, 0, 512, Hq, Hkv, D, P, KIND, A, A, ms, 128, 512, 0.088, A,
                                     NULL, NULL) == 0
+
+
+def test_bench_helpers_validate_before_any_hip_call():
+    lib = ubs.load()
+    assert lib.ubs_bench_read(NULL, 1024, A, NULL) == -1
+    assert lib.ubs_bench_read(A, 1024, NULL, NULL) == -1
+    assert lib.ubs_bench_read(A + 4, 1024, A, NULL) == -1     # misaligned
+    assert lib.ubs_bench_read(A, 8, A, NULL) == -1            # under 16 bytes
+    assert lib.ubs_bench_mfma(0, A, NULL) == -1
+    assert lib.ubs_bench_mfma(10, NULL, NULL) == -1
+

@@ -21,9 +21,9 @@ Build the library with ``python -m unified_block_sparse_amd.build``.
 """
 from ._lib import (UBSError, load, sparse_prefill, sparse_prefill_chunk, sparse_prefill_varlen, build_page_bounds,  # noqa: F401
                    select_pages, sparse_decode, estimate_block_mask, append_kv, quantize_kv_int4,
-                   sparse_decode_int4, check_paged, check_status, LIB_PATH, EXPORTED)
+                   sparse_decode_int4, check_paged, check_status, bench_read, bench_mfma, LIB_PATH, EXPORTED)
 
 __all__ = ["UBSError", "load", "sparse_prefill", "sparse_prefill_chunk", "sparse_prefill_varlen", "build_page_bounds",
            "select_pages",
            "sparse_decode", "estimate_block_mask", "append_kv", "quantize_kv_int4", "sparse_decode_int4",
-           "check_paged", "check_status"]
+           "check_paged", "check_status", "bench_read", "bench_mfma"]

@@ -27,6 +27,7 @@ EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "sparse_prefill_varlen", "
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
             "append_kv", "quantize_kv_int4", "sparse_decode_int4", "sparse_decode_static",
             "ubs_check_paged", "ubs_check_status",
+            "ubs_bench_read", "ubs_bench_mfma", "ubs_bench_mfma_waves",
             "ubs_last_error", "ubs_version")
 
 
@@ -95,6 +96,12 @@ def load() -> ctypes.CDLL:
         lib.ubs_check_paged.argtypes = [_p, _i, _i, _p, _p, _i, _i, _p, _i, _p, _p, _i, _p, _p]
         lib.ubs_check_status.restype = ctypes.c_int
         lib.ubs_check_status.argtypes = [_p, _p]
+        lib.ubs_bench_read.restype = ctypes.c_int
+        lib.ubs_bench_read.argtypes = [_p, _sz, _p, _p]
+        lib.ubs_bench_mfma.restype = ctypes.c_int
+        lib.ubs_bench_mfma.argtypes = [_i, _p, _p]
+        lib.ubs_bench_mfma_waves.restype = ctypes.c_int64
+        lib.ubs_bench_mfma_waves.argtypes = []
         _lib = lib
         return lib
 
@@ -583,3 +590,24 @@ def check_status(status: torch.Tensor) -> None:
     lib = load()
     rc = lib.ubs_check_status(_ptr(status), _stream(status.device))
     _check("ubs_check_status", rc)
+
+
+# ----------------------------------------------------------------------------- measurement helpers
+
+def bench_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Read all of `buf` once (include/ubs_bench.h: ubs_bench_read); `sink` is a device
+    tensor of at least 4 bytes. For timing the plain read rate with events."""
+    if not (buf.is_cuda and sink.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf and sink must be contiguous GPU tensors")
+    lib = load()
+    _check("ubs_bench_read", lib.ubs_bench_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                _stream(buf.device)))
+
+
+def bench_mfma(iters: int, out: torch.Tensor) -> int:
+    """Back-to-back bf16 MFMAs on every SIMD (include/ubs_bench.h: ubs_bench_mfma); returns
+    the flops the call performs."""
+    lib = load()
+    _check("ubs_bench_mfma", lib.ubs_bench_mfma(int(iters), _ptr(out), _stream(out.device)))
+    return int(lib.ubs_bench_mfma_waves()) * int(iters) * 4 * 32768
+
