@@ -237,8 +237,9 @@ int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* p
  *     out[b][h][:] = sum_t softmax_t(sm_scale * q[b][h] . k_t) * v_t
  *     lse[b][h]    = ln sum_t exp(sm_scale * q[b][h] . k_t)
  * An empty key set gives out = 0, lse = -inf. The key set is split across
- * work-groups (split-KV); partial (max, sum, output) triples are merged with a
- * log-sum-exp combine. Arithmetic is fp32 on bf16 inputs.
+ * waves (split-KV); partial (max, sum, output) triples are merged with a
+ * log-sum-exp combine. Scores, softmax and accumulation are fp32 on bf16 inputs;
+ * the weights enter the P.V product rounded to bf16, as in sparse_prefill.
  *
  *   q             bf16 [B][Hq][D]
  *   selected      int32 [B][Hkv][max_selected], entries in [0, ceil(L/P)),
