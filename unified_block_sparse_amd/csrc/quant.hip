@@ -75,10 +75,27 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
         const _Float16 s16 = (_Float16)__fdiv_rn(hi - lo, 15.0f);
         const _Float16 z16 = (_Float16)lo;
         const float s = (float)s16, z = (float)z16;
+        // n = rint((x - z) / s) with the division correctly rounded. The quotient by the
+        // correctly rounded reciprocal, q' = RN((x - z) RN(1/s)), is within 1.5 * 2^-23
+        // |q| of the exact one, so rint gives the same integer unless q' lies within
+        // 2^-17 of a half-integer (a bound for |q| < 16; quotients outside [-0.5, 15.5]
+        // clamp whatever their last bits). A wave with such a lane divides exactly.
+        const float rs = s == 0.f ? 0.f : __fdiv_rn(1.0f, s);
+        float q[8];
+        bool near = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          q[e] = (x[e] - z) * rs;
+          near |= fabsf(q[e] - floorf(q[e]) - 0.5f) < 0x1p-17f;
+        }
+        if (__ballot(near)) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) q[e] = s == 0.f ? 0.f : __fdiv_rn(x[e] - z, s);
+        }
         uint32_t code[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          code[e] = (uint32_t)(s == 0.f ? 0.f : fminf(fmaxf(__builtin_rintf(__fdiv_rn(x[e] - z, s)), 0.f), 15.f));
+          code[e] = (uint32_t)(s == 0.f ? 0.f : fminf(fmaxf(__builtin_rintf(q[e]), 0.f), 15.f));
         if (kv == 0) {
           uint32_t word = 0;
 #pragma unroll
