@@ -65,6 +65,29 @@ def test_quantize_int4_bit_exact(lens, Hkv, D, P):
     assert np.all(gv[~sel] == 0x5A), "v words outside the sequences touched"
 
 
+def test_quantize_int4_half_integer_quotients():
+    """Rows whose quotients (x - zero) / scale fall exactly on half-integers, and just
+    beside them: every row spans [0, 15] (scale 1, zero 0) and holds k + 0.5 for every
+    k < 15 (exact in bf16) and k + 0.5 -/+ 1/64 (rounded to bf16: beside the tie, or onto
+    it), so rint's ties (to even) occur many times a row. Codes and params bit-exact
+    against the oracle."""
+    P, D, Hkv, L = 16, 128, 2, 16
+    k = torch.arange(D, dtype=torch.float32)
+    ties = (k % 15) + 0.5                                  # 0.5 .. 14.5
+    row = torch.where(k % 3 == 0, ties, torch.where(k % 3 == 1, ties - 1 / 64, ties + 1 / 64))
+    row[0], row[1] = 0.0, 15.0                             # the row's range: scale 1, zero 0
+    rows = torch.stack([torch.roll(row, int(r)) for r in range(P)])       # [P, D], each a permutation
+    cache = rows.to(torch.bfloat16).reshape(1, 1, P, D).repeat(1, Hkv, 1, 1).contiguous().to(DEV)
+    pt = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+    kc, vc, kp, vp = ubs.quantize_kv_int4(cache, cache, pt, lens)
+    _sync()
+    rkq, rvq, rkp, rvp, written = oracle.quantize_cache_int4_ref(bits(cache), bits(cache), pt.cpu().numpy(), [L], P)
+    assert written.all()
+    assert np.array_equal(_u8(kc), rkq) and np.array_equal(_u8(vc), rvq), "codes differ"
+    assert np.array_equal(_u16(kp), rkp) and np.array_equal(_u16(vp), rvp), "params differ"
+
+
 DECODE4_CASES = [
     # lens, Hq, Hkv, D, P, Lp, head_kind, budget, sink, local
     ([37, 16, 1, 50, 0, 300], 8, 2, 128, 16, 4, [0, 1], 4 * 16, 5, 20),
