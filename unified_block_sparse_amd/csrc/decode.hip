@@ -690,6 +690,11 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   const int64_t total = (int64_t)B * ((int64_t)nd * cd + (int64_t)ns * cs);
   int cpw = (int)std::max<int64_t>(1, (total + kWaves - 1) / kWaves);
   while (cpw < std::max(cd, cs) && waves(cpw) > kWaves) ++cpw;
+  // At least 4 chunks a split: a wave's fixed part (resolving its pages, writing its
+  // partial, its share of the merge) costs about as much as streaming two chunks, so
+  // smaller splits lose more than the extra waves gain (Llama-3-8B decode, 4 sequences:
+  // a step of 31.4 us at 2 chunks a split, 27.6 at 4, 28.8 at 5, 31.6 at 8).
+  cpw = std::max(cpw, 4);
   // (measurement override: UBS_DECODE_CPW sets the chunks per split; the result does not
   // depend on it beyond the order of the split merge)
   if (const char* e = getenv("UBS_DECODE_CPW")) {
