@@ -87,6 +87,8 @@ def test_select_matches_oracle(lens, Hq, Hkv, D, P, Lp, hk, budget):
 
 @pytest.mark.parametrize("lens,P,Lp,budget", [
     ([3000, 777, 4096], 64, 16, 10 * 64),   # rows of at most 64 pages (one key per thread)
+    ([6400, 1000], 16, 16, 25 * 16),        # 400 pages (two keys per thread)
+    ([9000, 2500], 16, 16, 30 * 16),        # 563 pages (four keys per thread)
     ([20000, 3000], 16, 16, 40 * 16),       # a row of 1,250 pages (eight keys per thread)
 ])
 def test_select_exact_ties_break_to_lower_index(lens, P, Lp, budget):

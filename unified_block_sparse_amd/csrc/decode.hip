@@ -4,7 +4,9 @@
 // streaming heads in decode as well).
 //
 // Work split: one (sequence b, KV head g, split s) per WAVE, four independent waves per
-// 256-thread work-group. The key set of (b, g) is a list of 16-row units, each inside one
+// work-group (two or one for a launch too small to give every CU two work-groups: a CU
+// streams only its share of the bandwidth, so a small launch must reach them all). The
+// key set of (b, g) is a list of 16-row units, each inside one
 // physical page (a part of a selected page, or of a page of the sink / local window), two
 // units a 32-key chunk (INT4 pages: 32-row units, one a chunk), cut into splits of equal
 // size. The split size is chosen so that
@@ -192,7 +194,7 @@ void decode_kernel(const DecodeArgs a) {
   // groups go to the XCDs in turn), gets the same mix of the two list lengths.
   const int nS = a.streaming.n * a.splits_stream;
   const int per_b = a.dense.n * a.splits_dense + nS;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t gw = (int64_t)blockIdx.x * a.waves_per_group + wave;
   if (gw >= (int64_t)a.B * per_b) return;
   const int b = (int)(gw / per_b);
   const int r = (int)(gw % per_b);
@@ -742,19 +744,50 @@ hipError_t static_scratch(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  const int per_b = a.dense.n * a.splits_dense + a.streaming.n * a.splits_stream;
-  const int64_t blocks = ((int64_t)a.B * per_b + 3) / 4;   // one split per wave
-  if (blocks == 0) return hipSuccess;
+int device_cu_count() {
+  constexpr int kFallback = 256;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kFallback;
+  static std::mutex mu;
+  static int cache[64] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return kFallback;
+  cache[dev] = n;
+  return n;
+}
+
+int waves_per_group(int64_t waves, const char* env) {
+  if (env != nullptr) {
+    if (const char* e = getenv(env)) {
+      const int v = atoi(e);
+      if (v == 1 || v == 2 || v == 4) return v;
+    }
+  }
+  const int64_t cus = device_cu_count();
+  int wpg = 4;
+  while (wpg > 1 && (waves + wpg - 1) / wpg < 2 * cus) wpg >>= 1;
+  return wpg;
+}
+
+hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
+  const int per_b = args.dense.n * args.splits_dense + args.streaming.n * args.splits_stream;
+  const int64_t waves = (int64_t)args.B * per_b;   // one split per wave
+  if (waves == 0) return hipSuccess;
+  DecodeArgs a = args;
+  a.waves_per_group = waves_per_group(waves, "UBS_DECODE_WPG");
+  const int64_t blocks = (waves + a.waves_per_group - 1) / a.waves_per_group;
+  const dim3 block((unsigned)(64 * a.waves_per_group));
   const int G = a.Hq / a.Hkv;
   const int64_t merge_blocks = (int64_t)a.B * a.Hq;   // one work-group per (b, query head)
   const size_t merge_lds = (size_t)(((int64_t)a.max_splits * (a.D + 2) + 255) / 256 * 256 + a.max_splits) * sizeof(float);
 #define UBS_DECODE(DD, GG)                                                                            \
   if (a.D == DD && G == GG) {                                                                         \
     if (a.int4)                                                                                       \
-      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);  \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), dim3((unsigned)blocks), block, 0, s, a);     \
     else                                                                                              \
-      hipLaunchKernelGGL((decode_kernel<DD, GG, false>), dim3((unsigned)blocks), dim3(256), 0, s, a); \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, false>), dim3((unsigned)blocks), block, 0, s, a);    \
     hipError_t e = hipGetLastError();                                                                 \
     if (e != hipSuccess || merge_blocks == 0) return e;                                               \
     hipLaunchKernelGGL((decode_merge_kernel<DD>), dim3((unsigned)merge_blocks), dim3(256), merge_lds, s, a); \

@@ -67,6 +67,7 @@ struct DecodeArgs {
   float* lse;
   float* partials;     // workspace [B][Hq][max_splits][D + 2]
   int max_splits;
+  int waves_per_group;   // waves of a work-group (1, 2 or 4): set by launch_decode
   // INT4 pages (int4 != 0): codes [NP][Hkv][P][D/2], fp16 (scale, zero) [NP][Hkv][P][2]
   int int4;
   const uint8_t* k_codes;
@@ -153,6 +154,13 @@ struct DecodePlan {
 // CUs); the workspace size is computed for it, an upper bound of every launch's plan.
 constexpr int64_t kMaxWaveSlots = 4 * 4 * 256;
 int64_t decode_wave_slots(int D, int G, bool int4);
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+// Waves a work-group of a wave-independent launch (no work-group barrier) of `waves`
+// waves: 4, or fewer while the launch would otherwise have under two work-groups per CU,
+// so that a small launch still reaches every CU (each CU streams only its share of the
+// bandwidth). `env` names a measurement override (1, 2 or 4).
+int waves_per_group(int64_t waves, const char* env);
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4,
                        int64_t wave_slots);
 

@@ -32,10 +32,11 @@ __device__ __forceinline__ uint32_t pos_part_bf16x2(uint32_t w) {
   return lo | hi;
 }
 
-// Grid: blockIdx.x = ((b * n_dense) + dense index) * chunks + chunk. Each wave scores
+// Grid: blockIdx.x = ((b * n_dense) + dense index) * chunks + chunk, wpg waves a
+// work-group (4, fewer for a small launch). Each wave scores
 // `gpw` groups of 16 consecutive sub-pages of its (b, g); with U = P/Lp sub-pages per
 // page a group covers 16/U whole pages. At most 128 registers a lane: the allocator then
-// keeps the D = 128 kernel in 80 vector registers (6 waves per SIMD) instead of 95 plus 4
+// keeps the D = 128 kernel in 81 vector registers (5 waves per SIMD) instead of 95 plus 4
 // accumulation registers (4 waves); more waves keep more record loads in flight.
 template <int D, int U, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
@@ -44,7 +45,7 @@ void score_kernel(const uint16_t* __restrict__ q,
                   const int32_t* __restrict__ page_table,
                   const int32_t* __restrict__ seq_lens,
                   int max_pages, int Hq, int Hkv, int P, int Lp,
-                  HeadList dense, int chunks, int gpw,
+                  HeadList dense, int chunks, int wpg, int gpw,
                   float* __restrict__ scores) {
   constexpr int KK = D / 16;  // MFMA steps over the 2D-long record (K = 32 each)
   const int lane = lane_id();
@@ -57,7 +58,7 @@ void score_kernel(const uint16_t* __restrict__ q,
   const int L = seq_lens[b];
   const int n_pages = (L + P - 1) / P;
   const int n_sub = n_pages * U;
-  const int first_group = (chunk * 4 + wave) * gpw;
+  const int first_group = (chunk * wpg + wave) * gpw;
   if (first_group * 16 >= n_sub) return;
 
   // A operand: row m = query head of the group, k-slot (l/16)*8 + i of step kk maps
@@ -261,13 +262,13 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
 }
 
 template <int D, int U>
-static hipError_t launch_score_du(const SelectArgs& a, int G, int chunks, int gpw, hipStream_t s) {
+static hipError_t launch_score_du(const SelectArgs& a, int G, int chunks, int wpg, int gpw, hipStream_t s) {
   const dim3 grid((unsigned)(a.B * a.dense.n * chunks));
 #define UBS_SCORE_G(GG)                                                                          \
   if (G == GG) {                                                                                 \
-    hipLaunchKernelGGL((score_kernel<D, U, GG>), grid, dim3(256), 0, s, a.q, a.bounds,           \
+    hipLaunchKernelGGL((score_kernel<D, U, GG>), grid, dim3(64 * wpg), 0, s, a.q, a.bounds,      \
                        a.page_table, a.seq_lens, a.max_pages, a.Hq, a.Hkv, a.P, a.Lp, a.dense,   \
-                       chunks, gpw, a.scores);                                                   \
+                       chunks, wpg, gpw, a.scores);                                              \
     return hipGetLastError();                                                                    \
   }
   UBS_SCORE_G(1) UBS_SCORE_G(2) UBS_SCORE_G(4) UBS_SCORE_G(8) UBS_SCORE_G(16)
@@ -280,13 +281,14 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int U = a.P / a.Lp;
   if (a.dense.n > 0) {
-    // groups of 16 sub-pages per (b, dense g); a wave takes gpw groups, a WG 4 waves
+    // groups of 16 sub-pages per (b, dense g); a wave takes gpw groups, a WG wpg waves
     const int64_t groups = ((int64_t)a.max_pages * U + 15) / 16;
     const int gpw = groups >= 256 ? 2 : 1;
-    const int chunks = (int)((groups + 4 * gpw - 1) / (4 * gpw));
+    const int wpg = waves_per_group((int64_t)a.B * a.dense.n * ((groups + gpw - 1) / gpw), "UBS_SCORE_WPG");
+    const int chunks = (int)((groups + wpg * gpw - 1) / (wpg * gpw));
     hipError_t e = hipErrorInvalidValue;
 #define UBS_SCORE_DU(DD, UU) \
-    if (a.D == DD && U == UU) e = launch_score_du<DD, UU>(a, G, chunks, gpw, s);
+    if (a.D == DD && U == UU) e = launch_score_du<DD, UU>(a, G, chunks, wpg, gpw, s);
     UBS_SCORE_DU(64, 1) UBS_SCORE_DU(64, 2) UBS_SCORE_DU(64, 4) UBS_SCORE_DU(64, 8) UBS_SCORE_DU(64, 16)
     UBS_SCORE_DU(128, 1) UBS_SCORE_DU(128, 2) UBS_SCORE_DU(128, 4) UBS_SCORE_DU(128, 8) UBS_SCORE_DU(128, 16)
 #undef UBS_SCORE_DU
