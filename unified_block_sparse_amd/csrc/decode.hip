@@ -80,26 +80,34 @@ __device__ __forceinline__ uint32_t nibble_pair(uint32_t w) {
   constexpr int sh = 4 * J - POS;   // nibble J of each half to bit POS of that half
   return sh >= 0 ? w >> sh : w << -sh;
 }
-// (x & m) | c in one instruction. The three-operand form takes no literal and at most one
-// scalar operand on this architecture: m goes in a scalar register, c in a vector register
-// (loop-invariant, so set once); written with literals, the compiler emits an and and an
-// or, a third more vector instructions for the codes of a chunk.
-__device__ __forceinline__ uint32_t and_or_sv(uint32_t x, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
-  return r;
+// (x_i & m) | c for the four pairs of a word, one instruction each. The three-operand form
+// takes no literal and at most one scalar operand on this architecture: m goes in a
+// scalar register, c in a vector register (loop-invariant, so set once); written with
+// literals, the compiler emits an and and an or, a third more vector instructions for the
+// codes of a chunk. The four results are MFMA operands, and an MFMA may read a register
+// only two wait states after a vector instruction has written it: the compiler inserts
+// those waits for its own instructions but cannot see into inline assembly, so the block
+// ends with them (s_nop 1). Without them, an MFMA placed right after the block has read
+// stale operands. (Early-clobber outputs: each is written before the last input is read.)
+__device__ __forceinline__ u32x4 and_or4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, uint32_t m,
+                                         uint32_t c) {
+  uint32_t r0, r1, r2, r3;
+  asm("v_and_or_b32 %0, %4, %8, %9\n"
+      "v_and_or_b32 %1, %5, %8, %9\n"
+      "v_and_or_b32 %2, %6, %8, %9\n"
+      "v_and_or_b32 %3, %7, %8, %9\n"
+      "s_nop 1"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "s"(m), "v"(c));
+  return u32x4{r0, r1, r2, r3};
 }
 __device__ __forceinline__ bf16x8 codes_bf16(uint32_t w) {
-  constexpr uint32_t m = 0x00780078u, c = 0x41804180u;
-  const u32x4 r = {and_or_sv(nibble_pair<0, 3>(w), m, c), and_or_sv(nibble_pair<1, 3>(w), m, c),
-                   and_or_sv(nibble_pair<2, 3>(w), m, c), and_or_sv(nibble_pair<3, 3>(w), m, c)};
-  return as_bf16x8(r);
+  return as_bf16x8(and_or4(nibble_pair<0, 3>(w), nibble_pair<1, 3>(w), nibble_pair<2, 3>(w),
+                           nibble_pair<3, 3>(w), 0x00780078u, 0x41804180u));
 }
 __device__ __forceinline__ f16x8 codes_f16(uint32_t w) {
-  constexpr uint32_t m = 0x03C003C0u, c = 0x4C004C00u;
-  const u32x4 r = {and_or_sv(nibble_pair<0, 6>(w), m, c), and_or_sv(nibble_pair<1, 6>(w), m, c),
-                   and_or_sv(nibble_pair<2, 6>(w), m, c), and_or_sv(nibble_pair<3, 6>(w), m, c)};
-  return __builtin_bit_cast(f16x8, r);
+  return __builtin_bit_cast(f16x8, and_or4(nibble_pair<0, 6>(w), nibble_pair<1, 6>(w), nibble_pair<2, 6>(w),
+                                           nibble_pair<3, 6>(w), 0x03C003C0u, 0x4C004C00u));
 }
 
 // max of v over lanes l and l ^ 16 (rows 2r and 2r + 1 of 16 lanes swapped), and over l
