@@ -18,6 +18,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <cstdlib>
+
 namespace ubs {
 
 __device__ __forceinline__ uint32_t neg_part_bf16x2(uint32_t w) {
@@ -33,7 +35,7 @@ __device__ __forceinline__ uint32_t pos_part_bf16x2(uint32_t w) {
 }
 
 // Grid: blockIdx.x = ((b * n_dense) + dense index) * chunks + chunk, wpg waves a
-// work-group (4, fewer for a small launch). Each wave scores
+// work-group (one, unless a measurement override says otherwise). Each wave scores
 // `gpw` groups of 16 consecutive sub-pages of its (b, g); with U = P/Lp sub-pages per
 // page a group covers 16/U whole pages. At most 128 registers a lane: the allocator then
 // keeps the D = 128 kernel in 81 vector registers (5 waves per SIMD) instead of 95 plus 4
@@ -281,10 +283,24 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int U = a.P / a.Lp;
   if (a.dense.n > 0) {
-    // groups of 16 sub-pages per (b, dense g); a wave takes gpw groups, a WG wpg waves
+    // groups of 16 sub-pages per (b, dense g); a wave takes gpw groups. One wave a
+    // work-group (wpg = 1): the waves past a short row's end then leave the CU at once
+    // instead of holding a 4-wave group's slot while its other waves stream, and small
+    // launches reach every CU (ragged batch: selection 132-133 against 142 us with 4-wave
+    // groups; Llama-3-8B decode step 27.2 against 27.7 us).
     const int64_t groups = ((int64_t)a.max_pages * U + 15) / 16;
-    const int gpw = groups >= 256 ? 2 : 1;
-    const int wpg = waves_per_group((int64_t)a.B * a.dense.n * ((groups + gpw - 1) / gpw), "UBS_SCORE_WPG");
+    int gpw = groups >= 256 ? 2 : 1;
+    // (measurement overrides: UBS_SCORE_GPW sets the groups per wave, 1 or 2, and
+    // UBS_SCORE_WPG the waves per work-group, 1, 2 or 4; the scores do not depend on them)
+    if (const char* env = getenv("UBS_SCORE_GPW")) {
+      const int v = atoi(env);
+      if (v == 1 || v == 2) gpw = v;
+    }
+    int wpg = 1;
+    if (const char* env = getenv("UBS_SCORE_WPG")) {
+      const int v = atoi(env);
+      if (v == 1 || v == 2 || v == 4) wpg = v;
+    }
     const int chunks = (int)((groups + wpg * gpw - 1) / (wpg * gpw));
     hipError_t e = hipErrorInvalidValue;
 #define UBS_SCORE_DU(DD, UU) \
