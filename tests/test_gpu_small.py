@@ -90,6 +90,7 @@ def test_select_matches_oracle(lens, Hq, Hkv, D, P, Lp, hk, budget):
     ([6400, 1000], 16, 16, 25 * 16),        # 400 pages (two keys per thread)
     ([9000, 2500], 16, 16, 30 * 16),        # 563 pages (four keys per thread)
     ([20000, 3000], 16, 16, 40 * 16),       # a row of 1,250 pages (eight keys per thread)
+    ([262144, 3000], 16, 16, 100 * 16),     # 16,384 pages, the most select_pages takes (64 keys per thread)
 ])
 def test_select_exact_ties_break_to_lower_index(lens, P, Lp, budget):
     """Integer-valued q and keys make many page scores tie exactly (the sums are exact in
