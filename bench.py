@@ -427,11 +427,13 @@ def varlen_prefill(steps: int, warmup: int):
 # ----------------------------------------------------------------------------- graph-replayed decode
 
 def decode_graph_step(R: int = 24, replays: int = 10):
-    """Selection + decode of decode_llama8b, cycled over R independent cache instances
-    (seeds 1002 + r) captured once as one HIP graph: R x ~43 MB > 1 GiB of working set, so
-    each step reads HBM rather than the Infinity Cache, and graph replay takes the host
-    launch path out of the step. Time per step = replay time / R. Every replay's outputs
-    are checked bitwise against an eager run of the same calls before capture.
+    """Selection + decode of decode_llama8b (one sparse_decode_select call: page scores,
+    then the decode kernel ranking each row's scores itself, then the split merge), cycled
+    over R independent cache instances (seeds 1002 + r) captured once as one HIP graph:
+    R x ~43 MB > 1 GiB of working set, so each step reads HBM rather than the Infinity Cache,
+    and graph replay takes the host launch path out of the step. Time per step = replay
+    time / R. Every replay's outputs are checked bitwise against an eager run of the same
+    calls before capture.
     """
     import torch
     import unified_block_sparse_amd as ubs
@@ -448,18 +450,16 @@ def decode_graph_step(R: int = 24, replays: int = 10):
         out = torch.empty((d.B, d.Hq, d.D), dtype=torch.float32, device=dev)
         inst.append((d, bnd, sel, num, out))
     d0 = inst[0][0]
-    ws_sel = torch.zeros(max(256, lib.ubs_select_workspace_size(d0.B, d0.page_table.shape[1], d0.Hkv)),
-                         dtype=torch.uint8, device=dev)
-    ws_dec = torch.zeros(max(256, lib.ubs_decode_workspace_size(d0.B, d0.Hq, d0.Hkv, d0.D, d0.P, d0.k_pages,
-                                                                d0.sink_tokens, d0.local_tokens)),
-                         dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(256, lib.ubs_decode_select_workspace_size(d0.B, d0.page_table.shape[1], d0.Hq, d0.Hkv,
+                                                                   d0.D, d0.P, d0.token_budget, d0.sink_tokens,
+                                                                   d0.local_tokens)),
+                     dtype=torch.uint8, device=dev)
 
     def run_all():
         for d, bnd, sel, num, out in inst:
-            ubs.select_pages(d.q, bnd, d.page_table, d.seq_lens_t, d.head_kind, d.P, d.token_budget,
-                             selected=sel, num_selected=num, workspace=ws_sel)
-            ubs.sparse_decode(d.q, d.k_cache, d.v_cache, d.page_table, d.seq_lens_t, d.head_kind, sel, num,
-                              d.sink_tokens, d.local_tokens, d.sm_scale, out=out, workspace=ws_dec)
+            ubs.sparse_decode_select(d.q, bnd, d.k_cache, d.v_cache, d.page_table, d.seq_lens_t, d.head_kind, d.P,
+                                     d.token_budget, d.sink_tokens, d.local_tokens, d.sm_scale, out=out,
+                                     selected=sel, num_selected=num, workspace=ws)
 
     run_all()
     torch.cuda.synchronize(dev)
@@ -878,7 +878,7 @@ def main():
         r = decode_graph_step()
         legs_out["decode_step_graph"] = r
         per_config["decode_llama8b_step"] = {"frac": r["frac"], "bound": "hbm", "ms": r["ms"], "gbps": r["gbps"],
-                                             "note": "select_pages + sparse_decode, HIP graph over 24 instances"}
+                                             "note": "sparse_decode_select (scores, decode with in-kernel top-k, merge), HIP graph over 24 instances"}
     if "varlen" in legs:
         legs_out["sparse_prefill_varlen"] = varlen_prefill(max(2, args.steps // 4), 2)
     if "ragged" in legs:

@@ -16,6 +16,7 @@
  *   select_pages       query-aware page scores and top-k selection.
  *   sparse_decode      GQA decode attention over the kept pages (dense heads)
  *                      or the sink and local tokens (streaming heads).
+ *   sparse_decode_select  select_pages and sparse_decode in one call.
  *   estimate_block_mask  the dense heads' prefill block mask from mean-pooled
  *                      query/key tile scores.
  *   append_kv          new tokens into the paged cache, with the page summaries
@@ -260,6 +261,43 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
                   const int32_t* selected, const int32_t* num_selected, int32_t max_selected,
                   int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out, float* lse,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sparse_decode_select -- select_pages followed by sparse_decode, in one call.
+ *
+ * The decode step of the blog's "LServe -- Decode Phase" section as one pipeline
+ * (Figure 2: page scores from the per-page key bounds, the top pages under the
+ * token budget, then token-level attention inside them). Results are those of
+ *   select_pages(q, bounds, ..., token_budget, selected, num_selected)
+ *   sparse_decode(q, k_cache, v_cache, ..., selected, num_selected,
+ *                 max_selected = token_budget / P, ...)
+ * bit for bit: the same selection, ties to the lower page index, and the same
+ * outputs. The work differs: for rows of at most 1,024 pages (max_pages <= 1024) and
+ * token_budget / P <= 1,024, each decode wave of a dense head ranks its row's page
+ * scores itself, so the separate top-k launch is skipped; longer rows run the two
+ * calls' kernels as they are.
+ *
+ *   q, bounds, page_table, seq_lens, head_kind, P, Lp, token_budget
+ *                 as for select_pages; k_cache, v_cache, sink_tokens, local_tokens,
+ *                 sm_scale as for sparse_decode
+ *   selected      int32 [B][Hkv][token_budget / P]   (output, as select_pages writes it)
+ *   num_selected  int32 [B][Hkv]                      (output)
+ *   out, lse      as for sparse_decode
+ *   workspace     >= ubs_decode_select_workspace_size(...) bytes, any contents
+ * Supported: the intersection of select_pages and sparse_decode (D in {64, 128};
+ * Hq/Hkv and P/Lp in {1, 2, 4, 8, 16}; P in {16, 32, 64, 128}; max_pages <= 16384).
+ * Errors: as for the two calls.
+ */
+size_t ubs_decode_select_workspace_size(int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t P, int32_t token_budget, int32_t sink_tokens,
+                                        int32_t local_tokens);
+int sparse_decode_select(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const ubs_bf16_t* k_cache,
+                         const ubs_bf16_t* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                         int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                         int32_t Lp, int32_t token_budget, const uint8_t* head_kind /* host */,
+                         int32_t sink_tokens, int32_t local_tokens, float sm_scale, int32_t* selected,
+                         int32_t* num_selected, float* out, float* lse, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
 
 /*
  * sparse_decode_static -- sparse_decode that allocates nothing and takes no workspace.

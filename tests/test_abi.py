@@ -154,6 +154,45 @@ def test_decode_workspace_grows_with_budget():
     assert big > small >= 4 * 8 * 4
 
 
+def _dsel(**kw):
+    lib = ubs.load()
+    a = dict(q=A, bnd=A, k=A, v=A, pt=A, sl=A, B=4, maxp=512, Hq=32, Hkv=8, D=128, P=64, Lp=64, budget=4096,
+             kind=KIND, sink=128, local=512, scale=0.088, sel=A, nsel=A, out=A, lse=NULL, ws=A, wsb=None,
+             stream=NULL)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.ubs_decode_select_workspace_size(a["B"], a["maxp"], a["Hq"], a["Hkv"], a["D"], a["P"],
+                                                        a["budget"], a["sink"], a["local"])
+    return lib.sparse_decode_select(a["q"], a["bnd"], a["k"], a["v"], a["pt"], a["sl"], a["B"], a["maxp"], a["Hq"],
+                                    a["Hkv"], a["D"], a["P"], a["Lp"], a["budget"], a["kind"], a["sink"],
+                                    a["local"], a["scale"], a["sel"], a["nsel"], a["out"], a["lse"], a["ws"],
+                                    a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    # the selection half
+    (dict(budget=4000), -2), (dict(budget=0), -1), (dict(Lp=2), -2), (dict(Hq=24), -2), (dict(P=256), -2),
+    (dict(maxp=20000), -2), (dict(ws=None), -3), (dict(wsb=16), -3), (dict(bnd=None), -1), (dict(sel=None), -1),
+    (dict(nsel=None), -1),
+    # the decode half (including a workspace that covers the scores but not the partials)
+    (dict(k=None), -1), (dict(out=None), -1), (dict(k=A + 4), -1), (dict(scale=0.0), -1), (dict(sink=-1), -1),
+    (dict(wsb="scores_only"), -3),
+    # nothing to do
+    (dict(B=0), 0),
+])
+def test_decode_select_validation(kw, code):
+    if kw.get("wsb") == "scores_only":
+        kw = dict(kw, wsb=ubs.load().ubs_select_workspace_size(4, 512, 8) + 256)
+    assert _dsel(**kw) == code
+
+
+def test_decode_select_workspace_is_both_workspaces():
+    lib = ubs.load()
+    sel = lib.ubs_select_workspace_size(4, 512, 8)
+    dec = lib.ubs_decode_workspace_size(4, 32, 8, 128, 64, 64, 128, 512)
+    assert lib.ubs_decode_select_workspace_size(4, 512, 32, 8, 128, 64, 4096, 128, 512) == sel + dec
+
+
 def test_binding_rejects_cpu_tensors():
     import torch
     q = torch.zeros((4, 32, 128), dtype=torch.bfloat16)

@@ -16,14 +16,15 @@ and the steps around them in serving:
     append_kv            new tokens into the paged cache, page bounds refreshed
     quantize_kv_int4     INT4 pages of the cache (per-row 4-bit codes, fp16 scale/zero)
     sparse_decode_int4   sparse_decode over the INT4 pages
+    sparse_decode_select select_pages + sparse_decode in one call (same results)
 
 Build the library with ``python -m unified_block_sparse_amd.build``.
 """
 from ._lib import (UBSError, load, sparse_prefill, sparse_prefill_chunk, sparse_prefill_varlen, build_page_bounds,  # noqa: F401
-                   select_pages, sparse_decode, estimate_block_mask, append_kv, quantize_kv_int4,
+                   select_pages, sparse_decode, sparse_decode_select, estimate_block_mask, append_kv, quantize_kv_int4,
                    sparse_decode_int4, check_paged, check_status, bench_read, bench_mfma, LIB_PATH, EXPORTED)
 
 __all__ = ["UBSError", "load", "sparse_prefill", "sparse_prefill_chunk", "sparse_prefill_varlen", "build_page_bounds",
            "select_pages",
-           "sparse_decode", "estimate_block_mask", "append_kv", "quantize_kv_int4", "sparse_decode_int4",
+           "sparse_decode", "sparse_decode_select", "estimate_block_mask", "append_kv", "quantize_kv_int4", "sparse_decode_int4",
            "check_paged", "check_status", "bench_read", "bench_mfma"]

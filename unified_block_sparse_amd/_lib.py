@@ -26,6 +26,7 @@ CHECK_STATUS_BYTES = 64
 EXPORTED = ("sparse_prefill", "sparse_prefill_chunk", "sparse_prefill_varlen", "build_page_bounds", "select_pages", "ubs_select_workspace_size",
             "sparse_decode", "ubs_decode_workspace_size", "estimate_block_mask", "ubs_mask_workspace_size",
             "append_kv", "quantize_kv_int4", "sparse_decode_int4", "sparse_decode_static",
+            "sparse_decode_select", "ubs_decode_select_workspace_size",
             "ubs_check_paged", "ubs_check_status",
             "ubs_bench_read", "ubs_bench_mfma", "ubs_bench_mfma_waves",
             "ubs_last_error", "ubs_version")
@@ -81,6 +82,11 @@ def load() -> ctypes.CDLL:
         lib.sparse_decode_int4.restype = ctypes.c_int
         lib.sparse_decode_int4.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i,
                                            _i, _f, _p, _p, _p, _sz, _p]
+        lib.ubs_decode_select_workspace_size.restype = _sz
+        lib.ubs_decode_select_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i, _i, _i, _i]
+        lib.sparse_decode_select.restype = ctypes.c_int
+        lib.sparse_decode_select.argtypes = [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _i, _i,
+                                             _f, _p, _p, _p, _p, _p, _sz, _p]
         lib.sparse_decode_static.restype = ctypes.c_int
         lib.sparse_decode_static.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _i,
                                              _f, _p, _p, _p]
@@ -346,6 +352,60 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            workspace.numel() * workspace.element_size(), st)
     _check("sparse_decode", rc)
     return (out, lse) if return_lse else out
+
+
+def sparse_decode_select(q: torch.Tensor, bounds: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         page_table: torch.Tensor, seq_lens: torch.Tensor, head_kind: Sequence[int], P: int,
+                         token_budget: int, sink_tokens: int, local_tokens: int, sm_scale: float,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         return_lse: bool = False, selected: Optional[torch.Tensor] = None,
+                         num_selected: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """select_pages then sparse_decode in one call (see include/ubs.h). Returns (out, selected,
+    num_selected), and lse after out with return_lse: out fp32 [B, Hq, D], selected int32
+    [B, Hkv, token_budget / P], num_selected int32 [B, Hkv]."""
+    lib = load()
+    B, Hq, D = q.shape
+    NP, Hkv, P2, D2 = k_cache.shape
+    NPb, Hkv2, U, two, D3 = bounds.shape
+    _, max_pages = page_table.shape
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    _need(bounds, "bounds", torch.bfloat16, device=dev)
+    _need(k_cache, "k_cache", torch.bfloat16, device=dev)
+    _need(v_cache, "v_cache", torch.bfloat16, shape=k_cache.shape, device=dev)
+    _need(page_table, "page_table", torch.int32, shape=(B, max_pages), device=dev)
+    _need(seq_lens, "seq_lens", torch.int32, shape=(B,), device=dev)
+    if P2 != P or D2 != D or D3 != D or Hkv2 != Hkv or two != 2 or P % U:
+        raise ValueError("k_cache must be [NP, Hkv, P, D] and bounds [NP, Hkv, P/Lp, 2, D]")
+    Lp = P // U
+    if token_budget <= 0 or token_budget % P:
+        raise ValueError("token_budget must be a positive multiple of P")
+    k = token_budget // P
+    if selected is None:
+        selected = torch.empty((B, Hkv, k), dtype=torch.int32, device=dev)
+    if num_selected is None:
+        num_selected = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    _need(selected, "selected", torch.int32, shape=(B, Hkv, k), device=dev)
+    _need(num_selected, "num_selected", torch.int32, shape=(B, Hkv), device=dev)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, shape=(B, Hq, D), device=dev)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, shape=(B, Hq), device=dev)
+    st = _stream(dev)
+    need = lib.ubs_decode_select_workspace_size(B, max_pages, Hq, Hkv, D, P, token_budget, sink_tokens,
+                                                local_tokens)
+    if workspace is None:
+        workspace = _workspace("decode_select", dev, st, need)
+    rc = lib.sparse_decode_select(_ptr(q), _ptr(bounds), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                  _ptr(seq_lens), B, max_pages, Hq, Hkv, D, P, Lp, token_budget, _kinds(head_kind),
+                                  sink_tokens, local_tokens, float(sm_scale), _ptr(selected), _ptr(num_selected),
+                                  _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  st)
+    _check("sparse_decode_select", rc)
+    return (out, lse, selected, num_selected) if return_lse else (out, selected, num_selected)
 
 
 def quantize_kv_int4(k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,

@@ -243,10 +243,14 @@ size_t ubs_select_workspace_size(int32_t B, int32_t max_pages, int32_t Hkv) {
   return ((size_t)B * Hkv * max_pages * sizeof(float) + 255) / 256 * 256;
 }
 
-int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* page_table,
-                 const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D,
-                 int32_t P, int32_t Lp, int32_t token_budget, const uint8_t* head_kind, int32_t* selected,
-                 int32_t* num_selected, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Shared body of select_pages and the selection half of sparse_decode_select: validates
+// every argument, then (launch) enqueues the scores and, unless score_only (the decode
+// kernel then ranks them), the top-k.
+static int select_impl(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* page_table,
+                       const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D,
+                       int32_t P, int32_t Lp, int32_t token_budget, const uint8_t* head_kind, int32_t* selected,
+                       int32_t* num_selected, void* workspace, size_t workspace_bytes, bool score_only,
+                       bool launch, hipStream_t stream) {
   int rc = common_heads(Hq, Hkv, D);
   if (rc) return rc;
   REQUIRE(B >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT, "B=%d, max_pages=%d must be >= 0", B, max_pages);
@@ -290,7 +294,17 @@ int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* p
   a.selected = selected;
   a.num_selected = num_selected;
   a.scores = static_cast<float*>(workspace);
+  a.score_only = score_only ? 1 : 0;
+  if (!launch) return ok();
   return hip_status(ubs::launch_select(a, stream), "select_pages launch");
+}
+
+int select_pages(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const int32_t* page_table,
+                 const int32_t* seq_lens, int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D,
+                 int32_t P, int32_t Lp, int32_t token_budget, const uint8_t* head_kind, int32_t* selected,
+                 int32_t* num_selected, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return select_impl(q, bounds, page_table, seq_lens, B, max_pages, Hq, Hkv, D, P, Lp, token_budget, head_kind,
+                     selected, num_selected, workspace, workspace_bytes, false, true, stream);
 }
 
 size_t ubs_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
@@ -318,7 +332,12 @@ static int decode_impl(const char* name, bool int4, bool use_static, const ubs_b
                        int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                        const uint8_t* head_kind, const int32_t* selected, const int32_t* num_selected,
                        int32_t max_selected, int32_t sink_tokens, int32_t local_tokens, float sm_scale, float* out,
-                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                       float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       bool launch = true, const float* fused_scores = nullptr, int32_t* sel_out = nullptr,
+                       int32_t* nsel_out = nullptr) {
+  // fused (fused_scores != NULL): the kernel ranks the page scores itself and writes the
+  // selection to sel_out / nsel_out ([B][Hkv][max_selected], [B][Hkv])
+  const bool fused = fused_scores != nullptr;
   int rc = common_heads(Hq, Hkv, D);
   if (rc) return rc;
   REQUIRE(B >= 0 && max_pages >= 0, UBS_ERR_INVALID_ARGUMENT, "B=%d, max_pages=%d must be >= 0", B, max_pages);
@@ -346,9 +365,14 @@ static int decode_impl(const char* name, bool int4, bool use_static, const ubs_b
     REQUIRE(aligned16(q) && aligned16(k) && aligned16(v), UBS_ERR_INVALID_ARGUMENT,
             "q, k_cache and v_cache must be 16-byte aligned");
   }
-  REQUIRE(dense.n == 0 || max_selected == 0 || (selected && num_selected), UBS_ERR_INVALID_ARGUMENT,
-          "selected / num_selected are NULL but a KV head is dense");
-  REQUIRE(dense.n == 0 || num_selected, UBS_ERR_INVALID_ARGUMENT, "num_selected is NULL but a KV head is dense");
+  if (fused) {
+    REQUIRE(sel_out && nsel_out, UBS_ERR_INVALID_ARGUMENT, "selected and num_selected must be non-NULL");
+  } else {
+    REQUIRE(dense.n == 0 || max_selected == 0 || (selected && num_selected), UBS_ERR_INVALID_ARGUMENT,
+            "selected / num_selected are NULL but a KV head is dense");
+    REQUIRE(dense.n == 0 || num_selected, UBS_ERR_INVALID_ARGUMENT,
+            "num_selected is NULL but a KV head is dense");
+  }
   const size_t need = ubs_decode_workspace_size(B, Hq, Hkv, D, P, max_selected, sink_tokens, local_tokens);
   if (use_static) {
     REQUIRE(need <= ubs::kStaticScratchBytes, UBS_ERR_WORKSPACE_TOO_SMALL,
@@ -401,6 +425,13 @@ static int decode_impl(const char* name, bool int4, bool use_static, const ubs_b
   a.lse = lse;
   a.partials = static_cast<float*>(workspace);
   a.max_splits = pl.max_splits;
+  if (fused) {
+    a.scores = fused_scores;
+    a.fused_k = max_selected;
+    a.sel_out = sel_out;
+    a.nsel_out = nsel_out;
+  }
+  if (!launch) return ok();
   std::string what = std::string(name) + " launch";
   return hip_status(ubs::launch_decode(a, stream), what.c_str());
 }
@@ -425,6 +456,47 @@ int sparse_decode_static(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const u
   return decode_impl("sparse_decode_static", false, true, q, k_cache, v_cache, nullptr, nullptr, page_table,
                      seq_lens, B, max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, max_selected,
                      sink_tokens, local_tokens, sm_scale, out, lse, nullptr, 0, stream);
+}
+
+size_t ubs_decode_select_workspace_size(int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D,
+                                        int32_t P, int32_t token_budget, int32_t sink_tokens,
+                                        int32_t local_tokens) {
+  if (P <= 0 || token_budget <= 0) return 512;
+  // [page scores | split partials], each a multiple of 256 bytes
+  return ubs_select_workspace_size(B, max_pages, Hkv) +
+         ubs_decode_workspace_size(B, Hq, Hkv, D, P, token_budget / P, sink_tokens, local_tokens);
+}
+
+int sparse_decode_select(const ubs_bf16_t* q, const ubs_bf16_t* bounds, const ubs_bf16_t* k_cache,
+                         const ubs_bf16_t* v_cache, const int32_t* page_table, const int32_t* seq_lens,
+                         int32_t B, int32_t max_pages, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                         int32_t Lp, int32_t token_budget, const uint8_t* head_kind, int32_t sink_tokens,
+                         int32_t local_tokens, float sm_scale, int32_t* selected, int32_t* num_selected,
+                         float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // workspace: [page scores (ws_sel bytes) | split partials]; every argument of both
+  // halves is checked before anything is enqueued
+  const size_t ws_sel = ubs_select_workspace_size(B, max_pages, Hkv);
+  void* ws_dec = workspace ? static_cast<void*>(static_cast<char*>(workspace) + ws_sel) : nullptr;
+  const size_t ws_dec_bytes = workspace_bytes > ws_sel ? workspace_bytes - ws_sel : 0;
+  int rc = select_impl(q, bounds, page_table, seq_lens, B, max_pages, Hq, Hkv, D, P, Lp, token_budget, head_kind,
+                       selected, num_selected, workspace, workspace_bytes, false, false, stream);
+  if (rc) return rc;
+  const int32_t k = token_budget / P;
+  const bool fused = max_pages <= ubs::kMaxFusedPages && k <= ubs::kMaxFusedK;
+  const float* scores = static_cast<const float*>(workspace);
+  rc = decode_impl("sparse_decode_select", false, false, q, k_cache, v_cache, nullptr, nullptr, page_table,
+                   seq_lens, B, max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, k, sink_tokens,
+                   local_tokens, sm_scale, out, lse, ws_dec, ws_dec_bytes, stream, false,
+                   fused ? scores : nullptr, selected, num_selected);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  rc = select_impl(q, bounds, page_table, seq_lens, B, max_pages, Hq, Hkv, D, P, Lp, token_budget, head_kind,
+                   selected, num_selected, workspace, ws_sel, fused, true, stream);
+  if (rc) return rc;
+  return decode_impl("sparse_decode_select", false, false, q, k_cache, v_cache, nullptr, nullptr, page_table,
+                     seq_lens, B, max_pages, Hq, Hkv, D, P, head_kind, selected, num_selected, k, sink_tokens,
+                     local_tokens, sm_scale, out, lse, ws_dec, ws_dec_bytes, stream, true,
+                     fused ? scores : nullptr, selected, num_selected);
 }
 
 int sparse_decode_int4(const ubs_bf16_t* q, const uint8_t* k_codes, const uint8_t* v_codes, const uint16_t* k_params,

@@ -137,14 +137,14 @@ struct Chunk {
 };
 
 __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streaming, int b, int g, int c,
-                                              int L, int nsel) {
+                                              int L, int nsel, const int32_t* sel_row, int sel_cap) {
   Chunk ch{-1, 0, 0, 0};
   const int P = a.P;
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
   if (!streaming) {
     // (the selection entry is read before num_selected is known, so that the two loads,
     // and the sequence length, make one round trip; every slot below max_selected exists)
-    const int j = c < a.max_selected ? a.selected[((int64_t)b * a.Hkv + g) * a.max_selected + c] : -1;
+    const int j = c < sel_cap ? sel_row[c] : -1;
     if (c >= nsel) return ch;
     if (j < 0 || (int64_t)j * P >= L) return ch;
     ch.page = pt[j];
@@ -174,6 +174,110 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
   ch.t0 = max(j * P, Bs);
   ch.t1 = min(j * P + P, L);
   return ch;
+}
+
+// Selection inside the decode kernel: the wave's row of page scores (n pages, at most
+// kMaxFusedPages) ranked as topk_kernel ranks it (the k-th largest order-preserving key by
+// a bitwise search from the first bit where the row's keys differ, ties to the lower page
+// index), with every count a sum of the wave's own ballots and every prefix sum a wave
+// scan. The kept pages go in ascending order to sel[0, k) (this wave's LDS); with `write`
+// also to gsel / gnum (the caller's selection outputs). Lane t owns pages t*EPT ..
+// t*EPT + EPT - 1 (EPT = 8 or 16 from max_pages), so lane order is page order. Returns
+// the number kept, min(n, k).
+__device__ __forceinline__ int wave_scan_excl(int v, int& total) {
+  const int lane = lane_id();
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  total = __shfl(x, 63, 64);
+  return x - v;
+}
+template <int EPT>
+__device__ __forceinline__ int wave_topk(const float* __restrict__ sc, const int* __restrict__ seq_len, int P,
+                                         int max_pages, int k, __attribute__((address_space(3))) int32_t* sel,
+                                         int32_t* gsel, int32_t* gnum, bool write) {
+  const int lane = lane_id();
+  // the row's scores are loaded before its length is known (one round trip for both);
+  // entries past the row's pages are never ranked
+  float raw[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int j = lane * EPT + e;
+    raw[e] = j < max_pages ? sc[j] : 0.f;
+  }
+  const int L = *seq_len;
+  const int n = (L + P - 1) / P;
+  if (n <= k) {
+    for (int i = lane; i < k; i += 64) {
+      const int v = i < n ? i : -1;
+      sel[i] = v;
+      if (write) gsel[i] = v;
+    }
+    if (write && lane == 0) *gnum = n;
+    return n;
+  }
+  uint32_t key[EPT];
+  uint32_t kmin = ~0u, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const bool valid = lane * EPT + e < n;
+    key[e] = valid ? float_order_key(raw[e]) : 0u;   // valid keys are > 0
+    if (valid) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  const int top = kmin == kmax ? -1 : 31 - __builtin_clz(kmin ^ kmax);
+  uint32_t tau = kmin == kmax ? kmax : (top == 31 ? 0u : (kmax & ~((2u << top) - 1u)));
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = tau | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) c += __popcll(__ballot(key[e] >= cand));
+    if (c >= k) tau = cand;
+    if (c == k) break;
+  }
+  int gt = 0, ties = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    gt += key[e] > tau;
+    ties += key[e] == tau;
+  }
+  int n_gt, tie_total, kept_total;
+  wave_scan_excl(gt, n_gt);
+  int tie_rank = wave_scan_excl(ties, tie_total);
+  const int take_ties = k - n_gt;
+  uint32_t keep = 0;
+  int kept = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    bool kp = key[e] > tau;
+    if (key[e] == tau) {
+      kp = tie_rank < take_ties;
+      ++tie_rank;
+    }
+    keep |= (uint32_t)kp << e;
+    kept += kp;
+  }
+  int pos = wave_scan_excl(kept, kept_total);
+#pragma unroll
+  for (int e = 0; e < EPT; ++e)
+    if ((keep >> e) & 1u) {
+      const int j = lane * EPT + e;
+      sel[pos] = j;
+      if (write) gsel[pos] = j;
+      ++pos;
+    }
+  if (write && lane == 0) *gnum = k;
+  return k;
 }
 
 // At most 256 registers a lane (two waves per SIMD) wherever that costs no spill: the
@@ -213,7 +317,35 @@ void decode_kernel(const DecodeArgs a) {
   const int g = streaming ? a.streaming.h[idx / n_splits] : a.dense.h[idx / n_splits];
   const int split = idx % n_splits;
   const int L = a.seq_lens[b];
-  const int nsel = streaming ? 0 : min(a.num_selected[(int64_t)b * a.Hkv + g], a.max_selected);
+  // the (b, g) selection: read from `selected`, or (fused) ranked by this wave into its LDS
+  extern __shared__ int32_t fused_lds[];
+  const int64_t row = (int64_t)b * a.Hkv + g;
+  const int32_t* sel_row = a.selected + row * a.max_selected;
+  int sel_cap = a.max_selected;
+  int nsel = 0;
+  if (a.fused_k > 0) {
+    __attribute__((address_space(3))) int32_t* my_sel =
+        (__attribute__((address_space(3))) int32_t*)fused_lds + wave * a.fused_k;
+    if (!streaming) {
+      const float* sc = a.scores + row * a.max_pages;
+      nsel = a.max_pages <= 512
+                 ? wave_topk<8>(sc, a.seq_lens + b, a.P, a.max_pages, a.fused_k, my_sel, a.sel_out + row * a.fused_k,
+                                a.nsel_out + row, split == 0)
+                 : wave_topk<16>(sc, a.seq_lens + b, a.P, a.max_pages, a.fused_k, my_sel,
+                                 a.sel_out + row * a.fused_k, a.nsel_out + row, split == 0);
+      // (the other lanes' entries are read below: LDS writes of one wave complete in order)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else if (split == 0) {
+      // a streaming head's row of the selection outputs: nothing selected
+      for (int i = lane; i < a.fused_k; i += 64) a.sel_out[row * a.fused_k + i] = -1;
+      if (lane == 0) a.nsel_out[row] = 0;
+    }
+    sel_row = (const int32_t*)my_sel;
+    sel_cap = a.fused_k;
+  } else {
+    nsel = streaming ? 0 : min(a.num_selected[row], a.max_selected);
+  }
   const float scale_log2 = a.sm_scale * kLog2e;
 
   // ---- this wave's chunks c0 .. c0 + cpw - 1 of the (b, g) list (split s of S takes
@@ -522,7 +654,7 @@ void decode_kernel(const DecodeArgs a) {
     d_r0 = d_lo = d_hi = 0;
     if (lane < nt * UPC) {
       const int u = (c0 + t0) * UPC + lane;
-      const Chunk ch = decode_chunk(a, streaming, b, g, u / UPP, L, nsel);
+      const Chunk ch = decode_chunk(a, streaming, b, g, u / UPP, L, nsel, sel_row, sel_cap);
       const int r0 = (u % UPP) * U;                     // first row of the unit in the page
       const int lo = max(ch.t0 - ch.row_base, r0), hi = min(ch.t1 - ch.row_base, r0 + U);
       if (ch.page >= 0 && lo < hi) {
@@ -787,15 +919,16 @@ hipError_t launch_decode(const DecodeArgs& args, hipStream_t s) {
   a.waves_per_group = waves_per_group(waves, "UBS_DECODE_WPG");
   const int64_t blocks = (waves + a.waves_per_group - 1) / a.waves_per_group;
   const dim3 block((unsigned)(64 * a.waves_per_group));
+  const size_t fused_lds = (size_t)a.waves_per_group * a.fused_k * sizeof(int32_t);
   const int G = a.Hq / a.Hkv;
   const int64_t merge_blocks = (int64_t)a.B * a.Hq;   // one work-group per (b, query head)
   const size_t merge_lds = (size_t)(((int64_t)a.max_splits * (a.D + 2) + 255) / 256 * 256 + a.max_splits) * sizeof(float);
 #define UBS_DECODE(DD, GG)                                                                            \
   if (a.D == DD && G == GG) {                                                                         \
     if (a.int4)                                                                                       \
-      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), dim3((unsigned)blocks), block, 0, s, a);     \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), dim3((unsigned)blocks), block, fused_lds, s, a); \
     else                                                                                              \
-      hipLaunchKernelGGL((decode_kernel<DD, GG, false>), dim3((unsigned)blocks), block, 0, s, a);    \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, false>), dim3((unsigned)blocks), block, fused_lds, s, a); \
     hipError_t e = hipGetLastError();                                                                 \
     if (e != hipSuccess || merge_blocks == 0) return e;                                               \
     hipLaunchKernelGGL((decode_merge_kernel<DD>), dim3((unsigned)merge_blocks), dim3(256), merge_lds, s, a); \

@@ -37,6 +37,10 @@ struct AppendArgs {
   uint16_t* v_cache;
 };
 
+// Rows a decode wave ranks itself (64 lanes x 16 keys) and the largest budget it keeps
+constexpr int kMaxFusedPages = 1024;
+constexpr int kMaxFusedK = 1024;
+
 struct SelectArgs {
   const uint16_t* q;
   const uint16_t* bounds;
@@ -48,6 +52,7 @@ struct SelectArgs {
   int32_t* selected;
   int32_t* num_selected;
   float* scores;  // workspace [B][Hkv][max_pages]
+  int score_only;  // scores only: the decode kernel ranks them (fused selection)
 };
 
 struct DecodeArgs {
@@ -68,6 +73,14 @@ struct DecodeArgs {
   float* partials;     // workspace [B][Hq][max_splits][D + 2]
   int max_splits;
   int waves_per_group;   // waves of a work-group (1, 2 or 4): set by launch_decode
+  // Selection ranked inside the kernel (fused_k > 0, the page budget k; rows of at most
+  // kMaxFusedPages pages): each dense-head wave takes its row's top k from the page scores
+  // into LDS, and split 0 of each row writes the row to sel_out [B][Hkv][k] / nsel_out
+  // [B][Hkv]. fused_k = 0: the selection comes from `selected` / `num_selected`.
+  const float* scores;   // [B][Hkv][max_pages]
+  int fused_k;
+  int32_t* sel_out;
+  int32_t* nsel_out;
   // INT4 pages (int4 != 0): codes [NP][Hkv][P][D/2], fp16 (scale, zero) [NP][Hkv][P][2]
   int int4;
   const uint8_t* k_codes;

@@ -310,6 +310,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
 #undef UBS_SCORE_DU
     if (e != hipSuccess) return e;
   }
+  if (a.score_only) return hipSuccess;
   const dim3 grid((unsigned)(a.B * a.Hkv));
   const int need = (a.max_pages + 255) / 256;
 #define UBS_TOPK(E)                                                                               \
