@@ -333,9 +333,10 @@ void decode_kernel(const DecodeArgs a) {
                                 a.nsel_out + row, split == 0)
                  : wave_topk<16>(sc, a.seq_lens + b, a.P, a.max_pages, a.fused_k, my_sel,
                                  a.sel_out + row * a.fused_k, a.nsel_out + row, split == 0);
-      // (the other lanes' entries are read below: LDS writes of one wave complete in order)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // the list is read below by other lanes than wrote it: every LDS write done
+      // (lgkmcnt(0)), and no later load moved above this point
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
     } else if (split == 0) {
       // a streaming head's row of the selection outputs: nothing selected
       for (int i = lane; i < a.fused_k; i += 64) a.sel_out[row * a.fused_k + i] = -1;
