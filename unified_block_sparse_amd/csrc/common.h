@@ -63,4 +63,45 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Exclusive prefix sum over the wave of a count v in [0, 2^BITS), and its total, from
+// BITS ballots (bit b of every lane's count) and the count of set bits in the lanes below:
+// no LDS round trip, where a shuffle scan takes six.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_small(int v, int& total) {
+  int pre = 0;
+  total = 0;
+#pragma unroll
+  for (int bit = 0; bit < BITS; ++bit) {
+    const uint64_t m = __ballot((v >> bit) & 1);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    pre += below << bit;
+    total += __popcll(m) << bit;
+  }
+  return pre;
+}
+// min and max of v over the wave: DPP row permutes (neighbours, pairs, half-row and row
+// mirrors) within each 16-lane row, then the row-pair and half-wave swaps
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, int sel) {
+  switch (sel) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);
+  }
+}
+__device__ __forceinline__ void wave_min_max_u32(uint32_t& lo, uint32_t& hi) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    lo = min(lo, dpp_u32(lo, k));
+    hi = max(hi, dpp_u32(hi, k));
+  }
+  auto a16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto b16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  lo = min(a16[0], a16[1]);
+  hi = max(b16[0], b16[1]);
+  auto a32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto b32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  lo = min(a32[0], a32[1]);
+  hi = max(b32[0], b32[1]);
+}
 }  // namespace ubs

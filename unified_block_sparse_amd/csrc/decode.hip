@@ -179,22 +179,10 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
 // Selection inside the decode kernel: the wave's row of page scores (n pages, at most
 // kMaxFusedPages) ranked as topk_kernel ranks it (the k-th largest order-preserving key by
 // a bitwise search from the first bit where the row's keys differ, ties to the lower page
-// index), with every count a sum of the wave's own ballots and every prefix sum a wave
-// scan. The kept pages go in ascending order to sel[0, k) (this wave's LDS); with `write`
+// index), with every count and every prefix sum taken from the wave's own ballots. The kept pages go in ascending order to sel[0, k) (this wave's LDS); with `write`
 // also to gsel / gnum (the caller's selection outputs). Lane t owns pages t*EPT ..
 // t*EPT + EPT - 1 (EPT = 8 or 16 from max_pages), so lane order is page order. Returns
 // the number kept, min(n, k).
-__device__ __forceinline__ int wave_scan_excl(int v, int& total) {
-  const int lane = lane_id();
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  total = __shfl(x, 63, 64);
-  return x - v;
-}
 template <int EPT>
 __device__ __forceinline__ int wave_topk(const float* __restrict__ sc, const int* __restrict__ seq_len, int P,
                                          int max_pages, int k, __attribute__((address_space(3))) int32_t* sel,
@@ -230,11 +218,7 @@ __device__ __forceinline__ int wave_topk(const float* __restrict__ sc, const int
       kmax = max(kmax, key[e]);
     }
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  wave_min_max_u32(kmin, kmax);
   const int top = kmin == kmax ? -1 : 31 - __builtin_clz(kmin ^ kmax);
   uint32_t tau = kmin == kmax ? kmax : (top == 31 ? 0u : (kmax & ~((2u << top) - 1u)));
   for (int bit = top; bit >= 0; --bit) {
@@ -252,8 +236,8 @@ __device__ __forceinline__ int wave_topk(const float* __restrict__ sc, const int
     ties += key[e] == tau;
   }
   int n_gt, tie_total, kept_total;
-  wave_scan_excl(gt, n_gt);
-  int tie_rank = wave_scan_excl(ties, tie_total);
+  wave_prefix_small<5>(gt, n_gt);
+  int tie_rank = wave_prefix_small<5>(ties, tie_total);
   const int take_ties = k - n_gt;
   uint32_t keep = 0;
   int kept = 0;
@@ -267,7 +251,7 @@ __device__ __forceinline__ int wave_topk(const float* __restrict__ sc, const int
     keep |= (uint32_t)kp << e;
     kept += kp;
   }
-  int pos = wave_scan_excl(kept, kept_total);
+  int pos = wave_prefix_small<5>(kept, kept_total);
 #pragma unroll
   for (int e = 0; e < EPT; ++e)
     if ((keep >> e) & 1u) {

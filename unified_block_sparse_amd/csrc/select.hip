@@ -133,15 +133,13 @@ void score_kernel(const uint16_t* __restrict__ q,
 
 // ----------------------------------------------------------------------------- top-k
 
+// Block-wide exclusive prefix sum of a count v in [0, 128) per thread (4 waves): the wave
+// prefix from ballots, then the four wave totals through LDS.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int& total) {
   const int lane = lane_id(), w = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) tmp[w] = x;
+  int wt;
+  const int pre = wave_prefix_small<7>(v, wt);
+  if (lane == 0) tmp[w] = wt;
   __syncthreads();
   int base = 0;
   total = 0;
@@ -152,7 +150,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int& total)
     total += t;
   }
   __syncthreads();
-  return base + x - v;
+  return base + pre;
 }
 
 // One 256-thread work-group per (b, KV head). Thread t owns pages t*EPT .. t*EPT+EPT-1,
@@ -200,11 +198,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ sco
   const int w = tid >> 6, lane = lane_id();
   // every key, and so the k-th largest, shares the bits above the first bit where the
   // smallest and the largest key differ: the search starts there
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  wave_min_max_u32(kmin, kmax);
   if (lane == 0) {
     rng[0][w] = kmin;
     rng[1][w] = kmax;
