@@ -7,6 +7,27 @@
 
 namespace ubs {
 
+// min and max of v with its partner lane l ^ m for m = 8, 16, 32: a DPP rotate by 8
+// inside each 16-lane row, or the row-pair / half-wave swap (one vector instruction each,
+// where a shuffle is an LDS round trip)
+template <int M>
+__device__ __forceinline__ void min_max_xor(float& mn, float& mx) {
+  if constexpr (M == 8) {
+    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x128, 0xF, 0xF, false)));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x128, 0xF, 0xF, false)));
+  } else if constexpr (M == 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  } else {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+}
+
 // One wave per (sequence b, page index j, dense KV head); after an append of n_new
 // tokens, one wave per (b, page holding new tokens, dense KV head), recomputing only the
 // sub-pages that received new tokens (over all their valid tokens, old and new). Lane layout: CH = D/8
@@ -78,13 +99,12 @@ __global__ __launch_bounds__(256) void bounds_kernel(const uint16_t* __restrict_
         }
       }
     }
+    // across the RG row groups (lanes CH, 2 CH, ... apart)
 #pragma unroll
-    for (int m = CH; m < 64; m <<= 1) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        mn[e] = fminf(mn[e], shfl_xor(mn[e], m));
-        mx[e] = fmaxf(mx[e], shfl_xor(mx[e], m));
-      }
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (CH <= 8) min_max_xor<8>(mn[e], mx[e]);
+      min_max_xor<16>(mn[e], mx[e]);
+      min_max_xor<32>(mn[e], mx[e]);
     }
     if (rg == 0) {
       u32x4 vmin, vmax;
