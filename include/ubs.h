@@ -271,11 +271,13 @@ int sparse_decode(const ubs_bf16_t* q, const ubs_bf16_t* k_cache, const ubs_bf16
  *   select_pages(q, bounds, ..., token_budget, selected, num_selected)
  *   sparse_decode(q, k_cache, v_cache, ..., selected, num_selected,
  *                 max_selected = token_budget / P, ...)
- * bit for bit: the same selection, ties to the lower page index, and the same
- * outputs. The work differs: for rows of at most 1,024 pages (max_pages <= 1024) and
- * token_budget / P <= 1,024, each decode wave of a dense head ranks its row's page
- * scores itself, so the separate top-k launch is skipped; longer rows run the two
- * calls' kernels as they are.
+ * The selection is the same bit for bit (ties to the lower page index); out and lse
+ * are the same attention within sparse_decode's tolerance (the key lists may be cut
+ * into splits differently, and each split rounds its weights to bf16 against its own
+ * running max). The work
+ * differs: for rows of at most 1,024 pages (max_pages <= 1024) and token_budget / P
+ * <= 1,024, each decode wave of a dense head ranks its row's page scores itself, so the
+ * separate top-k launch is skipped; longer rows run the two calls' kernels as they are.
  *
  *   q, bounds, page_table, seq_lens, head_kind, P, Lp, token_budget
  *                 as for select_pages; k_cache, v_cache, sink_tokens, local_tokens,

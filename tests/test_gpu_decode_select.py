@@ -1,15 +1,21 @@
-"""sparse_decode_select against select_pages + sparse_decode, bit for bit.
+"""sparse_decode_select against select_pages + sparse_decode.
 
 The combined call ranks the page scores inside the decode kernel when a row has at most
 1,024 pages (one wave per row, up to 16 keys a lane) and falls back to the two calls'
-kernels for longer rows; either way its selection and its outputs must equal those of the
-two separate calls (which the other tests compare with the oracle). The cases cover both
-paths, rows shorter than the budget, streaming heads, exact score ties and G = 1 .. 16.
+kernels for longer rows. Its selection must equal the two calls' bit for bit. Its outputs
+are compared with the oracle's decode on that selection, to the attention tolerance: it may
+cut the key lists into splits differently from sparse_decode, and each split rounds its
+weights to bf16 against its own running max, so the two calls' outputs agree to that
+rounding, not bit for bit. The cases cover both paths, rows shorter than the budget,
+streaming heads, exact score ties and G = 1 .. 16.
 """
 import pytest
 import torch
 
+import oracle
 import unified_block_sparse_amd as ubs
+from tests.gpu_cases import assert_attention_close, assert_lse_close
+from tests.helpers import bits
 from workloads import cases
 
 pytestmark = pytest.mark.gpu
@@ -42,10 +48,16 @@ def test_decode_select_equals_separate_calls(lens, Hq, Hkv, D, P, Lp, hk, budget
     torch.cuda.synchronize(DEV)
     assert torch.equal(num2, num), "num_selected differs"
     assert torch.equal(sel2, sel), "selected differs"
-    assert torch.equal(out2, out), "out differs"
-    assert torch.equal(lse2, lse), "lse differs"
+    # both outputs against the oracle's decode on this selection
+    sel_h, num_h = sel.cpu().tolist(), num.cpu().tolist()
+    sel_d = {(b, g): sel_h[b][g][:num_h[b][g]] for b in range(c.B) for g in range(Hkv) if hk[g] == 0}
+    ref, ref_lse = oracle.decode_ref(bits(c.q), bits(c.k_cache), bits(c.v_cache), c.page_table.cpu().numpy(), lens,
+                                     Hq, Hkv, P, hk, sel_d, sink, local, c.sm_scale)
+    for o, l, what in ((out2, lse2, "sparse_decode_select"), (out, lse, "sparse_decode")):
+        assert_attention_close(o.cpu().numpy(), ref, what + " out")
+        assert_lse_close(l.cpu().numpy(), ref_lse, what + " lse")
     # a second call on the same (reused) workspace gives the same bits
     out3, sel3, num3 = ubs.sparse_decode_select(c.q, bnd, c.k_cache, c.v_cache, c.page_table, c.seq_lens_t, hk, P,
                                                 budget, sink, local, c.sm_scale)
     torch.cuda.synchronize(DEV)
-    assert torch.equal(out3, out) and torch.equal(sel3, sel) and torch.equal(num3, num)
+    assert torch.equal(out3, out2) and torch.equal(sel3, sel) and torch.equal(num3, num)

@@ -16,7 +16,7 @@ and the steps around them in serving:
     append_kv            new tokens into the paged cache, page bounds refreshed
     quantize_kv_int4     INT4 pages of the cache (per-row 4-bit codes, fp16 scale/zero)
     sparse_decode_int4   sparse_decode over the INT4 pages
-    sparse_decode_select select_pages + sparse_decode in one call (same results)
+    sparse_decode_select select_pages + sparse_decode in one call
 
 Build the library with ``python -m unified_block_sparse_amd.build``.
 """

@@ -385,7 +385,7 @@ static int decode_impl(const char* name, bool int4, bool use_static, const ubs_b
   REQUIRE(workspace && workspace_bytes >= need, UBS_ERR_WORKSPACE_TOO_SMALL,
           "workspace of %zu bytes, need %zu", workspace_bytes, need);
   const ubs::DecodePlan pl = ubs::plan_decode(B, Hkv, dense.n, P, max_selected, sink_tokens, local_tokens, int4,
-                                              ubs::decode_wave_slots(D, Hq / Hkv, int4 != 0));
+                                              ubs::decode_wave_slots(D, Hq / Hkv, int4 != 0), fused);
   const int64_t blocks = (int64_t)B * (dense.n * pl.splits_dense + streaming.n * pl.splits_stream);
   REQUIRE(blocks < (1ll << 31), UBS_ERR_UNSUPPORTED, "grid of %lld work-groups is too large", (long long)blocks);
   ubs::DecodeArgs a{};

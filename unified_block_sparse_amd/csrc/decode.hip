@@ -793,7 +793,7 @@ int64_t decode_wave_slots(int D, int G, bool int4) {
 }
 
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4,
-                       int64_t wave_slots) {
+                       int64_t wave_slots, bool ranks_selection) {
   DecodePlan pl{};
   // key lists in units of U rows of one page (16 for bf16 pages, 32 for INT4), two or one
   // units a 32-token chunk
@@ -820,8 +820,12 @@ DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int
   // At least 4 chunks a split: a wave's fixed part (resolving its pages, writing its
   // partial, its share of the merge) costs about as much as streaming two chunks, so
   // smaller splits lose more than the extra waves gain (Llama-3-8B decode, 4 sequences:
-  // a step of 31.4 us at 2 chunks a split, 27.6 at 4, 28.8 at 5, 31.6 at 8).
-  cpw = std::max(cpw, 4);
+  // a step of 31.4 us at 2 chunks a split, 27.6 at 4, 28.8 at 5, 31.6 at 8). At least 6
+  // when the waves also rank their selection, a larger fixed part (the same step with
+  // sparse_decode_select: 25.2 us at 3, 23.9-24.0 at 4, 23.5-23.7 at 5, 23.3-23.4 at 6,
+  // 23.9-24.1 at 8). (A larger floor only lowers the split count: the workspace bound,
+  // planned at the floor of 4, still holds.)
+  cpw = std::max(cpw, ranks_selection ? 6 : 4);
   // (measurement override: UBS_DECODE_CPW sets the chunks per split; the result does not
   // depend on it beyond the order of the split merge)
   if (const char* e = getenv("UBS_DECODE_CPW")) {

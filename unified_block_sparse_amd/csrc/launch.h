@@ -175,7 +175,7 @@ int device_cu_count();
 // bandwidth). `env` names a measurement override (1, 2 or 4).
 int waves_per_group(int64_t waves, const char* env);
 DecodePlan plan_decode(int B, int Hkv, int n_dense, int P, int max_selected, int sink, int local, bool int4,
-                       int64_t wave_slots);
+                       int64_t wave_slots, bool ranks_selection = false);
 
 // Size of the library-owned scratch of sparse_decode_static (per GPU), and its device
 // address on the current device (resolved on the first call there).
