@@ -143,7 +143,8 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
   if (!streaming) {
     // (the selection entry is read before num_selected is known, so that the two loads,
-    // and the sequence length, make one round trip; every slot below max_selected exists)
+    // and the sequence length, make one round trip; every slot below sel_cap exists: the
+    // `selected` row, or the row the wave ranked into its LDS)
     const int j = c < sel_cap ? sel_row[c] : -1;
     if (c >= nsel) return ch;
     if (j < 0 || (int64_t)j * P >= L) return ch;
@@ -179,10 +180,11 @@ __device__ __forceinline__ Chunk decode_chunk(const DecodeArgs& a, bool streamin
 // Selection inside the decode kernel: the wave's row of page scores (n pages, at most
 // kMaxFusedPages) ranked as topk_kernel ranks it (the k-th largest order-preserving key by
 // a bitwise search from the first bit where the row's keys differ, ties to the lower page
-// index), with every count and every prefix sum taken from the wave's own ballots. The kept pages go in ascending order to sel[0, k) (this wave's LDS); with `write`
-// also to gsel / gnum (the caller's selection outputs). Lane t owns pages t*EPT ..
-// t*EPT + EPT - 1 (EPT = 8 or 16 from max_pages), so lane order is page order. Returns
-// the number kept, min(n, k).
+// index), with every count and every prefix sum taken from the wave's own ballots. The
+// kept pages go in ascending order to sel[0, k) (this wave's LDS); with `write` also to
+// gsel / gnum (the caller's selection outputs). Lane t owns pages t*EPT .. t*EPT + EPT - 1
+// (EPT = 8 or 16 from max_pages), so lane order is page order. Returns the number kept,
+// min(n, k).
 template <int EPT>
 __device__ __forceinline__ int wave_topk(const float* __restrict__ sc, const int* __restrict__ seq_len, int P,
                                          int max_pages, int k, __attribute__((address_space(3))) int32_t* sel,
