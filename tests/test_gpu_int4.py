@@ -88,6 +88,40 @@ def test_quantize_int4_half_integer_quotients():
     assert np.array_equal(_u16(kp), rkp) and np.array_equal(_u16(vp), rvp), "params differ"
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_quantize_int4_edge_rows(D):
+    """Rows at the edges of the format (finite values whose range / 15 fits fp16), codes
+    and params bit-exact against the oracle: a minimum below -65504 (zero = -inf, every
+    code 15) or above it (zero = +inf, every code 0), constant rows (scale 0, every code
+    0) with a finite and an infinite zero, and values in fp16's subnormal range (zero
+    rounds above the minimum, so that row's quotient is negative and clamps to 0). The
+    first eight rows hold the extreme ones; at D = 128 the next eight, ordinary and
+    subnormal rows, fill another wave of their own."""
+    P, Hkv, L = 16, 2, 16
+    gen = torch.Generator().manual_seed(61)
+    u = torch.rand((P, D), generator=gen, dtype=torch.float64)
+    z = torch.randn((P, D), generator=gen, dtype=torch.float64)
+    rows = torch.stack([
+        -70000 + 10000 * u[0], 66000 + 4000 * u[1], torch.full((D,), 70000.0), torch.full((D,), -1.5),
+        -80000 + 100 * u[4], 65600 + 10 * u[5], torch.full((D,), -66000.0), z[7],
+        1e-7 + 3e-6 * u[8], 1e-7 + 3e-6 * u[9], z[10], 3 * z[11], torch.full((D,), 2.0 ** -24),
+        1e-6 * z[13], 0.01 * z[14], z[15]])
+    cache = rows.to(torch.bfloat16).reshape(1, 1, P, D).repeat(1, Hkv, 1, 1).contiguous().to(DEV)
+    pt = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    lens = torch.tensor([L], dtype=torch.int32, device=DEV)
+    kc, vc, kp, vp = ubs.quantize_kv_int4(cache, cache, pt, lens)
+    _sync()
+    with np.errstate(over="ignore", invalid="ignore"):
+        rkq, rvq, rkp, rvp, written = oracle.quantize_cache_int4_ref(bits(cache), bits(cache), pt.cpu().numpy(),
+                                                                     [L], P)
+    assert written.all()
+    assert np.array_equal(_u8(kc), rkq) and np.array_equal(_u8(vc), rvq), "codes differ"
+    assert np.array_equal(_u16(kp), rkp) and np.array_equal(_u16(vp), rvp), "params differ"
+    # the rows mean what the docstring says (a check of the inputs)
+    codes = oracle.unpack_int4(rkq[0, 0])
+    assert (codes[0] == 15).all() and (codes[1] == 0).all() and (codes[2] == 0).all() and (codes[3] == 0).all()
+
+
 DECODE4_CASES = [
     # lens, Hq, Hkv, D, P, Lp, head_kind, budget, sink, local
     ([37, 16, 1, 50, 0, 300], 8, 2, 128, 16, 4, [0, 1], 4 * 16, 5, 20),

@@ -8,10 +8,17 @@
 // high half (k odd). K rows keep channel order (words of 8 channels); V is channel-major
 // per page (for each channel, words of 8 tokens), the operand layout of decode's P.V.
 //
-// One work-group per (sequence, page). Per KV head: D/8 lanes share a row (16 bytes
-// each), min and max by xor shuffles inside the row; K words go straight out, V codes
-// go to LDS (P * D bytes) and leave as channel-major words. A V word holding no valid
-// token is not written; the invalid tokens of a word that is written get code 0.
+// One work-group per (sequence, page). Per KV head: D/16 lanes share a row (16 channels,
+// 32 bytes each), min and max by xor shuffles inside the row; K words go straight out, V
+// codes go to LDS (P * D bytes) and leave as channel-major words. A V word holding no
+// valid token is not written; the invalid tokens of a word that is written get code 0.
+//
+// The kernel is bound by vector instructions, not bytes, so the common case spends few
+// per code: x - zero, then fma(x - zero, RN(1/scale), 1.5 * 2^23), whose low mantissa
+// bits hold the rounded quotient (ulp 1 there), clamped to [0, 15] as an integer; a
+// second fma gives the distance of the unrounded product from that integer, and a wave
+// where some lane's distance comes within 2^-17 of 1/2 redoes its codes with correctly
+// rounded division.
 #include "common.h"
 #include "launch.h"
 
@@ -22,9 +29,20 @@ __device__ __forceinline__ int code_shift(int k) { return (k & 1) ? 16 + 4 * (k 
 
 template <int D>
 __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
-  constexpr int CH = D / 8;       // lanes per row
+  constexpr int EPL = 16;         // channels per lane
+  constexpr int CH = D / EPL;     // lanes per row
   constexpr int RPP = 256 / CH;   // rows per pass
-  constexpr int UN = 4;           // passes whose loads are issued together
+  // passes a round, their loads issued together: one keeps the kernel in 63 registers,
+  // 8 waves per SIMD (2: 79 registers, 6 waves, 5% slower; 4: 103, 4 waves, 9% slower)
+  constexpr int UN = 1;
+  constexpr float kMagic = 0x1.8p23f;           // 1.5 * 2^23: sums in [2^23, 2^24) have ulp 1
+  constexpr int32_t kMagicBits = 0x4B400000;    // its bit pattern; code n is kMagicBits + n
+  // the nibble words built by shift-and-add from kMagicBits + n carry this constant
+  constexpr uint32_t kWordBias = [] {
+    uint32_t w = 0;
+    for (int k = 0; k < 8; ++k) w += (uint32_t)kMagicBits << ((k & 1) ? 16 + 4 * (k >> 1) : 4 * (k >> 1));
+    return w;
+  }();
   // V codes of one head's page, [row][channel]: P * D bytes of dynamic LDS, so that small
   // pages leave room for more work-groups per CU
   extern __shared__ __attribute__((aligned(16))) uint8_t vcodes[];
@@ -34,98 +52,132 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
   if (n <= 0) return;
   const int page = a.page_table[(int64_t)b * a.max_pages + j];
   const int c = threadIdx.x % CH;
-  for (int g = 0; g < a.Hkv; ++g) {
-    const int64_t slab = (int64_t)page * a.Hkv + g;   // (page, KV head)
-    // rows idx < n are K rows, n <= idx < 2n the V rows; UN passes' loads go out before
-    // any of them is used (the lanes of a row agree on every branch)
-    for (int idx0 = threadIdx.x / CH; idx0 < 2 * n; idx0 += UN * RPP) {
-      u32x4 wu[UN];
+  // The (KV head, round) pairs of the page in one sequence, rounds of UN passes whose
+  // loads go out before any of them is used: rows idx < n of a head are its K rows,
+  // n <= idx < 2n its V rows (the lanes of a row agree on every branch).
+  const int R = (2 * n + UN * RPP - 1) / (UN * RPP);   // rounds per head
+  const int total = a.Hkv * R;
+  const int row0 = threadIdx.x / CH;
+  auto load_round = [&](int kr, u32x4 (&buf)[UN][2]) __attribute__((always_inline)) {
+    const int g = kr / R;
+    const int64_t slab = (int64_t)page * a.Hkv + g;
+    const int base = (kr - g * R) * (UN * RPP) + row0;
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int idx = idx0 + u * RPP;
-        const int kv = idx >= n;
-        const int64_t rid = slab * a.P + (idx - kv * n);
-        wu[u] = idx < 2 * n ? ld16((kv ? a.v_cache : a.k_cache) + rid * D + c * 8) : u32x4{0, 0, 0, 0};
-      }
+    for (int u = 0; u < UN; ++u) {
+      const int idx = base + u * RPP;
+      const int kv = idx >= n;
+      const int64_t rid = slab * a.P + (idx - kv * n);
+      const uint16_t* src = (kv ? a.v_cache : a.k_cache) + rid * D + c * EPL;
+      buf[u][0] = idx < 2 * n ? ld16(src) : u32x4{0, 0, 0, 0};
+      buf[u][1] = idx < 2 * n ? ld16(src + 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto run_round = [&](int kr, const u32x4 (&wu)[UN][2]) __attribute__((always_inline)) {
+    const int g = kr / R;
+    const int64_t slab = (int64_t)page * a.Hkv + g;
+    const int base = (kr - g * R) * (UN * RPP) + row0;
 #pragma unroll
-      for (int u = 0; u < UN; ++u) {
-        const int idx = idx0 + u * RPP;
-        if (idx >= 2 * n) break;
-        const int kv = idx >= n;
-        const int row = idx - kv * n;
-        const int64_t rid = slab * a.P + row;
-        const u32x4 w = wu[u];
-        float x[8];
+    for (int u = 0; u < UN; ++u) {
+      const int idx = base + u * RPP;
+      if (idx >= 2 * n) break;
+      const int kv = idx >= n;
+      const int row = idx - kv * n;
+      const int64_t rid = slab * a.P + row;
+      float x[EPL];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          x[2 * e] = bf16_lo(w[e]);
-          x[2 * e + 1] = bf16_hi(w[e]);
+          x[8 * h + 2 * e] = bf16_lo(wu[u][h][e]);
+          x[8 * h + 2 * e + 1] = bf16_hi(wu[u][h][e]);
         }
-        float lo = x[0], hi = x[0];
+      float lo = x[0], hi = x[0];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) {
-          lo = fminf(lo, x[e]);
-          hi = fmaxf(hi, x[e]);
-        }
+      for (int e = 1; e < EPL; ++e) {
+        lo = fminf(lo, x[e]);
+        hi = fmaxf(hi, x[e]);
+      }
 #pragma unroll
-        for (int o = 1; o < CH; o <<= 1) {
-          lo = fminf(lo, shfl_xor(lo, o));
-          hi = fmaxf(hi, shfl_xor(hi, o));
-        }
-        const _Float16 s16 = (_Float16)__fdiv_rn(hi - lo, 15.0f);
-        const _Float16 z16 = (_Float16)lo;
-        const float s = (float)s16, z = (float)z16;
-        // n = rint((x - z) / s) with the division correctly rounded. The quotient by the
-        // correctly rounded reciprocal, q' = RN((x - z) RN(1/s)), is within 1.5 * 2^-23
-        // |q| of the exact one, so rint gives the same integer unless q' lies within
-        // 2^-17 of a half-integer (a bound for |q| < 16; quotients outside [-0.5, 15.5]
-        // clamp whatever their last bits). A wave with such a lane divides exactly.
-        const float rs = s == 0.f ? 0.f : __fdiv_rn(1.0f, s);
-        float q[8];
-        bool near = false;
+      for (int o = 1; o < CH; o <<= 1) {
+        lo = fminf(lo, shfl_xor(lo, o));
+        hi = fmaxf(hi, shfl_xor(hi, o));
+      }
+      const _Float16 s16 = (_Float16)__fdiv_rn(hi - lo, 15.0f);
+      const _Float16 z16 = (_Float16)lo;
+      const float s = (float)s16, z = (float)z16;
+      const float rs = s == 0.f ? 0.f : __fdiv_rn(1.0f, s);
+      // Common case. With p = RN(x - z) RN(1/s) (exact inside the fma), t = RN(p + kMagic)
+      // is kMagic + rint(p) for |p| < 2^22 and far = |p - rint(p)| to within 2^-25. p is
+      // within 2^-23 |q| of the exact quotient q (two roundings), under 2^-19 for q in
+      // [-1/2, 31/2], the only range where the code is not a clamp bound; so when far
+      // stays 2^-17 below 1/2, q rounds to the same integer as p. Outside that range the
+      // clamp gives 0 or 15 for q and p alike (also when |p| >= 2^22: far then exceeds
+      // the bound or the bits clamp). s == 0 gives rs = 0, p = 0, code 0 as required; an
+      // infinite zero (|min| past the fp16 range) takes the exact path.
+      int32_t r[EPL];
+      float far = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          q[e] = (x[e] - z) * rs;
-          near |= fabsf(q[e] - floorf(q[e]) - 0.5f) < 0x1p-17f;
-        }
-        if (__ballot(near)) {
+      for (int e = 0; e < EPL; ++e) {
+        const float d = x[e] - z;
+        const float t = fmaf(d, rs, kMagic);
+        far = fmaxf(far, fabsf(fmaf(d, rs, -(t - kMagic))));
+        r[e] = min(max((int32_t)__float_as_uint(t), kMagicBits), kMagicBits + 15);
+      }
+      if (__ballot(far > 0.5f - 0x1p-17f || !__builtin_isfinite(z))) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[e] = s == 0.f ? 0.f : __fdiv_rn(x[e] - z, s);
-        }
-        uint32_t code[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          code[e] = (uint32_t)(s == 0.f ? 0.f : fminf(fmaxf(__builtin_rintf(q[e]), 0.f), 15.f));
-        if (kv == 0) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) word |= code[e] << code_shift(e);
-          *reinterpret_cast<uint32_t*>(a.k_codes + rid * (D / 2) + c * 4) = word;
-        } else {
-          *reinterpret_cast<uint32_t*>(&vcodes[row * D + c * 8]) = code[0] | code[1] << 8 | code[2] << 16 | code[3] << 24;
-          *reinterpret_cast<uint32_t*>(&vcodes[row * D + c * 8 + 4]) = code[4] | code[5] << 8 | code[6] << 16 | code[7] << 24;
-        }
-        if (c == 0) {
-          uint16_t* params = kv ? a.v_params : a.k_params;
-          *reinterpret_cast<uint32_t*>(params + rid * 2) =
-              (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+        for (int e = 0; e < EPL; ++e) {
+          const float q = s == 0.f ? 0.f : __fdiv_rn(x[e] - z, s);
+          r[e] = kMagicBits + (int32_t)(s == 0.f ? 0.f : fminf(fmaxf(__builtin_rintf(q), 0.f), 15.f));
         }
       }
-    }
-    __syncthreads();
-    // V words: channel ch, tokens 8r .. 8r+7 (code 0 past the valid rows)
-    const int ngr = (n + 7) / 8;
-    for (int idx = threadIdx.x; idx < D * ngr; idx += 256) {
-      const int ch = idx / ngr, r = idx % ngr;
-      uint32_t word = 0;
+      if (kv == 0) {
+        uint32_t w[2];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int t = 8 * r + k;
-        word |= (t < n ? (uint32_t)vcodes[t * D + ch] : 0u) << code_shift(k);
+        for (int h = 0; h < 2; ++h) {
+          uint32_t acc = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc += (uint32_t)r[8 * h + k] << code_shift(k);
+          w[h] = acc - kWordBias;
+        }
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + rid * (D / 2) + c * (EPL / 2));
+        dst[0] = w[0];
+        dst[1] = w[1];
+      } else {
+        // the low byte of kMagicBits + n is n
+        u32x4 cb;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          cb[m] = __builtin_amdgcn_perm((uint32_t)r[4 * m + 1], (uint32_t)r[4 * m], 0x0c0c0400u) |
+                  __builtin_amdgcn_perm((uint32_t)r[4 * m + 3], (uint32_t)r[4 * m + 2], 0x04000c0cu);
+        *reinterpret_cast<u32x4*>(&vcodes[row * D + c * EPL]) = cb;
       }
-      *reinterpret_cast<uint32_t*>(a.v_codes + (slab * D + ch) * (a.P / 2) + r * 4) = word;
+      if (c == 0) {
+        uint16_t* params = kv ? a.v_params : a.k_params;
+        *reinterpret_cast<uint32_t*>(params + rid * 2) =
+            (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+      }
     }
-    __syncthreads();
+    if (kr - g * R == R - 1) {   // the head's last round: its V words
+      __syncthreads();
+      // V words: channel ch, tokens 8r .. 8r+7 (code 0 past the valid rows)
+      const int ngr = (n + 7) / 8;
+      for (int idx = threadIdx.x; idx < D * ngr; idx += 256) {
+        const int ch = idx / ngr, r = idx % ngr;
+        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int t = 8 * r + k;
+          word |= (t < n ? (uint32_t)vcodes[t * D + ch] : 0u) << code_shift(k);
+        }
+        *reinterpret_cast<uint32_t*>(a.v_codes + (slab * D + ch) * (a.P / 2) + r * 4) = word;
+      }
+      __syncthreads();
+    }
+  };
+  for (int k = 0; k < total; ++k) {
+    u32x4 buf[UN][2];
+    load_round(k, buf);
+    run_round(k, buf);
   }
 }
 
