@@ -158,18 +158,37 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
       }
     }
     if (kr - g * R == R - 1) {   // the head's last round: its V words
+      const int ngr = (n + 7) / 8;   // words of 8 tokens a channel
+      // rows n .. 8 ngr - 1 of the last word hold code 0
+      for (int i = threadIdx.x; i < (8 * ngr - n) * (D / 16); i += 256)
+        *reinterpret_cast<u32x4*>(&vcodes[n * D + i * 16]) = u32x4{0, 0, 0, 0};
       __syncthreads();
-      // V words: channel ch, tokens 8r .. 8r+7 (code 0 past the valid rows)
-      const int ngr = (n + 7) / 8;
-      for (int idx = threadIdx.x; idx < D * ngr; idx += 256) {
-        const int ch = idx / ngr, r = idx % ngr;
-        uint32_t word = 0;
+      // One task per 4 channels and word: the 8 tokens' codes of channels 4q .. 4q+3 as 8
+      // LDS words (byte i = channel 4q + i), regrouped by byte permutes into the 4
+      // channels' words (n0|n2<<4, n4|n6<<4, n1|n3<<4, n5|n7<<4).
+      constexpr int NQ = D / 4;
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(vcodes);
+      const int q = threadIdx.x % NQ;
+      for (int r = threadIdx.x / NQ; r < ngr; r += 256 / NQ) {
+        uint32_t w8[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int t = 8 * r + k;
-          word |= (t < n ? (uint32_t)vcodes[t * D + ch] : 0u) << code_shift(k);
-        }
-        *reinterpret_cast<uint32_t*>(a.v_codes + (slab * D + ch) * (a.P / 2) + r * 4) = word;
+        for (int k = 0; k < 8; ++k) w8[k] = vw[(8 * r + k) * NQ + q];
+        // [w_a.b0, w_b.b0, w_a.b1, w_b.b1] and [w_a.b2, w_b.b2, w_a.b3, w_b.b3]
+        auto lo_pair = [](uint32_t wb, uint32_t wa) { return __builtin_amdgcn_perm(wb, wa, 0x05010400u); };
+        auto hi_pair = [](uint32_t wb, uint32_t wa) { return __builtin_amdgcn_perm(wb, wa, 0x07030602u); };
+        const uint32_t p04 = lo_pair(w8[4], w8[0]), q04 = hi_pair(w8[4], w8[0]);
+        const uint32_t p15 = lo_pair(w8[5], w8[1]), q15 = hi_pair(w8[5], w8[1]);
+        const uint32_t p26 = lo_pair(w8[6], w8[2]), q26 = hi_pair(w8[6], w8[2]);
+        const uint32_t p37 = lo_pair(w8[7], w8[3]), q37 = hi_pair(w8[7], w8[3]);
+        // channel i: A = bytes (n0, n4, n1, n5), B = bytes (n2, n6, n3, n7), word = A | B << 4
+        uint32_t word[4];
+        word[0] = __builtin_amdgcn_perm(p15, p04, 0x05040100u) | __builtin_amdgcn_perm(p37, p26, 0x05040100u) << 4;
+        word[1] = __builtin_amdgcn_perm(p15, p04, 0x07060302u) | __builtin_amdgcn_perm(p37, p26, 0x07060302u) << 4;
+        word[2] = __builtin_amdgcn_perm(q15, q04, 0x05040100u) | __builtin_amdgcn_perm(q37, q26, 0x05040100u) << 4;
+        word[3] = __builtin_amdgcn_perm(q15, q04, 0x07060302u) | __builtin_amdgcn_perm(q37, q26, 0x07060302u) << 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint32_t*>(a.v_codes + (slab * D + 4 * q + i) * (a.P / 2) + r * 4) = word[i];
       }
       __syncthreads();
     }
