@@ -31,10 +31,7 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
   constexpr int EPL = 16;         // channels per lane
   constexpr int CH = D / EPL;     // lanes per row
-  constexpr int RPP = 256 / CH;   // rows per pass
-  // passes a round, their loads issued together: one keeps the kernel in 63 registers,
-  // 8 waves per SIMD (2: 79 registers, 6 waves, 5% slower; 4: 103, 4 waves, 9% slower)
-  constexpr int UN = 1;
+  constexpr int RPP = 256 / CH;   // rows per round
   constexpr float kMagic = 0x1.8p23f;           // 1.5 * 2^23: sums in [2^23, 2^24) have ulp 1
   constexpr int32_t kMagicBits = 0x4B400000;    // its bit pattern; code n is kMagicBits + n
   // the nibble words built by shift-and-add from kMagicBits + n carry this constant
@@ -52,45 +49,32 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
   if (n <= 0) return;
   const int page = a.page_table[(int64_t)b * a.max_pages + j];
   const int c = threadIdx.x % CH;
-  // The (KV head, round) pairs of the page in one sequence, rounds of UN passes whose
-  // loads go out before any of them is used: rows idx < n of a head are its K rows,
-  // n <= idx < 2n its V rows (the lanes of a row agree on every branch).
-  const int R = (2 * n + UN * RPP - 1) / (UN * RPP);   // rounds per head
-  const int total = a.Hkv * R;
   const int row0 = threadIdx.x / CH;
-  auto load_round = [&](int kr, u32x4 (&buf)[UN][2]) __attribute__((always_inline)) {
-    const int g = kr / R;
-    const int64_t slab = (int64_t)page * a.Hkv + g;
-    const int base = (kr - g * R) * (UN * RPP) + row0;
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int idx = base + u * RPP;
-      const int kv = idx >= n;
-      const int64_t rid = slab * a.P + (idx - kv * n);
-      const uint16_t* src = (kv ? a.v_cache : a.k_cache) + rid * D + c * EPL;
-      buf[u][0] = idx < 2 * n ? ld16(src) : u32x4{0, 0, 0, 0};
-      buf[u][1] = idx < 2 * n ? ld16(src + 8) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto run_round = [&](int kr, const u32x4 (&wu)[UN][2]) __attribute__((always_inline)) {
-    const int g = kr / R;
-    const int64_t slab = (int64_t)page * a.Hkv + g;
-    const int base = (kr - g * R) * (UN * RPP) + row0;
-#pragma unroll
-    for (int u = 0; u < UN; ++u) {
-      const int idx = base + u * RPP;
-      if (idx >= 2 * n) break;
-      const int kv = idx >= n;
-      const int row = idx - kv * n;
-      const int64_t rid = slab * a.P + row;
+  // Rounds of RPP rows, one row a lane group: per KV head RK rounds of K rows, then RK of
+  // V rows, so that a round's tensor and (page, head) base are uniform and lanes address
+  // with 32-bit offsets. One round's loads at a time keeps the kernel at 7 waves per SIMD
+  // (two rounds' loads in flight: 79 registers, 6 waves, 5% slower; four: 4 waves, 9%).
+  const int RK = (n + RPP - 1) / RPP;
+  const int R = 2 * RK;
+  const int total = a.Hkv * R;
+  for (int kr = 0; kr < total; ++kr) {
+    const int g = kr / R, h = kr - g * R;
+    const bool kv = h >= RK;
+    const int row = (kv ? h - RK : h) * RPP + row0;
+    const int64_t slab = (int64_t)page * a.Hkv + g;   // (page, KV head)
+    const int64_t first = slab * a.P;                 // its first row
+    if (row < n) {   // the lanes of a row agree on every branch
+      const char* src = reinterpret_cast<const char*>((kv ? a.v_cache : a.k_cache) + first * D);
+      const uint32_t off = (uint32_t)(row * D + c * EPL) * 2u;   // bytes
+      const u32x4 w0 = ld16(src + off), w1 = ld16(src + off + 16);
       float x[EPL];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[8 * h + 2 * e] = bf16_lo(wu[u][h][e]);
-          x[8 * h + 2 * e + 1] = bf16_hi(wu[u][h][e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_lo(w0[e]);
+        x[2 * e + 1] = bf16_hi(w0[e]);
+        x[8 + 2 * e] = bf16_lo(w1[e]);
+        x[9 + 2 * e] = bf16_hi(w1[e]);
+      }
       float lo = x[0], hi = x[0];
 #pragma unroll
       for (int e = 1; e < EPL; ++e) {
@@ -113,7 +97,12 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
       // stays 2^-17 below 1/2, q rounds to the same integer as p. Outside that range the
       // clamp gives 0 or 15 for q and p alike (also when |p| >= 2^22: far then exceeds
       // the bound or the bits clamp). s == 0 gives rs = 0, p = 0, code 0 as required; an
-      // infinite zero (|min| past the fp16 range) takes the exact path.
+      // infinite zero (|min| past the fp16 range) takes the exact path. t grows with x
+      // (rs >= 0), so when the row's min and max land in [0, 15] every code does and the
+      // wave skips the clamp (the usual case: zero = min exactly for bf16 values in
+      // fp16's normal range, and max rounds to 15).
+      const bool in_range = (int32_t)__float_as_uint(fmaf(lo - z, rs, kMagic)) >= kMagicBits &&
+                            (int32_t)__float_as_uint(fmaf(hi - z, rs, kMagic)) <= kMagicBits + 15;
       int32_t r[EPL];
       float far = 0.f;
 #pragma unroll
@@ -121,7 +110,7 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
         const float d = x[e] - z;
         const float t = fmaf(d, rs, kMagic);
         far = fmaxf(far, fabsf(fmaf(d, rs, -(t - kMagic))));
-        r[e] = min(max((int32_t)__float_as_uint(t), kMagicBits), kMagicBits + 15);
+        r[e] = (int32_t)__float_as_uint(t);
       }
       if (__ballot(far > 0.5f - 0x1p-17f || !__builtin_isfinite(z))) {
 #pragma unroll
@@ -129,17 +118,20 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
           const float q = s == 0.f ? 0.f : __fdiv_rn(x[e] - z, s);
           r[e] = kMagicBits + (int32_t)(s == 0.f ? 0.f : fminf(fmaxf(__builtin_rintf(q), 0.f), 15.f));
         }
+      } else if (__ballot(!in_range)) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) r[e] = min(max(r[e], kMagicBits), kMagicBits + 15);
       }
-      if (kv == 0) {
+      if (!kv) {
         uint32_t w[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int hh = 0; hh < 2; ++hh) {
           uint32_t acc = 0;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc += (uint32_t)r[8 * h + k] << code_shift(k);
-          w[h] = acc - kWordBias;
+          for (int k = 0; k < 8; ++k) acc += (uint32_t)r[8 * hh + k] << code_shift(k);
+          w[hh] = acc - kWordBias;
         }
-        uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + rid * (D / 2) + c * (EPL / 2));
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + first * (D / 2) + (uint32_t)(row * (D / 2) + c * (EPL / 2)));
         dst[0] = w[0];
         dst[1] = w[1];
       } else {
@@ -152,12 +144,12 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
         *reinterpret_cast<u32x4*>(&vcodes[row * D + c * EPL]) = cb;
       }
       if (c == 0) {
-        uint16_t* params = kv ? a.v_params : a.k_params;
-        *reinterpret_cast<uint32_t*>(params + rid * 2) =
+        char* params = reinterpret_cast<char*>((kv ? a.v_params : a.k_params) + first * 2);
+        *reinterpret_cast<uint32_t*>(params + (uint32_t)row * 4u) =
             (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
       }
     }
-    if (kr - g * R == R - 1) {   // the head's last round: its V words
+    if (h == R - 1) {   // the head's last round: its V words
       const int ngr = (n + 7) / 8;   // words of 8 tokens a channel
       // rows n .. 8 ngr - 1 of the last word hold code 0
       for (int i = threadIdx.x; i < (8 * ngr - n) * (D / 16); i += 256)
@@ -192,11 +184,6 @@ __global__ __launch_bounds__(256) void quant_kernel(const QuantArgs a) {
       }
       __syncthreads();
     }
-  };
-  for (int k = 0; k < total; ++k) {
-    u32x4 buf[UN][2];
-    load_round(k, buf);
-    run_round(k, buf);
   }
 }
 
