@@ -573,6 +573,22 @@ def ragged_decode_step(steps: int, warmup: int, cpu: bool = False):
            "selection_reused_4_steps": {"ms_per_step": round(t_r * 1e3, 4), "bytes_per_step": int(b_r),
                                         "gbps": round(b_r / t_r / 1e9, 1),
                                         "frac": round(b_r / t_r / 1e9 / PEAK_HBM_GBPS, 4)}}
+    # build_page_bounds over the whole cache (once per filled page in serving; timed here
+    # as its own pass: 19.3 GB of K/V, far beyond the Infinity Cache)
+    b_bounds, _, _ = decode_bytes(r, sel_pages)
+    n_b = max(2, steps // 4)
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(n_b + 1)]
+    for i in range(n_b):
+        eb[i].record(stream)
+        ubs.build_page_bounds(r.k_cache, r.page_table, r.seq_lens_t, r.head_kind, r.Lp, bounds=bnd)
+    eb[n_b].record(stream)
+    torch.cuda.synchronize(dev)
+    tb = sorted(eb[i].elapsed_time(eb[i + 1]) * 1e-3 for i in range(n_b))
+    t_b = tb[len(tb) // 2]
+    res["build_page_bounds"] = {"ms": round(t_b * 1e3, 4), "bytes": int(b_bounds),
+                                "gbps": round(b_bounds / t_b / 1e9, 1),
+                                "frac": round(b_bounds / t_b / 1e9 / PEAK_HBM_GBPS, 4),
+                                "note": f"median of {n_b} calls"}
     res["int4"] = ragged_int4(r, sel, num, sel_pages, b_select, op_select, steps, warmup)
     if cpu:
         # the oracle's whole step (bounds, selection, decode) on 16 seeded sequences
