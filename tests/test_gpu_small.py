@@ -30,6 +30,14 @@ BOUNDS_CASES = [
     ([1000, 77], 32, 32, 64, [0, 1]),
     ([129], 64, 4, 128, [1, 0]),
     ([70, 3], 64, 1, 128, [0]),
+    # the compile-time sub-page sizes (Lp = P, Lp = 16) at every P and both D, and
+    # sub-pages smaller than a D = 64 row group (two rows per load)
+    ([300, 129], 128, 16, 128, [0, 1]),
+    ([130, 64], 128, 128, 64, [0]),
+    ([45, 90], 32, 16, 128, [0]),
+    ([16, 17], 16, 16, 64, [1, 0]),
+    ([33, 64], 64, 2, 64, [0, 1]),
+    ([20, 5], 16, 1, 64, [0]),
 ]
 
 
