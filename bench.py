@@ -235,14 +235,19 @@ def _host_bits(t):
 
 
 def oracle_prefill_sample(c, rows_per_head: int, seed: int = 11):
-    """The fp64 oracle on `rows_per_head` seeded query rows of every head of prefill case c.
+    """The fp64 oracle on `rows_per_head` query rows of every head of prefill case c: rows 0,
+    T-1, T and L-1 (the first tile's edges and the last row), the others seeded.
     Returns (seconds for the sample, the oracle's fixed per-call part (K/V gather and
     decode), seconds extrapolated to all L rows)."""
     import numpy as np
     import torch
     import oracle
+    # the rows at the first tile's edges and the last row, then seeded others
+    fixed = sorted({r for r in (0, c.T - 1, c.T, c.L - 1) if 0 <= r < c.L})[:rows_per_head]
+    rest = np.setdiff1d(np.arange(c.L), fixed)
     rng = np.random.default_rng(seed)
-    rows = sorted(rng.choice(c.L, size=min(rows_per_head, c.L), replace=False).tolist())
+    extra = rng.choice(rest, size=min(rows_per_head - len(fixed), len(rest)), replace=False).tolist()
+    rows = sorted(fixed + [int(x) for x in extra])
     q_host = np.zeros(tuple(c.q.shape), dtype=np.uint16)
     q_host[rows] = _host_bits(c.q[torch.tensor(rows, device=c.q.device)])
     kb, vb = _host_bits(c.k_cache), _host_bits(c.v_cache)
@@ -256,6 +261,13 @@ def oracle_prefill_sample(c, rows_per_head: int, seed: int = 11):
                        c.local_tiles, c.sm_scale, rows=rows)
     t = time.perf_counter() - t0
     return t, t_fixed, t_fixed + max(t - t_fixed, 0.0) * (c.L / len(rows)), len(rows)
+
+
+def _host_ram_bytes() -> int:
+    try:
+        return os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES")
+    except (ValueError, OSError, AttributeError):
+        return 0
 
 
 def oracle_decode_sample(d, batches):
@@ -291,7 +303,7 @@ def cpu_baseline(c, d, rows_per_head: int, ideal_s: float, extra: dict):
     step_s = pf_full + t_dec
     per_config = {
         "prefill_llama8b": {"rows_per_s": round(n_rows * c.Hq / max(t_pf - t_fixed, 1e-9), 1),
-                            "sample": f"{n_rows} seeded rows x {c.Hq} heads, {t_pf:.2f} s",
+                            "sample": f"{n_rows} rows (0, T-1, T, L-1, the rest seeded) x {c.Hq} heads, {t_pf:.2f} s",
                             "full_config_s_extrapolated": round(pf_full, 1)},
         "decode_llama8b": {"steps_per_s": round(1.0 / t_dec, 3),
                            "sample": f"all {d.B} sequences (bounds, selection, decode), {t_dec:.2f} s"},
@@ -316,7 +328,7 @@ def cpu_baseline(c, d, rows_per_head: int, ideal_s: float, extra: dict):
         "unit": "% of MI355X roofline",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: {c.name} {n_rows} seeded rows x {c.Hq} heads "
+        "sample": (f"fp64 NumPy oracle: {c.name} {n_rows} rows (0, T-1, T, L-1, the rest seeded) x {c.Hq} heads "
                    f"({t_pf:.2f} s incl. {t_fixed:.2f} s K/V gather; per-row part extrapolated "
                    f"x{c.L / n_rows:.1f} to all {c.L} rows) + {d.name} "
                    f"bounds/selection/decode of all {d.B} sequences ({t_dec:.2f} s); "
@@ -591,16 +603,23 @@ def ragged_decode_step(steps: int, warmup: int, cpu: bool = False):
                                 "note": f"median of {n_b} calls"}
     res["int4"] = ragged_int4(r, sel, num, sel_pages, b_select, op_select, steps, warmup)
     if cpu:
-        # the oracle's whole step (bounds, selection, decode) on 16 seeded sequences
+        # the oracle's whole step (bounds, selection, decode): every sequence when the host
+        # has 48 GB or more, else 16 seeded ones (extrapolated by tokens)
         import numpy as np
-        batches = sorted(np.random.default_rng(13).choice(r.B, size=16, replace=False).tolist())
+        ram = _host_ram_bytes()
+        if ram >= 48 * 2**30:
+            batches = list(range(r.B))
+        else:
+            batches = sorted(np.random.default_rng(13).choice(r.B, size=16, replace=False).tolist())
         t = oracle_decode_sample(r, batches)
+        scale = sum(r.seq_lens) / sum(r.seq_lens[b] for b in batches)
+        what = (f"all {r.B} sequences" if len(batches) == r.B else
+                f"16 seeded sequences of {r.B} ({sum(r.seq_lens[b] for b in batches)} tokens)")
         res["_oracle"] = {
-                          "sample": f"16 seeded sequences of {r.B} ({sum(r.seq_lens[b] for b in batches)} "
-                                    f"tokens), {t:.2f} s; the step over all {r.B} extrapolated by tokens x "
-                                    f"{sum(r.seq_lens) / sum(r.seq_lens[b] for b in batches):.2f}",
-                          "step_s_extrapolated": round(t * sum(r.seq_lens) / sum(r.seq_lens[b] for b in batches),
-                                                       2)}
+                          "sample": f"{what}, {t:.2f} s (host RAM {ram / 2**30:.0f} GiB)" +
+                                    ("" if len(batches) == r.B else
+                                     f"; the step over all {r.B} extrapolated by tokens x {scale:.2f}"),
+                          "step_s_extrapolated" if len(batches) < r.B else "step_s": round(t * scale, 2)}
     del r, bnd
     torch.cuda.empty_cache()
     return res
@@ -713,7 +732,7 @@ def prefill_leg(c, steps: int, warmup: int, cpu_rows: int = 0):
     if cpu_rows:
         t_s, t_fixed, full, n = oracle_prefill_sample(c, cpu_rows, seed=14)
         res["_oracle"] = {"rows_per_s": round(n * c.Hq / max(t_s - t_fixed, 1e-9), 1),
-                          "sample": f"{n} seeded rows x {c.Hq} heads, {t_s:.2f} s incl. {t_fixed:.2f} s "
+                          "sample": f"{n} rows (0, T-1, T, L-1, the rest seeded) x {c.Hq} heads, {t_s:.2f} s incl. {t_fixed:.2f} s "
                                     f"K/V gather; all {c.L} rows extrapolated",
                           "full_config_s_extrapolated": round(full, 1)}
     return res
@@ -906,7 +925,7 @@ def main():
                                             "note": "select_pages + sparse_decode, 64 sequences"}
     if "extreme" in legs:
         c5 = cases.prefill_extreme(dev)
-        r = prefill_leg(c5, max(2, args.steps // 4), min(args.warmup, 1), cpu_rows=8 if cpu else 0)
+        r = prefill_leg(c5, max(2, args.steps // 4), min(args.warmup, 1), cpu_rows=32 if cpu else 0)
         del c5
         torch.cuda.empty_cache()
         if "_oracle" in r:
