@@ -114,6 +114,32 @@ def test_select_exact_ties_break_to_lower_index(lens, P, Lp, budget):
     assert swaps == 0
 
 
+def test_score_work_group_orders_give_the_same_scores(monkeypatch):
+    """The page scores (the workspace select_pages leaves behind) and the selection do not
+    depend on the order in which the scoring work-groups cover the (sequence, page chunk,
+    dense head) items: the measurement override's row order equals the default."""
+    lib = ubs.load()
+    c = cases.make_decode("o", [9000, 333, 4100, 64], 16, 4, 128, 64, 16, [0, 1, 0, 0], 12 * 64, 4, 8, 34, DEV,
+                          planted=True)
+    bnd = ubs.build_page_bounds(c.k_cache, c.page_table, c.seq_lens_t, c.head_kind, c.Lp)
+    n = lib.ubs_select_workspace_size(c.B, c.page_table.shape[1], c.Hkv)
+    got = []
+    for order in ("1", "0"):
+        monkeypatch.setenv("UBS_SCORE_ORDER", order)
+        ws = torch.full((n,), 0x7f, dtype=torch.uint8, device=DEV)
+        sel, num = ubs.select_pages(c.q, bnd, c.page_table, c.seq_lens_t, c.head_kind, c.P, c.token_budget,
+                                    workspace=ws)
+        _sync()
+        # the scores of every valid page of every dense row (entries past a row are not written)
+        sc = ws[:c.B * c.Hkv * c.page_table.shape[1] * 4].view(torch.float32).view(c.B, c.Hkv, -1).cpu()
+        rows = {(b, g): sc[b, g, :(L + c.P - 1) // c.P].clone()
+                for b, L in enumerate(c.seq_lens) for g in range(c.Hkv) if not c.head_kind[g]}
+        got.append((sel.cpu(), num.cpu(), rows))
+    assert torch.equal(got[0][0], got[1][0]) and torch.equal(got[0][1], got[1][1])
+    for key in got[0][2]:
+        assert torch.equal(got[0][2][key].view(torch.int32), got[1][2][key].view(torch.int32)), key
+
+
 # ----------------------------------------------------------------------------- decode
 
 DECODE_CASES = [
