@@ -21,13 +21,13 @@ The same line carries, outside `value`, one roofline fraction per named workload
 (`per_config`): prefill_tiny, the decode_llama8b step replayed as a HIP graph over 24
 cache instances, prefill_llama8b, the decode_ragged step (64 sequences of 16K-128K tokens)
 and prefill_extreme (262,144 tokens, Llama-3-70B heads), plus further legs (mask
-estimation, batched prefill, reused selection, INT4 pages) and the fp64 oracle timed on
-the host cores (`cpu_baseline`).
+estimation, batched and chunked prefill, KV append, reused selection, INT4 pages) and the
+fp64 oracle timed on the host cores (`cpu_baseline`).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--legs LIST] [--no-cpu-baseline]
 
 --legs selects what runs (default: all): step, tiny, graph, ragged, extreme, mask,
-varlen, cpu. Without `step` the line holds only the selected legs' results; profiling
+varlen, chunk, append, peaks, cpu. Without `step` the line holds only the selected legs' results; profiling
 runs use this to trace one workload at a time.
 """
 from __future__ import annotations
@@ -46,7 +46,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU, dense
 PEAK_HBM_GBPS = 8000.0
 METRIC = "sparse prefill TFLOP/s (kept tiles) + decode KV GB/s, as % of MI355X roofline"
-LEGS = ("step", "tiny", "graph", "ragged", "extreme", "mask", "varlen", "peaks", "cpu")
+LEGS = ("step", "tiny", "graph", "ragged", "extreme", "mask", "varlen", "chunk", "append", "peaks", "cpu")
 # The pages' own figures for this method, quoted as context (relative speedups, no hardware
 # or absolute numbers given): LServe index page, Abstract.
 PAGES_CONTEXT = ("LServe (arXiv 2502.14866) abstract: up to 2.9x prefill and 1.3-2.1x decode speedup over "
@@ -169,19 +169,20 @@ def measured_peaks():
 
 # ----------------------------------------------------------------------------- work accounting
 
-def kept_tile_count(c) -> int:
-    """Kept (query head, query tile, KV tile) triples: the tiles the kernel computes."""
+def kept_tile_count(c, first_tile: int = 0) -> int:
+    """Kept (query head, query tile, KV tile) triples of query tiles first_tile .. nT-1: the
+    tiles the kernel computes."""
     import torch
     nT = c.nT
     total = 0
-    i = torch.arange(nT)
+    i = torch.arange(first_tile, nT)
     lam = (torch.clamp(i + 1, max=c.sink_tiles) +
            torch.clamp(torch.clamp(i + 1 - c.sink_tiles, min=0), max=c.local_tiles)).sum().item()
     for h in range(c.Hq):
         if c.head_kind[h // c.G]:
             total += int(lam)
         else:
-            total += int(torch.tril(c.block_mask[h] != 0).sum().item())
+            total += int(torch.tril(c.block_mask[h] != 0)[first_tile:].sum().item())
     return total
 
 
@@ -738,6 +739,104 @@ def prefill_leg(c, steps: int, warmup: int, cpu_rows: int = 0):
     return res
 
 
+# ----------------------------------------------------------------------------- serving-loop legs
+
+def chunk_prefill(c, steps: int, warmup: int):
+    """sparse_prefill_chunk: the last 8,192 query rows (64 query tiles) of prefill_llama8b
+    over its whole 65,536-token cache, the last chunk of a chunked prefill. Kept-tile
+    TFLOP/s of the chunk's query tiles against the bf16 MFMA peak."""
+    import torch
+    import unified_block_sparse_amd as ubs
+    q0 = c.L - 8192
+    i0 = q0 // c.T
+    kept = kept_tile_count(c, first_tile=i0)
+    flops = prefill_flops(c, kept)
+    q = c.q[q0:].contiguous()
+    mask = c.block_mask[:, i0:, :].contiguous()
+    out = torch.empty((c.L - q0, c.Hq, c.D), dtype=torch.float32, device=c.q.device)
+    f = lambda: ubs.sparse_prefill_chunk(q, c.k_cache, c.v_cache, c.page_table, c.L, q0, c.head_kind, mask,
+                                         c.sink_tiles, c.local_tiles, c.T, c.sm_scale, out=out)
+    t, t_min, t_med = time_calls(f, steps, warmup, torch.cuda.current_stream(c.q.device))
+    del q, mask, out
+    return {"workload": f"{c.name}: query rows {q0}..{c.L - 1} ({c.nT - i0} query tiles) over all {c.L} tokens",
+            "calls": steps, "ms": round(t * 1e3, 4), "ms_median": round(t_med * 1e3, 4),
+            "kept_tiles": kept, "tflop": round(flops / 1e12, 4), "tflops": round(flops / t / 1e12, 2),
+            "frac": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def append_leg(steps: int, warmup: int):
+    """append_kv in the serving loop, with the dense heads' page bounds refreshed: one decoded
+    token for each of 64 sequences of 2K-8K tokens (Llama-3-8B KV heads, P = 64, Lp = 16),
+    and a 4,096-token prefill chunk for each of 4 sequences (P = Lp = 64). Every call writes
+    the same tokens at the same positions (the lengths do not change), so repeated calls
+    time one append. The calls are captured in a HIP graph and replayed (the binding's
+    host work per call is longer than the GPU work of these appends); the chunk appends
+    cycle over four cache instances, so that a call does not find the previous one's
+    data in the 256 MB Infinity Cache. Algorithmic bytes: the new K and V rows read and
+    written, the K rows of the dense heads' sub-pages holding a new token read (their
+    valid rows, old and new) and those sub-pages' bounds written."""
+    import numpy as np
+    import torch
+    import unified_block_sparse_amd as ubs
+    from workloads import cases, gen
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    kind = [0, 0, 0, 0, 1, 1, 1, 1]
+    rng = np.random.default_rng(21)
+    res = {}
+    for name, lens, n_new, Lp, R in (("decode_token", rng.integers(2048, 8193, size=64).tolist(), 1, 16, 1),
+                                     ("prefill_chunk", [32768] * 4, 4096, 64, 4)):
+        inst = []
+        for r in range(R):
+            d = cases.make_decode(f"append_{name}", lens, 32, 8, 128, 64, Lp, kind, 4096, 128, 512,
+                                  1700 + n_new + r, dev)
+            old_t = torch.tensor([L - n_new for L in lens], dtype=torch.int32, device=dev)
+            k_new = gen.normal_bf16((d.B, n_new, d.Hkv, d.D), 1800 + n_new + r, 1, dev)
+            v_new = gen.normal_bf16((d.B, n_new, d.Hkv, d.D), 1800 + n_new + r, 2, dev)
+            bnd = ubs.build_page_bounds(d.k_cache, d.page_table, old_t, kind, Lp)
+            inst.append((d, old_t, k_new, v_new, bnd))
+
+        def run_all(reps):
+            for _ in range(reps):
+                for d, old_t, k_new, v_new, bnd in inst:
+                    ubs.append_kv(k_new, v_new, d.page_table, old_t, kind, d.k_cache, d.v_cache, bounds=bnd, Lp=Lp)
+
+        reps = max(1, 24 // R)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            run_all(max(1, warmup))
+        stream.wait_stream(side)
+        torch.cuda.synchronize(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_all(reps)
+        g.replay()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        t = e0.elapsed_time(e1) * 1e-3 / (steps * reps * R)
+        d = inst[0][0]
+        old = [L - n_new for L in lens]
+        row = d.D * 2
+        nd = kind.count(0)
+        sub_rows = sum(L1 - (L0 // Lp) * Lp for L0, L1 in zip(old, lens))
+        n_sub = sum((L1 - 1) // Lp - L0 // Lp + 1 for L0, L1 in zip(old, lens))
+        nbytes = 2 * d.B * n_new * d.Hkv * 2 * row + nd * (sub_rows * row + n_sub * 2 * row)
+        res[name] = {"workload": f"{d.B} sequences, {n_new} new token(s) each, Hkv={d.Hkv} (4 dense), D={d.D}, "
+                                 f"P={d.P}, Lp={Lp}",
+                     "ms": round(t * 1e3, 4), "bytes": int(nbytes),
+                     "gbps": round(nbytes / t / 1e9, 1), "frac": round(nbytes / t / 1e9 / PEAK_HBM_GBPS, 4),
+                     "note": f"HIP graph of {reps * R} calls over {R} cache instance(s), {steps} replays"}
+        del inst, g
+        torch.cuda.empty_cache()
+    return res
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -893,14 +992,19 @@ def main():
         del out
         if "mask" in legs:
             breakdown["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
+        if "chunk" in legs:
+            breakdown["sparse_prefill_chunk"] = chunk_prefill(c, max(3, args.steps // 2), min(args.warmup, 2))
         if cpu:
             cpu_args = (c, d, args.cpu_rows_per_head, ideal_s)
         else:
             del c, d
         torch.cuda.empty_cache()
-    elif "mask" in legs:
+    elif "mask" in legs or "chunk" in legs:
         c = cases.prefill_llama8b(dev)
-        legs_out["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
+        if "mask" in legs:
+            legs_out["estimate_block_mask"] = mask_estimation(c, args.steps, args.warmup)
+        if "chunk" in legs:
+            legs_out["sparse_prefill_chunk"] = chunk_prefill(c, max(3, args.steps // 2), min(args.warmup, 2))
         del c
         torch.cuda.empty_cache()
 
@@ -916,6 +1020,8 @@ def main():
                                              "note": "sparse_decode_select (scores, decode with in-kernel top-k, merge), HIP graph over 24 instances"}
     if "varlen" in legs:
         legs_out["sparse_prefill_varlen"] = varlen_prefill(max(2, args.steps // 4), 2)
+    if "append" in legs:
+        legs_out["append_kv"] = append_leg(args.steps, args.warmup)
     if "ragged" in legs:
         r = ragged_decode_step(args.steps, args.warmup, cpu=cpu)
         if "_oracle" in r:
