@@ -296,8 +296,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
     // instead of holding a 4-wave group's slot while its other waves stream, and small
     // launches reach every CU (ragged batch: selection 132-133 against 142 us with 4-wave
     // groups; Llama-3-8B decode step 27.2 against 27.7 us).
+    // One group a wave: with the head-inner work-group order, 1 group (4 pages at Lp = 16)
+    // a wave beat 2 on the ragged batch (selection 127.8-128.9 against 131.6-132.4 us, two
+    // alternations on one box; 2 groups with 2-wave work-groups 128.6-129.6).
     const int64_t groups = ((int64_t)a.max_pages * U + 15) / 16;
-    int gpw = groups >= 256 ? 2 : 1;
+    int gpw = 1;
     // (measurement overrides: UBS_SCORE_GPW sets the groups per wave, 1 or 2, and
     // UBS_SCORE_WPG the waves per work-group, 1, 2 or 4; the scores do not depend on them)
     if (const char* env = getenv("UBS_SCORE_GPW")) {
